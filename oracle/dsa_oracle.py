@@ -1,0 +1,305 @@
+"""CPU oracle for the DSA (DeepSeek Sparse Attention) decode hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module; only the tests, the smoke check and the benchmark's CPU-baseline leg do.
+It shares no code with the HIP library.
+
+Plain, slow and written to be checked by eye: numpy in fp64, full sorts, dense
+softmax.  Every function names the passage it follows.  "The K3.1 page" below is
+the vLLM blog page on Kimi K3.1 Pro day-0 support (sparse attention, DCP,
+zero-mismatch RL); its section titles are given in English with the original.
+
+Readings of points the pages leave open (each is listed in the design notes):
+  * FP8 means OCP E4M3FN: 4 exponent bits (bias 7), 3 mantissa bits, max 448,
+    0x7F/0xFF NaN, no infinities.  The cache scales are "absmax / 448".
+  * Queries are quantised to E4M3 before both contractions, one power-of-two scale
+    per (row, head): the K3.1 page's fused indexer front quantises the indexer query
+    to FP8 ("Fused low-latency decode for DSA layers" / DSA層のための融合低レイテンシデコード).
+    The power-of-two scale sq is the smallest 2^e with absmax <= 448 * 2^e, so
+    q / sq is exact and one round-to-nearest-even gives the code.
+  * A query row at absolute position pos sees tokens 0..pos inclusive.
+  * Top-k ties are broken by the lower token index; -0.0 equals +0.0.
+  * The LSE is the natural log-sum-exp of the scaled logits.
+  * Softmax probabilities are not quantised here (the kernel's FP8 probabilities
+    in the value contraction are a bounded deviation: parity unpinned for that
+    rounding alone).
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+E4M3_MAX = 448.0
+PAGE = 64
+IDX_HEADS, IDX_DIM = 32, 128
+MLA_HEADS, LAT_DIM, V_DIM = 96, 576, 512
+IDX_PAGE_KEY_BYTES = PAGE * IDX_DIM           # 8192 bytes of codes, then 64 fp32 scales
+LAT_ROW = LAT_DIM
+
+
+# --------------------------------------------------------------------------------------
+# Number formats
+# --------------------------------------------------------------------------------------
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3FN byte: sign s, exponent e (bias 7), mantissa m.
+
+    e = 15 and m = 7 is NaN; e = 0 is subnormal m * 2^-9; else (1 + m/8) * 2^(e-7).
+    The K3.1 page stores index keys and latents in FP8 ("What changed in Kimi K3.1
+    Pro" / Kimi K3.1 Proの変更点, "Packed KV cache" / パック型KVキャッシュ).
+    """
+    s = (code >> 7) & 1
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        v = m * 2.0 ** -9
+    else:
+        v = (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+# magnitudes of codes 0x00..0x7E in increasing order (0 .. 448)
+_E4M3_POS = E4M3_TABLE[:0x7F].copy()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round-to-nearest-even onto the E4M3 grid, saturating at +-448, sign kept.
+
+    The nearest representable magnitude is looked up among the 127 finite
+    non-negative codes; on an exact tie the code with the even mantissa (even code)
+    wins.  Inputs must not be NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    lo = np.clip(np.searchsorted(_E4M3_POS, a, side="right") - 1, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
+    code = np.where(take_hi, hi, lo)
+    code = np.where(a >= E4M3_MAX, 0x7E, code)
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (code.astype(np.int64) | sign).astype(np.uint8)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64: a bf16 is the top 16 bits of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# Query quantisation (reading of the fused indexer front, see module docstring)
+# --------------------------------------------------------------------------------------
+def pow2_scale(absmax: float) -> float:
+    """Smallest power of two 2^e with absmax <= 448 * 2^e (1.0 when absmax is 0)."""
+    if absmax == 0.0:
+        return 1.0
+    _, E = math.frexp(absmax)
+    e = E - 12
+    while absmax > E4M3_MAX * 2.0 ** e:
+        e += 1
+    return 2.0 ** e
+
+
+def quantize_heads(q: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """q [H, D] real values -> (E4M3 codes [H, D], power-of-two scale [H]).
+
+    Dequantised query = e4m3_decode(codes) * scale[:, None].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    sq = np.array([pow2_scale(float(np.max(np.abs(row)))) for row in q])
+    codes = e4m3_encode(q / sq[:, None])
+    return codes, sq
+
+
+def dequantized_query(q: np.ndarray) -> np.ndarray:
+    codes, sq = quantize_heads(q)
+    return e4m3_decode(codes) * sq[:, None]
+
+
+# --------------------------------------------------------------------------------------
+# Paged caches: block table -> physical page -> bytes
+# (the K3.1 page: block tables and cache slots are translated to kernel page
+#  addresses before each step; kernels see small fixed-size pages; 132 B per index
+#  key, 576 B per latent — "Packed KV cache" / パック型KVキャッシュ)
+# --------------------------------------------------------------------------------------
+def physical_slot(block_table_row: np.ndarray, t: np.ndarray) -> np.ndarray:
+    t = np.asarray(t, dtype=np.int64)
+    return block_table_row[t // PAGE].astype(np.int64) * PAGE + t % PAGE
+
+
+def read_index_keys(key_pool: np.ndarray, block_table_row: np.ndarray, n: int):
+    """Codes [n, 128] and scales [n] of logical tokens 0..n-1 of one request.
+
+    Index-key page: byte d of token o at (d // 16) * 1024 + o * 16 + d % 16; the
+    fp32 scale of token o at 8192 + 4 * o.
+    """
+    pool = np.asarray(key_pool, dtype=np.uint8)
+    codes = np.empty((n, IDX_DIM), dtype=np.uint8)
+    scales = np.empty(n, dtype=np.float64)
+    for t in range(0, n, PAGE):
+        page = pool[int(block_table_row[t // PAGE])]
+        cnt = min(PAGE, n - t)
+        blocks = page[:IDX_PAGE_KEY_BYTES].reshape(IDX_DIM // 16, PAGE, 16)   # [8, 64, 16]
+        codes[t:t + cnt] = blocks.transpose(1, 0, 2).reshape(PAGE, IDX_DIM)[:cnt]
+        sc = page[IDX_PAGE_KEY_BYTES:IDX_PAGE_KEY_BYTES + 4 * PAGE].view(np.float32)
+        scales[t:t + cnt] = sc[:cnt]
+    return codes, scales
+
+
+def read_latents(latent_pool: np.ndarray, slots: np.ndarray) -> np.ndarray:
+    """Latent codes [len(slots), 576] of physical slots (page * 64 + offset)."""
+    pool = np.asarray(latent_pool, dtype=np.uint8)
+    slots = np.asarray(slots, dtype=np.int64)
+    rows = pool.reshape(pool.shape[0], PAGE, LAT_ROW)
+    return rows[slots // PAGE, slots % PAGE]
+
+
+# --------------------------------------------------------------------------------------
+# Stage 1: lightning-indexer score
+# --------------------------------------------------------------------------------------
+def index_scores(q_idx: np.ndarray, head_w: np.ndarray, key_codes: np.ndarray,
+                 key_scales: np.ndarray, quantize_query: bool = True) -> np.ndarray:
+    """score_t = sum_h w_h * ReLU(q_h . k_t * s_t) for every given token, as fp32.
+
+    The K3.1 page ("What changed in Kimi K3.1 Pro" / Kimi K3.1 Proの変更点) has 32
+    light heads score every prior token against one FP8 key (with its scale) per
+    token and defers the exact form to DeepSeek-V3.2's lightning indexer: a
+    head-weighted sum of ReLU'd query-key dot products.  The "Native MXFP4
+    indexer" section (ネイティブMXFP4インデクサー) adds FP32 accumulation and the
+    head-weighted reduction.  q_h is the E4M3-quantised query (module docstring);
+    k_t = decoded key codes, s_t = its fp32 scale.  Evaluated in fp64, rounded once.
+    """
+    q = dequantized_query(q_idx) if quantize_query else np.asarray(q_idx, np.float64)
+    k = e4m3_decode(key_codes)                                  # [n, 128]
+    logits = (q @ k.T) * np.asarray(key_scales, np.float64)[None, :]   # [32, n]
+    w = np.asarray(head_w, dtype=np.float64)[:, None]           # [32, 1]
+    score = np.sum(w * np.maximum(logits, 0.0), axis=0)
+    return score.astype(np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# Stage 2: top-k
+# --------------------------------------------------------------------------------------
+def topk_indices(scores: np.ndarray, k: int) -> np.ndarray:
+    """The min(k, n) best token indices under (score descending, index ascending).
+
+    The K3.1 page keeps the top 2,048 tokens per query ("What changed in Kimi K3.1
+    Pro") with exact selection ("Exact top-k merge" / 正確なtop-kマージ) and a
+    consistent tie rule ("Inter-GPU communication" / GPU間通信).  A full sort:
+    -0.0 is made +0.0 first, so the two zeros tie and the lower index wins.
+    """
+    s = np.asarray(scores, dtype=np.float64) + 0.0
+    assert not np.isnan(s).any(), "NaN score"
+    t = np.arange(s.shape[0])
+    order = np.lexsort((t, -s))
+    return order[:min(k, s.shape[0])]
+
+
+# --------------------------------------------------------------------------------------
+# Stage 3: exact MLA over the selected tokens (NoPE, shared 576-dim latent)
+# --------------------------------------------------------------------------------------
+def mla_attend(q_mla: np.ndarray, latent_codes: np.ndarray, latent_scale: float,
+               softmax_scale: float, quantize_query: bool = True):
+    """Softmax attention of 96 heads over the given latent rows.
+
+    The K3.1 page runs MLA exactly over only the selected tokens ("What changed in
+    Kimi K3.1 Pro"), on a 576-byte FP8 latent ("Sparse attention cuts long-context
+    decode bandwidth" / スパースアテンションが長いコンテキストのデコード帯域幅を削減)
+    with no positional encoding (NoPE) and 96 heads ("Token-sharded prefill").
+    Keys are all 576 dims of the decoded latent, values its first 512 dims.
+
+    Returns O [96, 512] and LSE [96] in fp64.  No rows: O = 0, LSE = -inf.
+    """
+    q = dequantized_query(q_mla) if quantize_query else np.asarray(q_mla, np.float64)
+    n = latent_codes.shape[0]
+    if n == 0:
+        return np.zeros((q.shape[0], V_DIM)), np.full(q.shape[0], -np.inf)
+    kv = e4m3_decode(latent_codes) * float(latent_scale)       # [n, 576]
+    x = float(softmax_scale) * (q @ kv.T)                      # [96, n]
+    m = np.max(x, axis=1, keepdims=True)
+    e = np.exp(x - m)
+    z = np.sum(e, axis=1, keepdims=True)
+    o = (e / z) @ kv[:, :V_DIM]
+    lse = m[:, 0] + np.log(z[:, 0])
+    return o, lse
+
+
+def dense_mla(q_mla: np.ndarray, latent_codes_all: np.ndarray, latent_scale: float,
+              softmax_scale: float, quantize_query: bool = True):
+    """Dense MLA over every visible token, written independently of mla_attend.
+
+    Uses the log-domain form: LSE = log(sum exp(x)), weights = exp(x - LSE).  It is
+    the right-hand side of the check that a top-k equal to the context length
+    reproduces dense attention.
+    """
+    q = dequantized_query(q_mla) if quantize_query else np.asarray(q_mla, np.float64)
+    kv = e4m3_decode(latent_codes_all) * float(latent_scale)
+    logits = float(softmax_scale) * np.einsum("hd,td->ht", q, kv)
+    lse = np.logaddexp.reduce(logits, axis=1)
+    weights = np.exp(logits - lse[:, None])
+    o = np.einsum("ht,td->hd", weights, kv[:, :V_DIM])
+    return o, lse
+
+
+# --------------------------------------------------------------------------------------
+# Stage 4: log-sum-exp combine of split partials
+# --------------------------------------------------------------------------------------
+def lse_combine(parts: Sequence[Tuple[np.ndarray, np.ndarray]]):
+    """Merge per-split (O_s normalised by its own sum, LSE_s) into (O, LSE).
+
+    The K3.1 page merges partial attention outputs by log-sum-exp ("Decode context
+    parallelism with the sparse indexer" / スパースインデクサーを使用したデコード
+    コンテキスト並列処理, and the exchange-and-combine kernels of "Exact top-k
+    merge").  LSE = m + ln sum_s exp(LSE_s - m), O = sum_s exp(LSE_s - LSE) O_s.
+    An empty split has LSE_s = -inf and contributes nothing; all empty -> O = 0,
+    LSE = -inf.
+    """
+    lses = np.stack([np.asarray(l, np.float64) for _, l in parts])      # [S, H]
+    outs = np.stack([np.asarray(o, np.float64) for o, _ in parts])      # [S, H, D]
+    m = np.max(lses, axis=0)                                           # [H]
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - m_safe[None, :]), 0.0)
+    tot = np.sum(w, axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    coef = np.where(finite[None, :], w / np.where(finite, tot, 1.0)[None, :], 0.0)
+    o = np.einsum("sh,shd->hd", coef, outs)
+    return o, lse
+
+
+def split_ranges(n: int, num_splits: int) -> List[Tuple[int, int]]:
+    """Balanced contiguous ranges [s*n//S, (s+1)*n//S) of the selected list."""
+    return [(s * n // num_splits, (s + 1) * n // num_splits) for s in range(num_splits)]
+
+
+# --------------------------------------------------------------------------------------
+# Whole row
+# --------------------------------------------------------------------------------------
+def decode_row(q_idx, head_w, q_mla, key_codes, key_scales, latent_codes, latent_scale,
+               softmax_scale, pos: int, k: int, block_table_row=None):
+    """Every stage for one query row that sees tokens 0..pos.
+
+    key_codes / key_scales / latent_codes are the request's logical rows (at least
+    pos + 1 of them).  Returns a dict with scores (fp32), the selected indices
+    (sorted by score), O and LSE (fp64), and physical slots if a block table row
+    is given.
+    """
+    n = pos + 1
+    scores = index_scores(q_idx, head_w, key_codes[:n], key_scales[:n])
+    sel = topk_indices(scores, k)
+    o, lse = mla_attend(q_mla, latent_codes[sel], latent_scale, softmax_scale)
+    out = {"scores": scores, "topk": sel, "o": o, "lse": lse}
+    if block_table_row is not None:
+        out["slots"] = physical_slot(block_table_row, sel)
+    return out
