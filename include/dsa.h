@@ -1,0 +1,178 @@
+/*
+ * dsa.h — C ABI of the MI355X (gfx950) DSA decode hot path.
+ *
+ * DeepSeek Sparse Attention as served for Kimi K3.1 Pro's full-attention layers
+ * (the vLLM day-0 page on Kimi K3.1 Pro: sparse attention, DCP and zero-mismatch RL):
+ * a lightning indexer scores every prior token, the best 2,048 are kept, MLA runs
+ * exactly over those only, and split partial outputs are merged by log-sum-exp.
+ *
+ *   dsa_index_score       stage 1  indexer scores           ("What changed in Kimi K3.1 Pro")
+ *   dsa_topk              stage 2  exact top-k select       ("Exact top-k merge with ~10x less traffic")
+ *   dsa_sparse_mla_decode stage 3  MLA over selected tokens ("Sparse attention cuts long-context
+ *                                                             decode bandwidth")
+ *   dsa_lse_combine       stage 4  LSE merge of splits      ("Decode context parallelism with the
+ *                                                             sparse indexer")
+ *   dsa_quantize_q        the query quantisation the stages 1 and 3 apply internally
+ *                         (fused indexer front of "Fused low-latency decode for DSA layers"),
+ *                         exposed so callers and tests can see the exact FP8 codes.
+ *
+ * Conventions shared by every call
+ *  - Every pointer is a DEVICE pointer on the current HIP device unless marked (host).
+ *    The caller owns and allocates all memory, including the top-k workspace.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work
+ *    on it: no allocation, no host synchronisation, no device-to-host reads.
+ *  - Host scalars and pointer nullness/alignment are validated before anything is
+ *    launched; on failure nothing is launched and the call returns a non-OK status with
+ *    a message available from dsa_last_error() (thread-local).
+ *  - Device array CONTENTS are trusted preconditions (block-table entries in range,
+ *    seq_lens >= rows of the request, slots in range or -1).  They are not checked.
+ *  - Fixed shapes: page 64 tokens, indexer 32 heads x 128 dims, MLA 96 heads on a
+ *    576-dim latent whose first 512 dims are the values.  FP8 is OCP E4M3FN.
+ *
+ * Batch description (used by stages 1 and 2).  Query rows are grouped by request: the
+ * rows of request b are cu_q[b] .. cu_q[b+1]-1 and they are the LAST
+ * n_b = cu_q[b+1]-cu_q[b] tokens of that request, so row j of request b sits at
+ * position seq_lens[b] - n_b + j and sees tokens 0..position (inclusive causal).
+ * This covers plain decode (n_b = 1), speculative verification (n_b <= 8, causal among
+ * the new tokens) and prefill append (n_b new tokens on a cached prefix).
+ *
+ * Cache layouts ("Packed KV cache for three kinds of state": 132 B per index key,
+ * 576 B per latent, small fixed-size pages addressed through a block table).
+ *  - block_table: int32 [num_seqs][bt_stride]; entry j is the physical page holding
+ *    logical tokens 64j .. 64j+63 of the request.  A physical slot is page*64 + offset.
+ *  - index-key page (at key_pages + page * key_page_stride, 16-byte aligned):
+ *      bytes [0, 8192): E4M3 codes; byte d of token o at (d/16)*1024 + o*16 + d%16
+ *      bytes [8192, 8448): fp32 scale of token o at 8192 + 4*o (key = codes * scale)
+ *  - latent page (at latent_pages + page * latent_page_stride, 16-byte aligned):
+ *      token o's 576 E4M3 codes at o*576; latent = codes * latent_scale (per tensor).
+ *  Page strides are in bytes, multiples of 16, at least 8448 / 36864, so several
+ *  per-layer pages can share one packed block row.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or inconsistent host scalars */
+  DSA_ERR_UNSUPPORTED = 2,   /* shape the library does not implement */
+  DSA_ERR_WORKSPACE = 3,     /* workspace smaller than dsa_topk_workspace_size() */
+  DSA_ERR_LAUNCH = 4         /* the HIP runtime rejected a launch */
+} dsa_status;
+
+#define DSA_PAGE_SIZE 64
+#define DSA_IDX_HEADS 32
+#define DSA_IDX_DIM 128
+#define DSA_IDX_PAGE_BYTES 8448
+#define DSA_MLA_HEADS 96
+#define DSA_LATENT_DIM 576
+#define DSA_V_DIM 512
+#define DSA_LATENT_PAGE_BYTES 36864
+#define DSA_MAX_TOPK 4096
+#define DSA_MAX_SPLITS 64
+
+/*
+ * Stage 1 — lightning-indexer scores.
+ *   score[i][t] = sum_h w'[i][h] * ReLU(sum_d q8[i][h][d] * k8[t][d]) * s[t]
+ * where q8 / sq are the E4M3 codes and power-of-two scale of dsa_quantize_q applied to
+ * q_bf16 row i, head h, and w' = head_w * sq.  Because sq, s > 0 this equals
+ * sum_h w_h ReLU(q_h . k_t s_t) with q_h the dequantised query, the head-weighted ReLU
+ * form of DeepSeek-V3.2's lightning indexer that the K3.1 page defers to.
+ * FP8 MFMA products, fp32 accumulation.
+ *
+ *   num_seqs, n_q       (host) requests and total query rows (>= 1 each)
+ *   max_seq_len         (host) >= every seq_lens[b]; sizes the grid
+ *   max_q_per_seq       (host) >= every request's row count
+ *   cu_q [num_seqs+1], seq_lens [num_seqs]   batch description above
+ *   q_bf16   [n_q][32][128] bf16            head_w [n_q][32] fp32
+ *   key_pages, key_page_stride, block_table, bt_stride   index-key cache
+ *   scores   fp32 [n_q][score_stride], score_stride >= max_seq_len.  Row i's columns
+ *            0 .. seq_lens[b]-1 are written; columns past its position hold scores of
+ *            keys it may not see (ignored by dsa_topk); other columns are not touched.
+ */
+dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                           int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
+                           const void* q_bf16, const float* head_w, const void* key_pages,
+                           int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
+                           float* scores, int64_t score_stride, void* stream);
+
+/*
+ * Stage 2 — exact top-k over each row's visible scores (tokens 0..position).
+ * Order: score descending, then token index ascending (-0.0 == +0.0; NaN ranks lowest).
+ * Two passes: every 8,192-token chunk keeps its best m candidates, then one workgroup
+ * per row selects from the candidates; if a chunk could have held more of the winners
+ * than it sent (the detection rule of the K3.1 page's exact one-round merge), that row
+ * is re-selected from all of its scores, so the result is always exact.
+ *
+ *   k in 1..4096.  topk_idx int32 [n_q][k]: the min(k, position+1) selected logical
+ *   token indices in increasing index order, then -1.  topk_slot int32 [n_q][k]: the
+ *   physical slots of the same tokens (page*64 + offset via block_table), -1 padded;
+ *   pass block_table = NULL and topk_slot = NULL to skip slots.
+ *   workspace: device memory of at least dsa_topk_workspace_size() bytes, 256-byte
+ *   aligned; its contents need no initialisation and are scratch after the call.
+ */
+size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k);
+dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
+                    const int32_t* seq_lens, const float* scores, int64_t score_stride, int32_t k,
+                    const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
+                    int32_t* topk_slot, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 3 — exact MLA (NoPE) over the selected slots, one query row at a time.
+ *   logit[h][t] = softmax_scale * (q8[h] * sq[h]) . (latent_scale * L8[t])   (576 dims)
+ *   O[h] = sum_t softmax(logit[h])[t] * latent_scale * L8[t][0:512],
+ *   LSE[h] = log(sum_t exp(logit[h][t]))   (natural log)
+ * The query is E4M3-quantised per (row, head) as dsa_quantize_q does.  Both
+ * contractions run on FP8 MFMA; the probabilities enter the value product as E4M3.
+ *
+ *   q_bf16 [n_q][96][576] bf16.  topk_slot int32 [n_q][k]; -1 entries are skipped.
+ *   num_splits S in 1..64, S <= k: split s of a row covers entries
+ *   [s*k/S, (s+1)*k/S) of its slot list.
+ *   S == 1: out_bf16 [n_q][96][512] bf16 and lse [n_q][96] fp32 are written
+ *           (o_part / lse_part unused, may be NULL).
+ *   S > 1:  o_part fp32 [S][n_q][96][512] (each split normalised by its own sum) and
+ *           lse_part fp32 [S][n_q][96] are written (out_bf16 / lse unused); an empty
+ *           split has O = 0 and LSE = -inf.  Merge them with dsa_lse_combine.
+ */
+dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* latent_pages,
+                                 int64_t latent_page_stride, float latent_scale,
+                                 const int32_t* topk_slot, int32_t k, float softmax_scale,
+                                 int32_t num_splits, float* o_part, float* lse_part,
+                                 void* out_bf16, float* lse, void* stream);
+
+/*
+ * Stage 4 — log-sum-exp merge of split partials:
+ *   LSE = m + log(sum_s exp(LSE_s - m)),  O = sum_s exp(LSE_s - LSE) * O_s.
+ * Splits with LSE_s = -inf contribute nothing; if all are empty, O = 0, LSE = -inf.
+ *   o_part fp32 [S][n_q][96][512], lse_part fp32 [S][n_q][96]  ->
+ *   out_bf16 [n_q][96][512] bf16, lse [n_q][96] fp32.   S in 1..64.
+ */
+dsa_status dsa_lse_combine(int32_t num_splits, int32_t n_q, const float* o_part,
+                           const float* lse_part, void* out_bf16, float* lse, void* stream);
+
+/*
+ * Per-(row, head) E4M3 query quantisation used inside stages 1 and 3.
+ *   sq = smallest power of two 2^e with max_d |q[d]| <= 448 * 2^e (1 if all zero);
+ *   codes[d] = E4M3 round-to-nearest-even of q[d] / sq.
+ *   q_bf16 [rows][heads][dim] bf16 -> codes uint8 [rows][heads][dim], scales fp32
+ *   [rows][heads].  dim must be 128 or 576.
+ */
+dsa_status dsa_quantize_q(int32_t rows, int32_t heads, int32_t dim, const void* q_bf16,
+                          uint8_t* codes, float* scales, void* stream);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+/* Library version string. */
+const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,229 @@
+"""Python binding of libdsa, the MI355X (gfx950) DSA decode hot path.
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+PyTorch supplies device memory (tensors) and the stream; each function passes raw
+pointers, host scalars and `torch.cuda.current_stream().cuda_stream` to the C ABI
+declared in include/dsa.h, under the same names.
+
+The library is loaded from this package's lib/ folder (built by build.py).  There is
+no fallback: if it is missing, or a tensor is not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libdsa.so")
+
+PAGE = 64
+IDX_HEADS, IDX_DIM, IDX_PAGE_BYTES = 32, 128, 8448
+MLA_HEADS, LATENT_DIM, V_DIM, LATENT_PAGE_BYTES = 96, 576, 512, 36864
+MAX_TOPK, MAX_SPLITS = 4096, 64
+
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
+          3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_LAUNCH"}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdsa (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python sparse_attention_decode_score_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.dsa_index_score.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32,
+                                      _P, _I64, _P]
+        L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
+        L.dsa_topk_workspace_size.restype = _SZ
+        L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ, _P]
+        L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _I64, _F32, _P, _I32, _F32, _I32, _P, _P,
+                                            _P, _P, _P]
+        L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
+        L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
+        L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_version.restype = ctypes.c_char_p
+        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_combine",
+                  "dsa_quantize_q"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsaError(status, lib().dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("DSA tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("DSA tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _expect(t: torch.Tensor, name: str, dtype, shape=None):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def dsa_version() -> str:
+    return lib().dsa_version().decode()
+
+
+def dsa_quantize_q(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """E4M3 codes [rows, heads, dim] (uint8) and power-of-two scales [rows, heads] of q."""
+    _expect(q, "q", torch.bfloat16)
+    rows, heads, dim = q.shape
+    _expect(codes, "codes", torch.uint8, (rows, heads, dim))
+    _expect(scales, "scales", torch.float32, (rows, heads))
+    _check(lib().dsa_quantize_q(rows, heads, dim, _ptr(q), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Tensor,
+                    head_w: torch.Tensor, key_pages: torch.Tensor, block_table: torch.Tensor,
+                    scores: torch.Tensor, *, max_seq_len: int, max_q_per_seq: int,
+                    key_page_stride: Optional[int] = None, stream=None) -> None:
+    """Indexer scores into scores [n_q, score_stride] (fp32)."""
+    num_seqs = seq_lens.shape[0]
+    n_q = q_idx.shape[0]
+    _expect(cu_q, "cu_q", torch.int32, (num_seqs + 1,))
+    _expect(seq_lens, "seq_lens", torch.int32)
+    _expect(q_idx, "q_idx", torch.bfloat16, (n_q, IDX_HEADS, IDX_DIM))
+    _expect(head_w, "head_w", torch.float32, (n_q, IDX_HEADS))
+    _expect(block_table, "block_table", torch.int32)
+    _expect(scores, "scores", torch.float32)
+    if scores.dim() != 2 or scores.shape[0] != n_q:
+        raise ValueError("scores must be [n_q, score_stride]")
+    stride = key_page_stride if key_page_stride is not None else key_pages.stride(0) * key_pages.element_size()
+    _check(lib().dsa_index_score(num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q),
+                                 _ptr(seq_lens), _ptr(q_idx), _ptr(head_w), _ptr(key_pages),
+                                 int(stride), _ptr(block_table), block_table.shape[1],
+                                 _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
+    return int(lib().dsa_topk_workspace_size(int(n_q), int(max_seq_len), int(k)))
+
+
+def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,
+             block_table: Optional[torch.Tensor], topk_idx: torch.Tensor,
+             topk_slot: Optional[torch.Tensor], workspace: torch.Tensor, *, max_seq_len: int,
+             stream=None) -> None:
+    """Exact top-k token indices (and physical slots) of every row's visible scores."""
+    num_seqs = seq_lens.shape[0]
+    n_q = scores.shape[0]
+    _expect(scores, "scores", torch.float32)
+    _expect(topk_idx, "topk_idx", torch.int32, (n_q, k))
+    if topk_slot is not None:
+        _expect(topk_slot, "topk_slot", torch.int32, (n_q, k))
+    _expect(workspace, "workspace", torch.uint8)
+    _check(lib().dsa_topk(num_seqs, n_q, int(max_seq_len), _ptr(cu_q), _ptr(seq_lens), _ptr(scores),
+                          scores.shape[1], int(k), _ptr(block_table),
+                          block_table.shape[1] if block_table is not None else 0,
+                          _ptr(topk_idx), _ptr(topk_slot), _ptr(workspace), workspace.numel(),
+                          _stream(stream)))
+
+
+def dsa_sparse_mla_decode(q_mla: torch.Tensor, latent_pages: torch.Tensor, latent_scale: float,
+                          topk_slot: torch.Tensor, softmax_scale: float, num_splits: int, *,
+                          o_part: Optional[torch.Tensor] = None,
+                          lse_part: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          latent_page_stride: Optional[int] = None, stream=None) -> None:
+    """MLA over the selected slots: (out, lse) when num_splits == 1, else (o_part, lse_part)."""
+    n_q = q_mla.shape[0]
+    _expect(q_mla, "q_mla", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+    _expect(topk_slot, "topk_slot", torch.int32)
+    k = topk_slot.shape[1]
+    if num_splits == 1:
+        _expect(out, "out", torch.bfloat16, (n_q, MLA_HEADS, V_DIM))
+        _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
+    else:
+        _expect(o_part, "o_part", torch.float32, (num_splits, n_q, MLA_HEADS, V_DIM))
+        _expect(lse_part, "lse_part", torch.float32, (num_splits, n_q, MLA_HEADS))
+    stride = (latent_page_stride if latent_page_stride is not None
+              else latent_pages.stride(0) * latent_pages.element_size())
+    _check(lib().dsa_sparse_mla_decode(n_q, _ptr(q_mla), _ptr(latent_pages), int(stride),
+                                       float(latent_scale), _ptr(topk_slot), int(k),
+                                       float(softmax_scale), int(num_splits), _ptr(o_part),
+                                       _ptr(lse_part), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
+                    lse: torch.Tensor, stream=None) -> None:
+    """LSE merge of split partials [S, n_q, 96, 512] / [S, n_q, 96] into bf16 out and lse."""
+    S, n_q = o_part.shape[0], o_part.shape[1]
+    _expect(o_part, "o_part", torch.float32, (S, n_q, MLA_HEADS, V_DIM))
+    _expect(lse_part, "lse_part", torch.float32, (S, n_q, MLA_HEADS))
+    _expect(out, "out", torch.bfloat16, (n_q, MLA_HEADS, V_DIM))
+    _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
+    _check(lib().dsa_lse_combine(S, n_q, _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
+                                 _stream(stream)))
+
+
+class DecodeStep:
+    """Device buffers for one pass of the whole path over a fixed batch shape.
+
+    Allocates (through torch) the scores, top-k outputs, workspace and partials once;
+    run() then issues the four library calls on the current stream.
+    """
+
+    def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda"):
+        self.n_q, self.max_seq_len, self.k, self.num_splits = n_q, max_seq_len, k, num_splits
+        dev = torch.device(device)
+        self.scores = torch.empty((n_q, max_seq_len), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+        self.topk_slot = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+        ws = dsa_topk_workspace_size(n_q, max_seq_len, k)
+        self.workspace = torch.empty((ws + 256,), dtype=torch.uint8, device=dev)
+        off = (-self.workspace.data_ptr()) % 256
+        self.workspace = self.workspace[off:off + ws]
+        self.out = torch.empty((n_q, MLA_HEADS, V_DIM), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)
+        if num_splits > 1:
+            self.o_part = torch.empty((num_splits, n_q, MLA_HEADS, V_DIM), dtype=torch.float32, device=dev)
+            self.lse_part = torch.empty((num_splits, n_q, MLA_HEADS), dtype=torch.float32, device=dev)
+        else:
+            self.o_part = self.lse_part = None
+
+    def run(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, q_mla, latent_pages,
+            latent_scale, softmax_scale, max_q_per_seq, stream=None):
+        dsa_index_score(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, self.scores,
+                        max_seq_len=self.max_seq_len, max_q_per_seq=max_q_per_seq, stream=stream)
+        dsa_topk(cu_q, seq_lens, self.scores, self.k, block_table, self.topk_idx, self.topk_slot,
+                 self.workspace, max_seq_len=self.max_seq_len, stream=stream)
+        if self.num_splits == 1:
+            dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
+                                  1, out=self.out, lse=self.lse, stream=stream)
+        else:
+            dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
+                                  self.num_splits, o_part=self.o_part, lse_part=self.lse_part,
+                                  stream=stream)
+            dsa_lse_combine(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
+        return self.out, self.lse

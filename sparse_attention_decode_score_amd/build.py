@@ -1,0 +1,61 @@
+"""Builds libdsa.so (the C ABI of the DSA decode path) for gfx950 with hipcc, in-tree."""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "lib")
+LIB = os.path.join(LIBDIR, "libdsa.so")
+SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "lse_combine.hip", "capi.cpp"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the DSA library needs ROCm's hipcc to build")
+
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+          # packed fp32 instructions stay off: plain float code only
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I" + os.path.join(ROOT, "include")]
+
+
+def _compile(src: str, obj: str) -> None:
+    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".hip"):
+        cmd.insert(1, "-xhip")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source for gfx950 and links lib/libdsa.so; returns its path."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    with tempfile.TemporaryDirectory() as tmp:
+        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+        with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+            list(ex.map(_compile, SOURCES, objs))
+        out_tmp = LIB + ".tmp"
+        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(out_tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,180 @@
+// C ABI of the DSA decode library: argument validation, then launches on the caller's stream.
+// Every check here runs on the host before anything is enqueued; a failed check launches
+// nothing and records a message for dsa_last_error().
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dsa_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define DSA_REQUIRE(cond, ...)                                  \
+  do {                                                          \
+    if (!(cond)) return fail(DSA_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+
+dsa_status check_batch(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
+                       const int32_t* seq_lens) {
+  DSA_REQUIRE(num_seqs >= 1, "num_seqs must be >= 1 (got %d)", num_seqs);
+  DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+  DSA_REQUIRE(n_q >= num_seqs, "n_q (%d) must be >= num_seqs (%d): every request has a row", n_q,
+              num_seqs);
+  DSA_REQUIRE(max_seq_len >= 1, "max_seq_len must be >= 1 (got %d)", max_seq_len);
+  DSA_REQUIRE(cu_q != nullptr && seq_lens != nullptr, "cu_q and seq_lens must be non-null");
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+const char* dsa_version(void) { return "dsa-mi355x 0.1.0 (gfx950)"; }
+
+dsa_status dsa_quantize_q(int32_t rows, int32_t heads, int32_t dim, const void* q_bf16,
+                          uint8_t* codes, float* scales, void* stream) {
+  DSA_REQUIRE(rows >= 0 && heads >= 1, "rows must be >= 0 and heads >= 1");
+  if (dim != DSA_IDX_DIM && dim != DSA_LATENT_DIM)
+    return fail(DSA_ERR_UNSUPPORTED, "dim must be 128 or 576 (got %d)", dim);
+  DSA_REQUIRE(q_bf16 && codes && scales, "q_bf16, codes and scales must be non-null");
+  return launched(dsa::launch_quantize_q(rows, heads, dim, static_cast<const uint16_t*>(q_bf16),
+                                         codes, scales, static_cast<hipStream_t>(stream)),
+                  "dsa_quantize_q");
+}
+
+dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                           int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
+                           const void* q_bf16, const float* head_w, const void* key_pages,
+                           int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
+                           float* scores, int64_t score_stride, void* stream) {
+  dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
+  if (st != DSA_OK) return st;
+  DSA_REQUIRE(max_q_per_seq >= 1 && max_q_per_seq <= n_q,
+              "max_q_per_seq must be in 1..n_q (got %d)", max_q_per_seq);
+  DSA_REQUIRE(q_bf16 && head_w && key_pages && block_table && scores,
+              "q_bf16, head_w, key_pages, block_table and scores must be non-null");
+  DSA_REQUIRE(aligned(q_bf16, 16), "q_bf16 must be 16-byte aligned");
+  DSA_REQUIRE(aligned(head_w, 16), "head_w must be 16-byte aligned");
+  DSA_REQUIRE(aligned(key_pages, 16), "key_pages must be 16-byte aligned");
+  DSA_REQUIRE(key_page_stride >= DSA_IDX_PAGE_BYTES && key_page_stride % 16 == 0,
+              "key_page_stride must be >= 8448 and a multiple of 16 (got %lld)",
+              (long long)key_page_stride);
+  DSA_REQUIRE(bt_stride >= (max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE,
+              "bt_stride (%d) must cover max_seq_len (%d) in pages of 64", bt_stride, max_seq_len);
+  DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
+              (long long)score_stride, max_seq_len);
+  return launched(dsa::launch_index_score(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens,
+                                          static_cast<const uint16_t*>(q_bf16), head_w,
+                                          static_cast<const uint8_t*>(key_pages), key_page_stride,
+                                          block_table, bt_stride, scores, score_stride,
+                                          static_cast<hipStream_t>(stream)),
+                  "dsa_index_score");
+}
+
+size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k) {
+  if (n_q < 1 || max_seq_len < 1 || k < 1 || k > DSA_MAX_TOPK) return 0;
+  return dsa::topk_workspace_bytes(n_q, max_seq_len, k);
+}
+
+dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
+                    const int32_t* seq_lens, const float* scores, int64_t score_stride, int32_t k,
+                    const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
+                    int32_t* topk_slot, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
+  if (st != DSA_OK) return st;
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
+  DSA_REQUIRE(scores && topk_idx, "scores and topk_idx must be non-null");
+  DSA_REQUIRE((block_table == nullptr) == (topk_slot == nullptr),
+              "block_table and topk_slot must both be given or both be NULL");
+  DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
+              (long long)score_stride, max_seq_len);
+  if (block_table)
+    DSA_REQUIRE(bt_stride >= (max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE,
+                "bt_stride (%d) must cover max_seq_len (%d) in pages of 64", bt_stride, max_seq_len);
+  const size_t need = dsa::topk_workspace_bytes(n_q, max_seq_len, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+  return launched(dsa::launch_topk(num_seqs, n_q, max_seq_len, cu_q, seq_lens, scores, score_stride,
+                                   k, block_table, bt_stride, topk_idx, topk_slot, workspace,
+                                   static_cast<hipStream_t>(stream)),
+                  "dsa_topk");
+}
+
+dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* latent_pages,
+                                 int64_t latent_page_stride, float latent_scale,
+                                 const int32_t* topk_slot, int32_t k, float softmax_scale,
+                                 int32_t num_splits, float* o_part, float* lse_part,
+                                 void* out_bf16, float* lse, void* stream) {
+  DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
+  if (num_splits < 1 || num_splits > DSA_MAX_SPLITS)
+    return fail(DSA_ERR_UNSUPPORTED, "num_splits must be in 1..64 (got %d)", num_splits);
+  DSA_REQUIRE(num_splits <= k, "num_splits (%d) must be <= k (%d)", num_splits, k);
+  DSA_REQUIRE(q_bf16 && latent_pages && topk_slot, "q_bf16, latent_pages and topk_slot must be non-null");
+  DSA_REQUIRE(aligned(q_bf16, 16) && aligned(latent_pages, 16),
+              "q_bf16 and latent_pages must be 16-byte aligned");
+  DSA_REQUIRE(latent_page_stride >= DSA_LATENT_PAGE_BYTES && latent_page_stride % 16 == 0,
+              "latent_page_stride must be >= 36864 and a multiple of 16 (got %lld)",
+              (long long)latent_page_stride);
+  DSA_REQUIRE(latent_scale > 0.f, "latent_scale must be > 0");
+  DSA_REQUIRE(softmax_scale > 0.f, "softmax_scale must be > 0");
+  if (num_splits == 1) {
+    DSA_REQUIRE(out_bf16 && lse, "num_splits == 1 needs out_bf16 and lse");
+  } else {
+    DSA_REQUIRE(o_part && lse_part, "num_splits > 1 needs o_part and lse_part");
+    DSA_REQUIRE(aligned(o_part, 16), "o_part must be 16-byte aligned");
+  }
+  return launched(dsa::launch_sparse_mla(n_q, static_cast<const uint16_t*>(q_bf16),
+                                         static_cast<const uint8_t*>(latent_pages),
+                                         latent_page_stride, latent_scale, topk_slot, k,
+                                         softmax_scale, num_splits, o_part, lse_part,
+                                         static_cast<uint16_t*>(out_bf16), lse,
+                                         static_cast<hipStream_t>(stream)),
+                  "dsa_sparse_mla_decode");
+}
+
+dsa_status dsa_lse_combine(int32_t num_splits, int32_t n_q, const float* o_part,
+                           const float* lse_part, void* out_bf16, float* lse, void* stream) {
+  if (num_splits < 1 || num_splits > DSA_MAX_SPLITS)
+    return fail(DSA_ERR_UNSUPPORTED, "num_splits must be in 1..64 (got %d)", num_splits);
+  DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+  DSA_REQUIRE(o_part && lse_part && out_bf16 && lse, "o_part, lse_part, out_bf16, lse must be non-null");
+  DSA_REQUIRE(aligned(o_part, 16) && aligned(out_bf16, 8), "o_part must be 16-byte and out_bf16 8-byte aligned");
+  return launched(dsa::launch_lse_combine(num_splits, n_q, o_part, lse_part,
+                                          static_cast<uint16_t*>(out_bf16), lse,
+                                          static_cast<hipStream_t>(stream)),
+                  "dsa_lse_combine");
+}
+
+}  // extern "C"

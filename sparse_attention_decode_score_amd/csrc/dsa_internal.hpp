@@ -1,0 +1,42 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct TopkPlan {
+  int chunk;        // tokens per chunk of the first pass
+  int num_chunks;   // chunks covering max_seq_len
+  int row_cap;      // candidate slots reserved per row
+};
+
+TopkPlan topk_plan(int max_seq_len, int k);
+size_t topk_workspace_bytes(int n_q, int max_seq_len, int k);
+
+hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, uint8_t* codes,
+                             float* scales, hipStream_t st);
+
+hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_per_seq,
+                              const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
+                              const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
+                              const int32_t* block_table, int bt_stride, float* scores,
+                              int64_t score_stride, hipStream_t st);
+
+hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu_q,
+                       const int32_t* seq_lens, const float* scores, int64_t score_stride, int k,
+                       const int32_t* block_table, int bt_stride, int32_t* topk_idx,
+                       int32_t* topk_slot, void* workspace, hipStream_t st);
+
+hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* latent_pages,
+                             int64_t latent_page_stride, float latent_scale,
+                             const int32_t* topk_slot, int k, float softmax_scale, int num_splits,
+                             float* o_part, float* lse_part, uint16_t* out_bf16, float* lse,
+                             hipStream_t st);
+
+hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
+                              uint16_t* out_bf16, float* lse, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,217 @@
+// Stage 1 of the DSA decode path: lightning-indexer scores over a paged FP8 key cache.
+//
+// score[i][t] = sum_h w_h * sq_h * ReLU(q8_h . k8_t) * s_t  (the head-weighted ReLU form of
+// DeepSeek-V3.2's lightning indexer that the vLLM Kimi K3.1 Pro page defers to in "What
+// changed in Kimi K3.1 Pro"; fp32 accumulation and head-weighted reduction as in its
+// "Native MXFP4 indexer" section).  The per-(row, head) power-of-two query scale sq is
+// folded into the head weight, so the FP8 product needs no rescaling inside the loop.
+//
+// Work split: one workgroup per (request, chunk of 16 pages, group of up to R query rows).
+// Every workgroup streams its keys exactly once from HBM and reuses them for all R rows of
+// the request (keys are shared by the verification rows of a speculative step, as the
+// page's MI355X indexer does), so the grid is balanced by keys, not by requests.
+//
+// One wave handles one 64-token page at a time as two 32-token halves:
+//   D[head][token] = Q8[32 heads x 128] * K8^T[128 x 32 tokens]  (2 x v_mfma 32x32x64 fp8)
+// Lane l reads 64 contiguous key bytes of token l%32 (bytes 64*(l/32) ..); the page stores
+// keys in 16-byte column blocks so each of the 8 loads per lane is a fully coalesced 1 KB
+// wave access.  The head reduction is 16 in-register FMAs, then one permlane32 swap that
+// also places token l of the page in lane l for a coalesced 256-byte score store.
+#include "dsa_device.hpp"
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kPagesPerWg = 16;
+constexpr int kQRowStride = 144;  // LDS row stride of the FP8 query (128 + 16 pad: no bank conflicts)
+
+struct KeyPage {
+  v8i k[2][2];  // [half][k-block]
+  float s;
+};
+
+__device__ __forceinline__ void load_key_page(KeyPage& kp, const uint8_t* base, int lane) {
+  const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const uint8_t* tok = base + (32 * hf + n) * 16;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const v4i a = *reinterpret_cast<const v4i*>(tok + (4 * g + 2 * kb) * 1024);
+      const v4i b = *reinterpret_cast<const v4i*>(tok + (4 * g + 2 * kb + 1) * 1024);
+      kp.k[hf][kb] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+  }
+  kp.s = *reinterpret_cast<const float*>(base + kIdxPageKeyBytes + 4 * lane);
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void index_score_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
+    const uint16_t* __restrict__ q, const float* __restrict__ head_w,
+    const uint8_t* __restrict__ key_pages, int64_t page_stride,
+    const int32_t* __restrict__ block_table, int bt_stride, float* __restrict__ scores,
+    int64_t score_stride) {
+  __shared__ __attribute__((aligned(16))) uint8_t q8s[R][kIdxHeads][kQRowStride];
+  __shared__ __attribute__((aligned(16))) float wps[R][kIdxHeads];
+
+  const int b = blockIdx.y;
+  const int q0 = cu_q[b], q1 = cu_q[b + 1];
+  const int r0 = q0 + (int)blockIdx.z * R;
+  if (r0 >= q1) return;
+  const int nr = min(R, q1 - r0);
+  const int L = seq_lens[b];
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int p0 = (int)blockIdx.x * kPagesPerWg;
+  // the last position any row of this group may see
+  const int max_pos = L - (q1 - q0) + (r0 + nr - 1 - q0);
+  if (p0 >= n_pages || p0 * kPage > max_pos) return;
+  const int p_end = min(min(n_pages, p0 + kPagesPerWg), max_pos / kPage + 1);
+
+  const int tid = threadIdx.x;
+  // ---- fused query prep: E4M3 codes with one power-of-two scale per (row, head) --------
+  {
+    const int h = tid >> 3, part = tid & 7;  // 32 heads x 8 parts of 16 dims
+    for (int r = 0; r < R; ++r) {
+      if (r < nr) {
+        const uint16_t* src = q + ((int64_t)(r0 + r) * kIdxHeads + h) * kIdxDim + part * 16;
+        const v4i u0 = *reinterpret_cast<const v4i*>(src);
+        const v4i u1 = *reinterpret_cast<const v4i*>(src + 8);
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = bf16_lo((uint32_t)u0[j]);
+          x[2 * j + 1] = bf16_hi((uint32_t)u0[j]);
+          x[8 + 2 * j] = bf16_lo((uint32_t)u1[j]);
+          x[8 + 2 * j + 1] = bf16_hi((uint32_t)u1[j]);
+        }
+        float am = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
+        am = fmaxf(am, __shfl_xor(am, 1, 64));
+        am = fmaxf(am, __shfl_xor(am, 2, 64));
+        am = fmaxf(am, __shfl_xor(am, 4, 64));
+        const int e = pow2_scale_exp(am);
+        const float inv = ldexpf(1.0f, -e);
+        v4i c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          c[j] = (int)cvt4_e4m3(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv,
+                                x[4 * j + 3] * inv);
+        *reinterpret_cast<v4i*>(&q8s[r][h][part * 16]) = c;
+        if (part == 0) wps[r][h] = head_w[(int64_t)(r0 + r) * kIdxHeads + h] * ldexpf(1.0f, e);
+      } else {
+        *reinterpret_cast<v4i*>(&q8s[r][h][part * 16]) = v4i{0, 0, 0, 0};
+        if (part == 0) wps[r][h] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31, g = lane >> 5;
+  int p = p0 + wave;
+  if (p >= p_end) return;
+
+  const int32_t* bt = block_table + (int64_t)b * bt_stride;
+  KeyPage cur;
+  load_key_page(cur, key_pages + (int64_t)bt[p] * page_stride, lane);
+  for (; p < p_end; p += 4) {
+    KeyPage nxt;
+    const bool more = p + 4 < p_end;
+    if (more) load_key_page(nxt, key_pages + (int64_t)bt[p + 4] * page_stride, lane);
+    const int t = p * kPage + lane;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r < nr) {
+        const uint8_t* qa = &q8s[r][n][64 * g];
+        const v4i a0 = *reinterpret_cast<const v4i*>(qa);
+        const v4i a1 = *reinterpret_cast<const v4i*>(qa + 16);
+        const v4i a2 = *reinterpret_cast<const v4i*>(qa + 32);
+        const v4i a3 = *reinterpret_cast<const v4i*>(qa + 48);
+        const v8i A0 = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const v8i A1 = v8i{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+        const v16f z = {};
+        v16f d0 = mfma_32x32x64_fp8(A0, cur.k[0][0], z);
+        d0 = mfma_32x32x64_fp8(A1, cur.k[0][1], d0);
+        v16f d1 = mfma_32x32x64_fp8(A0, cur.k[1][0], z);
+        d1 = mfma_32x32x64_fp8(A1, cur.k[1][1], d1);
+        // output register i of lane l is head 8*(i/4) + 4*g + i%4 for token l%32
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const v4f w = *reinterpret_cast<const v4f*>(&wps[r][8 * a + 4 * g]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc0 = fmaf(w[c], fmaxf(d0[4 * a + c], 0.f), acc0);
+            acc1 = fmaf(w[c], fmaxf(d1[4 * a + c], 0.f), acc1);
+          }
+        }
+        // lanes 0..31: (half-0 partial, partner's half-0 partial); lanes 32..63: half 1
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0),
+                                                         __float_as_uint(acc1), false, false);
+        const float score = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * cur.s;
+        if (t < L) scores[(int64_t)(r0 + r) * score_stride + t] = score;
+      }
+    }
+    if (more) cur = nxt;
+  }
+}
+
+__global__ __launch_bounds__(64) void quantize_q_kernel(const uint16_t* __restrict__ q,
+                                                        uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales, int dim) {
+  const int64_t rh = blockIdx.x;  // (row, head)
+  const int lane = threadIdx.x;
+  const uint16_t* src = q + rh * dim;
+  float am = 0.f;
+  for (int d = lane; d < dim; d += 64) am = fmaxf(am, fabsf(__uint_as_float((uint32_t)src[d] << 16)));
+  am = wave_max(am);
+  const int e = pow2_scale_exp(am);
+  const float inv = ldexpf(1.0f, -e);
+  for (int d = lane; d < dim; d += 64)
+    codes[rh * dim + d] = (uint8_t)cvt2_e4m3(__uint_as_float((uint32_t)src[d] << 16) * inv, 0.f);
+  if (lane == 0) scales[rh] = ldexpf(1.0f, e);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, uint8_t* codes,
+                             float* scales, hipStream_t st) {
+  const int64_t n = (int64_t)rows * heads;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)n), dim3(64), 0, st, q, codes, scales, dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_per_seq,
+                              const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
+                              const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
+                              const int32_t* block_table, int bt_stride, float* scores,
+                              int64_t score_stride, hipStream_t st) {
+  (void)n_q;
+  const int max_pages = (max_seq_len + kPage - 1) / kPage;
+  const unsigned gx = (unsigned)((max_pages + kPagesPerWg - 1) / kPagesPerWg);
+  int R = 8;
+  if (max_q_per_seq <= 1) R = 1;
+  else if (max_q_per_seq <= 2) R = 2;
+  else if (max_q_per_seq <= 4) R = 4;
+  const unsigned gz = (unsigned)((max_q_per_seq + R - 1) / R);
+  const dim3 grid(gx, (unsigned)num_seqs, gz), block(256);
+#define DSA_LAUNCH_IDX(RR)                                                                       \
+  hipLaunchKernelGGL(index_score_kernel<RR>, grid, block, 0, st, cu_q, seq_lens, q, head_w,      \
+                     key_pages, key_page_stride, block_table, bt_stride, scores, score_stride)
+  switch (R) {
+    case 1: DSA_LAUNCH_IDX(1); break;
+    case 2: DSA_LAUNCH_IDX(2); break;
+    case 4: DSA_LAUNCH_IDX(4); break;
+    default: DSA_LAUNCH_IDX(8); break;
+  }
+#undef DSA_LAUNCH_IDX
+  return hipGetLastError();
+}
+
+}  // namespace dsa

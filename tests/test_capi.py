@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry point,
+and rejects bad host arguments with the documented status before launching anything.
+None of these calls reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_decode_score_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.LIB_PATH):
+        from sparse_attention_decode_score_amd import build
+        build.build()
+    return dsa.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"dsa_index_score", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
+            "dsa_lse_combine", "dsa_quantize_q", "dsa_last_error", "dsa_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version(L):
+    assert "gfx950" in dsa.dsa_version()
+
+
+FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x1001)
+
+
+def _err():
+    return dsa.lib().dsa_last_error().decode()
+
+
+def test_index_score_rejects_bad_host_args(L):
+    f = L.dsa_index_score
+    ok_args = [2, 3, 1000, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 8448, FAKE, 16, FAKE, 1000, None]
+    bad = dict(enumerate(ok_args))
+    cases = [({0: 0}, 1, "num_seqs"), ({1: 1}, 1, "n_q"), ({2: 0}, 1, "max_seq_len"),
+             ({3: 0}, 1, "max_q_per_seq"), ({4: None}, 1, "cu_q"), ({8: None}, 1, "key_pages"),
+             ({9: 8447}, 1, "key_page_stride"), ({9: 8456}, 1, "key_page_stride"),
+             ({11: 15}, 1, "bt_stride"), ({13: 999}, 1, "score_stride"),
+             ({6: FAKE_ODD}, 1, "aligned")]
+    for patch, status, word in cases:
+        args = list(ok_args)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == status, patch
+        assert word in _err(), (patch, _err())
+
+
+def test_topk_rejects_bad_host_args(L):
+    f = L.dsa_topk
+    need = L.dsa_topk_workspace_size(3, 1000, 2048)
+    assert need > 0
+    base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE, ctypes.c_void_p(0x10000), need, None]
+    for patch, status in [({7: 0}, 2), ({7: 4097}, 2), ({8: None}, 1), ({6: 10}, 1),
+                          ({13: need - 1}, 3), ({12: None}, 3), ({12: ctypes.c_void_p(0x10010)}, 1)]:
+        args = list(base)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == status, (patch, _err())
+    assert L.dsa_topk_workspace_size(0, 10, 10) == 0
+    assert L.dsa_topk_workspace_size(4, 10, 5000) == 0
+
+
+def test_sparse_mla_and_combine_reject_bad_host_args(L):
+    f = L.dsa_sparse_mla_decode
+    base = [4, FAKE, FAKE, 36864, ctypes.c_float(0.01), FAKE, 2048, ctypes.c_float(0.04), 4, FAKE,
+            FAKE, None, None, None]
+    for patch, status in [({0: 0}, 1), ({6: 0}, 2), ({8: 0}, 2), ({8: 65}, 2), ({3: 36863}, 1),
+                          ({4: ctypes.c_float(0.0)}, 1), ({9: None}, 1), ({2: FAKE_ODD}, 1)]:
+        args = list(base)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == status, (patch, _err())
+    args = list(base)
+    args[6], args[8] = 3, 4                      # more splits than selected tokens
+    assert f(*args) == 1
+    args = list(base)
+    args[8] = 1                                  # one split needs out/lse
+    assert f(*args) == 1
+    g = L.dsa_lse_combine
+    assert g(0, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert g(65, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert g(4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert g(4, 4, None, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_quantize_rejects_bad_dim(L):
+    assert L.dsa_quantize_q(1, 1, 100, FAKE, FAKE, FAKE, None) == 2
+    assert "dim" in _err()
+    assert L.dsa_quantize_q(1, 1, 128, None, FAKE, FAKE, None) == 1
+
+
+def test_python_binding_refuses_host_tensors(L):
+    import torch
+    q = torch.zeros((1, 32, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dsa.dsa_quantize_q(q, torch.zeros((1, 32, 128), dtype=torch.uint8), torch.zeros((1, 32)))

@@ -1,0 +1,375 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle on the same seeded inputs.
+
+Small ragged batches span several tiles and chunk tails; the named workloads run at full
+size with sampled rows.  Top-k is compared bit for bit on identical fp32 scores (scores the
+oracle computed, uploaded to both sides); the indexer within 1e-3 relative; attention
+outputs within 2e-2 abs + 1e-2 rel and the LSE within 1e-4.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import sparse_attention_decode_score_amd as dsa
+from dsa_testlib import (check_attention, check_scores, host, latent_rows, oracle_scores,
+                         request_keys, topk_is_valid_for)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dsa.lib()
+
+
+def run_scores(batch):
+    wl = batch.wl
+    scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, scores, max_seq_len=wl.max_seq_len,
+                        max_q_per_seq=max(wl.q_per_seq))
+    torch.cuda.synchronize()
+    return scores
+
+
+def run_topk(batch, scores, k, with_slots=True):
+    wl = batch.wl
+    idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV) if with_slots else None
+    ws = torch.empty(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k), dtype=torch.uint8, device=DEV)
+    dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table if with_slots else None,
+                 idx, slot, ws, max_seq_len=wl.max_seq_len)
+    torch.cuda.synchronize()
+    return idx, slot
+
+
+def run_mla(batch, slots, num_splits):
+    n_q = batch.wl.n_q
+    if num_splits == 1:
+        out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
+        dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale, slots,
+                                  batch.softmax_scale, 1, out=out, lse=lse)
+        torch.cuda.synchronize()
+        return out, lse, None, None
+    op = torch.full((num_splits, n_q, 96, 512), float("nan"), device=DEV)
+    lp = torch.full((num_splits, n_q, 96), float("nan"), device=DEV)
+    dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale, slots,
+                              batch.softmax_scale, num_splits, o_part=op, lse_part=lp)
+    out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
+    dsa.dsa_lse_combine(op, lp, out, lse)
+    torch.cuda.synchronize()
+    return out, lse, op, lp
+
+
+# ------------------------------------------------------------------------ a0: quantisation
+@pytest.mark.parametrize("dim,heads", [(128, 32), (576, 96)])
+def test_query_quantisation_bit_exact(dim, heads):
+    say("quantise", dim)
+    g = torch.Generator().manual_seed(dim)
+    q = torch.randn((6, heads, dim), generator=g) * torch.logspace(-6, 4, 6).view(6, 1, 1)
+    q[0, 0] = 0.0                     # all-zero head -> scale 1
+    q[1, 1, :] = 1e-3
+    q[1, 1, 5] = -448.0 * 2.0 ** -7   # absmax exactly on a power-of-two boundary
+    qb = q.to(torch.bfloat16)
+    codes = torch.empty((6, heads, dim), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((6, heads), device=DEV)
+    dsa.dsa_quantize_q(qb.to(DEV), codes, scales)
+    torch.cuda.synchronize()
+    vals = qb.double().numpy()
+    for r in range(6):
+        ref_c, ref_s = O.quantize_heads(vals[r])
+        np.testing.assert_array_equal(scales[r].cpu().numpy().astype(np.float64), ref_s)
+        np.testing.assert_array_equal(codes[r].cpu().numpy(), ref_c)
+
+
+# ------------------------------------------------------------------------ a2: indexer
+SMALL = [
+    synth.custom([300, 64, 129, 1000], [1, 2, 3, 8], topk=128, seed=21, name="ragged"),
+    synth.custom([5000, 4097], [4, 5], topk=2048, seed=22, name="spec-small"),
+    synth.custom([1, 63, 65], [1, 1, 1], topk=16, seed=23, name="tiny-tails"),
+    synth.custom([2100], [20], topk=64, seed=24, name="many-rows"),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_index_scores_small(wl):
+    say("index", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    scores = run_scores(batch).cpu().numpy()
+    h = host(batch)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref, mag = oracle_scores(batch, row, keys=request_keys(batch, b, h["key_pool"], h["bt"]))
+        check_scores(scores[row, : pos + 1], ref, mag, f"{wl.name} row {row}")
+
+
+def test_index_scores_block_table_permutation_is_bit_identical():
+    wl = synth.custom([3000, 777], [2, 1], seed=25)
+    batch = synth.make_batch(wl, DEV)
+    s1 = run_scores(batch)
+    # move every page to a new physical location (and a packed stride of 8448 + 64)
+    P = batch.num_pages
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5)).to(DEV)
+    stride = 8448 + 64
+    pool2 = torch.full((P, stride), 0x7F, dtype=torch.uint8, device=DEV)
+    pool2[perm, :8448] = batch.key_pool
+    bt2 = torch.where(batch.block_table >= 0, perm[batch.block_table.long().clamp(min=0)].int(),
+                      batch.block_table)
+    scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, pool2, bt2.contiguous(),
+                        scores, max_seq_len=wl.max_seq_len, max_q_per_seq=2, key_page_stride=stride)
+    torch.cuda.synchronize()
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        assert torch.equal(s1[row, : pos + 1], scores[row, : pos + 1])
+
+
+# ------------------------------------------------------------------------ a3: top-k
+def _topk_case(lens, q_per, k, kind, seed):
+    """A batch whose score matrix is oracle-free synthetic data of a given structure."""
+    wl = synth.custom(lens, q_per, topk=k, seed=seed)
+    batch = synth.make_batch(wl, DEV)
+    sc = synth.random_scores(wl.n_q, wl.max_seq_len, seed, kind)
+    return wl, batch, sc
+
+
+TOPK_CASES = [
+    ([131072, 9000], [1, 2], 2048, "normal"),
+    ([8192, 8193, 16385, 2047], [1, 1, 1, 1], 2048, "normal"),
+    ([40000], [3], 4096, "ties"),
+    ([30000], [1], 2048, "equal"),
+    ([20000], [2], 1000, "signed_zero"),
+    ([50000], [1], 2048, "increasing"),
+    ([70000], [1], 100, "neg_inf_tail"),
+    ([5000, 3000], [1, 1], 1, "normal"),
+    ([3000], [1], 4096, "normal"),          # k >= visible: everything, then -1
+]
+
+
+@pytest.mark.parametrize("lens,q_per,k,kind", TOPK_CASES)
+def test_topk_bit_exact_on_identical_scores(lens, q_per, k, kind):
+    say("topk", lens, k, kind)
+    wl, batch, sc = _topk_case(lens, q_per, k, kind, seed=len(lens) * 100 + k)
+    idx, slot = run_topk(batch, sc.to(DEV), k)
+    idx, slot = idx.cpu().numpy(), slot.cpu().numpy()
+    bt = batch.block_table.cpu().numpy()
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref = O.topk_indices(sc[row, : pos + 1].numpy(), k)
+        got = idx[row]
+        n = min(k, pos + 1)
+        assert (got[n:] == -1).all()
+        assert np.array_equal(got[:n], np.sort(ref)), f"row {row}"
+        assert np.array_equal(slot[row, :n], O.physical_slot(bt[b], got[:n]))
+        assert (slot[row, n:] == -1).all()
+
+
+def test_topk_all_winners_in_one_chunk_forces_exact_reselect():
+    # every one of the top 2048 sits in chunk 3 of 16: that chunk can only send ~192
+    # candidates, so the exactness check must trigger the full re-selection
+    L = 131072
+    wl = synth.custom([L], [1], topk=2048, seed=31)
+    batch = synth.make_batch(wl, DEV)
+    sc = torch.randn((1, L), generator=torch.Generator().manual_seed(3))
+    sc[0, 3 * 8192: 3 * 8192 + 2500] += 100.0
+    idx, _ = run_topk(batch, sc.to(DEV), 2048)
+    ref = np.sort(O.topk_indices(sc[0].numpy(), 2048))
+    assert np.array_equal(idx[0].cpu().numpy(), ref)
+
+
+def test_topk_on_oracle_scores_of_a_real_batch():
+    wl = synth.custom([20000, 9000], [5, 1], topk=2048, seed=32)
+    batch = synth.make_batch(wl, DEV)
+    h = host(batch)
+    sc = torch.full((wl.n_q, wl.max_seq_len), -1e30)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        s, _ = oracle_scores(batch, row, keys=request_keys(batch, b, h["key_pool"], h["bt"]))
+        sc[row, : pos + 1] = torch.from_numpy(s)
+    idx, _ = run_topk(batch, sc.to(DEV), 2048)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref = np.sort(O.topk_indices(sc[row, : pos + 1].numpy(), 2048))
+        assert np.array_equal(idx[row].cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------------ a4 + a5: attention
+def _oracle_attention(batch, row, slots_row, num_splits):
+    slots_row = np.asarray(slots_row)
+    qm = batch.q_mla[row].cpu().double().numpy()
+    c, sm = batch.latent_scale, batch.softmax_scale
+    k = slots_row.shape[0]
+    parts = []
+    for a, e in O.split_ranges(k, num_splits):
+        seg = slots_row[a:e]
+        seg = seg[seg >= 0]
+        lat = latent_rows(batch, seg) if seg.size else np.zeros((0, 576), np.uint8)
+        parts.append(O.mla_attend(qm, lat, c, sm))
+    return parts
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16])
+def test_sparse_mla_small(num_splits):
+    say("mla", num_splits)
+    wl = synth.custom([3000, 700, 64], [2, 1, 1], topk=256, seed=41)
+    batch = synth.make_batch(wl, DEV)
+    # selections: random distinct visible tokens, the short request padded with -1
+    rng = np.random.default_rng(num_splits)
+    bt = batch.block_table.cpu().numpy()
+    slots = np.full((wl.n_q, 256), -1, np.int32)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        n = min(256, pos + 1)
+        t = np.sort(rng.choice(pos + 1, size=n, replace=False))
+        slots[row, :n] = O.physical_slot(bt[b], t)
+    slots_d = torch.from_numpy(slots).to(DEV)
+    out, lse, op, lp = run_mla(batch, slots_d, num_splits)
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for row in range(wl.n_q):
+        parts = _oracle_attention(batch, row, slots[row], num_splits)
+        o_ref, l_ref = O.lse_combine(parts)
+        check_attention(out[row], lse[row], o_ref, l_ref, f"row {row} S={num_splits}")
+        if num_splits > 1:
+            for s_, (po, pl) in enumerate(parts):
+                check_attention(op[s_, row].cpu().numpy(), lp[s_, row].cpu().numpy(), po, pl,
+                                f"row {row} split {s_}")
+
+
+def test_sparse_mla_topk_equal_to_context_is_dense_mla():
+    wl = synth.custom([2048], [1], topk=2048, seed=42)
+    batch = synth.make_batch(wl, DEV)
+    bt = batch.block_table.cpu().numpy()
+    slots = torch.from_numpy(O.physical_slot(bt[0], np.arange(2048)).astype(np.int32)[None]).to(DEV)
+    out, lse, _, _ = run_mla(batch, slots, 1)
+    lat = latent_rows(batch, slots[0].cpu().numpy())
+    o_d, l_d = O.dense_mla(batch.q_mla[0].cpu().double().numpy(), lat, batch.latent_scale,
+                           batch.softmax_scale)
+    check_attention(out[0].float().cpu().numpy(), lse[0].cpu().numpy(), o_d, l_d, "dense")
+
+
+def test_lse_combine_matches_oracle_with_empty_splits():
+    rng = np.random.default_rng(7)
+    S, n_q = 5, 3
+    o = rng.normal(size=(S, n_q, 96, 512)).astype(np.float32)
+    l = rng.normal(size=(S, n_q, 96)).astype(np.float32) * 3
+    l[1] = -np.inf
+    o[1] = 0
+    l[3, 2] = -np.inf
+    o[3, 2] = 0
+    l[:, 0, 7] = -np.inf                # one head empty in every split
+    o[:, 0, 7] = 0
+    out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((n_q, 96), device=DEV)
+    dsa.dsa_lse_combine(torch.from_numpy(o).to(DEV), torch.from_numpy(l).to(DEV), out, lse)
+    torch.cuda.synchronize()
+    for r in range(n_q):
+        ref_o, ref_l = O.lse_combine([(o[s, r].astype(np.float64), l[s, r].astype(np.float64))
+                                      for s in range(S)])
+        check_attention(out[r].float().cpu().numpy(), lse[r].cpu().numpy(), ref_o, ref_l, f"row {r}")
+
+
+# ------------------------------------------------------------------------ whole path
+def _end_to_end(wl, rows, num_splits=None):
+    S = num_splits or wl.num_splits
+    say("e2e", wl.name, "rows", rows, "S", S)
+    batch = synth.make_batch(wl, DEV)
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S)
+    out, lse = step.run(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, batch.q_mla, batch.latent_pool, batch.latent_scale,
+                        batch.softmax_scale, max(wl.q_per_seq))
+    torch.cuda.synchronize()
+    scores = step.scores
+    idx = step.topk_idx.cpu().numpy()
+    slots = step.topk_slot.cpu().numpy()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    rowpos = wl.row_positions()
+    for row in rows:
+        b, pos = rowpos[row]
+        keys = request_keys(batch, b)
+        ref, mag = oracle_scores(batch, row, keys=keys)
+        got_s = scores[row, : pos + 1].cpu().numpy()
+        check_scores(got_s, ref, mag, f"{wl.name} row {row}")
+        # the GPU's selection is a valid top-k of the GPU's own scores ...
+        assert topk_is_valid_for(got_s, idx[row], wl.topk)
+        # ... and agrees with the oracle's selection except where the two score sets differ
+        # within tolerance at the selection boundary
+        ref_sel = set(O.topk_indices(ref, wl.topk).tolist())
+        gsel = set(int(t) for t in idx[row] if t >= 0)
+        diff = ref_sel ^ gsel
+        if diff:
+            kth = np.sort(ref.astype(np.float64))[::-1][min(wl.topk, pos + 1) - 1]
+            for t in diff:
+                assert abs(float(ref[t]) - kth) <= 2e-3 * max(abs(kth), float(mag[t])), (row, t)
+        assert len(diff) <= 8, (row, len(diff))
+        # attention on the GPU's own selection, oracle from the same slots
+        parts = _oracle_attention(batch, row, slots[row], S)
+        o_ref, l_ref = O.lse_combine(parts)
+        check_attention(out[row], lse[row], o_ref, l_ref, f"{wl.name} row {row}")
+    return batch
+
+
+def test_end_to_end_tiny():
+    _end_to_end(synth.workload("tiny"), rows=[0])
+
+
+def test_end_to_end_spec_full_size():
+    wl = synth.workload("spec")
+    _end_to_end(wl, rows=[0, 4, 77, 159])
+
+
+def test_end_to_end_long_full_size():
+    wl = synth.workload("long")
+    _end_to_end(wl, rows=[0, 13, 31])
+
+
+@pytest.mark.slow
+def test_end_to_end_million_full_size():
+    wl = synth.workload("million")
+    _end_to_end(wl, rows=[0, 4])
+
+
+@pytest.mark.slow
+def test_end_to_end_prefill_full_size():
+    wl = synth.workload("prefill")
+    _end_to_end(wl, rows=[0, 1000, 2047])
+
+
+def test_batch_composition_does_not_change_a_row():
+    """A request's outputs are bitwise identical alone and inside a larger batch."""
+    lens, q_per = [6000, 9000, 3000], [1, 5, 2]
+    wl = synth.custom(lens, q_per, topk=2048, num_splits=4, seed=51)
+    big = synth.make_batch(wl, DEV)
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, 2048, 4)
+    out_big, lse_big = step.run(big.cu_q, big.seq_lens, big.q_idx, big.head_w, big.key_pool,
+                                big.block_table, big.q_mla, big.latent_pool, big.latent_scale,
+                                big.softmax_scale, 5)
+    out_big, lse_big = out_big.clone(), lse_big.clone()
+    # request 1 alone, same pools and block-table row
+    rows = slice(1, 6)
+    one = dsa.DecodeStep(5, wl.max_seq_len, 2048, 4)
+    cu = torch.tensor([0, 5], dtype=torch.int32, device=DEV)
+    out1, lse1 = one.run(cu, big.seq_lens[1:2].contiguous(), big.q_idx[rows].contiguous(),
+                         big.head_w[rows].contiguous(), big.key_pool, big.block_table[1:2].contiguous(),
+                         big.q_mla[rows].contiguous(), big.latent_pool, big.latent_scale,
+                         big.softmax_scale, 5)
+    torch.cuda.synchronize()
+    out1, lse1 = out1.clone(), lse1.clone()
+    assert torch.equal(out1, out_big[rows]) and torch.equal(lse1, lse_big[rows])
+    # and a repeat run is bitwise identical
+    out2, lse2 = one.run(cu, big.seq_lens[1:2].contiguous(), big.q_idx[rows].contiguous(),
+                         big.head_w[rows].contiguous(), big.key_pool, big.block_table[1:2].contiguous(),
+                         big.q_mla[rows].contiguous(), big.latent_pool, big.latent_scale,
+                         big.softmax_scale, 5)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
