@@ -1,0 +1,284 @@
+"""Benchmark of the MI355X DSA decode hot path: one step = indexer scores -> top-2048 ->
+sparse MLA over the selected latents -> LSE combine of the split partials, for every query
+row of one synthetic batch (the four library calls on one stream).
+
+Default workload: decode of 32 requests x 1 query row at 131,072 tokens of context each
+(FP8 index keys 132 B/token, FP8 latents 576 B/token, top-2048, 16 splits).  Prints ONE
+JSON line.  `value` is the whole step's algorithmic HBM traffic divided by its time (GB/s);
+the JSON also carries us/layer, the indexer kernel's roofline, and the CPU oracle timed on
+a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|spec|...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, vendor figure
+PAGE = 64
+IDX_BYTES_PER_TOKEN = 132        # 128 B E4M3 key + 4 B fp32 scale
+LAT_BYTES_PER_TOKEN = 576        # E4M3 latent
+QIDX_BYTES_PER_ROW = 32 * 128 * 2 + 32 * 4     # bf16 indexer query + fp32 head weights
+QMLA_BYTES_PER_ROW = 96 * 576 * 2              # bf16 MLA query
+OUT_BYTES_PER_ROW = 96 * 512 * 2 + 96 * 4      # bf16 output + fp32 LSE
+BT_BYTES_PER_PAGE = 4
+
+
+def algorithmic_bytes(seq_lens, q_per_seq, topk):
+    """Bytes the method itself must move for one step (the byte model of the K3.1 page's
+    "Sparse attention cuts long-context decode bandwidth" section: the whole context's
+    132-byte index keys once per request, 576 bytes for each selected token of each row,
+    plus queries, outputs and the block table).  Returns a dict of parts and the total."""
+    keys = sum(L * IDX_BYTES_PER_TOKEN for L in seq_lens)
+    lat = 0
+    n_rows = 0
+    for L, nq in zip(seq_lens, q_per_seq):
+        for j in range(nq):
+            pos = L - nq + j
+            lat += min(topk, pos + 1) * LAT_BYTES_PER_TOKEN
+        n_rows += nq
+    bt = sum(((L + PAGE - 1) // PAGE) * BT_BYTES_PER_PAGE for L in seq_lens)
+    q = n_rows * (QIDX_BYTES_PER_ROW + QMLA_BYTES_PER_ROW)
+    out = n_rows * OUT_BYTES_PER_ROW
+    parts = {"index_keys": keys, "latents": lat, "queries": q, "outputs": out, "block_table": bt}
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def index_score_bytes(seq_lens):
+    """Algorithmic bytes of one dsa_index_score launch: 132 B per context token of every
+    request (keys are read once and shared by that request's rows)."""
+    return sum(L * IDX_BYTES_PER_TOKEN for L in seq_lens)
+
+
+def dense_mla_bytes(seq_lens, q_per_seq):
+    """Bytes a dense-MLA decode reads for the same batch: every context token's latent."""
+    return sum(L * LAT_BYTES_PER_TOKEN for L in seq_lens)
+
+
+def _source_hash(name):
+    p = os.path.join(ROOT, "sparse_attention_decode_score_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(kernel_src):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; None otherwise."""
+    p = os.path.join(ROOT, "profiles", "index_score_long_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_sha256_16") != _source_hash(kernel_src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(batch, rows, budget_s=20.0):
+    """Times the oracle (as it stands) on a bounded sample of rows of the same workload and
+    returns throughput in the benchmark's unit (algorithmic GB/s)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle as O
+
+    wl = batch.wl
+    rowpos = wl.row_positions()
+    done, t_total, byts = 0, 0.0, 0
+    for row in rows:
+        b, pos = rowpos[row]
+        L = wl.seq_lens[b]
+        pages = batch.block_table[b, : (L + 63) // 64].long()
+        key_pages = batch.key_pool[pages].cpu().numpy()
+        bt_local = np.arange(len(pages))
+        qi = batch.q_idx[row].cpu().double().numpy()
+        w = batch.head_w[row].cpu().numpy()
+        qm = batch.q_mla[row].cpu().double().numpy()
+        lat_pages = batch.latent_pool[pages].cpu().numpy()
+        t0 = time.perf_counter()
+        kc, ks = O.read_index_keys(key_pages, bt_local, L)
+        scores = O.index_scores(qi, w, kc[: pos + 1], ks[: pos + 1])
+        sel = O.topk_indices(scores, wl.topk)
+        lat = O.read_latents(lat_pages, O.physical_slot(bt_local, sel))
+        parts = [O.mla_attend(qm, lat[a:e], batch.latent_scale, batch.softmax_scale)
+                 for a, e in O.split_ranges(len(sel), wl.num_splits)]
+        O.lse_combine(parts)
+        t_total += time.perf_counter() - t0
+        # the row's share of the algorithmic bytes: its request's keys divided over the
+        # request's rows, its selected latents, its query / output
+        nq = wl.q_per_seq[b]
+        byts += (L * IDX_BYTES_PER_TOKEN) / nq + min(wl.topk, pos + 1) * LAT_BYTES_PER_TOKEN \
+            + QIDX_BYTES_PER_ROW + QMLA_BYTES_PER_ROW + OUT_BYTES_PER_ROW
+        done += 1
+        if t_total > budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} query rows of the {wl.name} workload (rows {list(rows)[:done]}), "
+                      f"whole path per row, {t_total:.1f} s of CPU time; GB/s = those rows' "
+                      f"share of the algorithmic bytes / time"}
+
+
+def stream_read_ceiling(torch, n_bytes=4 << 30):
+    """Achievable streaming-read rate of this GPU: a large fp32 sum (read-bound)."""
+    x = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 5 * n_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
+    return gbps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--splits", type=int, default=0, help="sparse-attention splits (0 = workload default)")
+    ap.add_argument("--no-flush", action="store_true", help="keep the 256 MB last-level cache warm")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import sparse_attention_decode_score_amd as dsa
+
+    wl = synth.workload(args.workload)
+    S = args.splits or wl.num_splits
+    torch.cuda.set_device(0)
+    batch = synth.make_batch(wl, "cuda")
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one_step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                            batch.block_table, step.scores, max_seq_len=wl.max_seq_len,
+                            max_q_per_seq=max(wl.q_per_seq))
+        if evs:
+            evs[1].record(stream)
+        dsa.dsa_topk(batch.cu_q, batch.seq_lens, step.scores, wl.topk, batch.block_table,
+                     step.topk_idx, step.topk_slot, step.workspace, max_seq_len=wl.max_seq_len)
+        if evs:
+            evs[2].record(stream)
+        if S == 1:
+            dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale,
+                                      step.topk_slot, batch.softmax_scale, 1, out=step.out,
+                                      lse=step.lse)
+            if evs:
+                evs[3].record(stream)
+                evs[4].record(stream)
+        else:
+            dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale,
+                                      step.topk_slot, batch.softmax_scale, S, o_part=step.o_part,
+                                      lse_part=step.lse_part)
+            if evs:
+                evs[3].record(stream)
+            dsa.dsa_lse_combine(step.o_part, step.lse_part, step.out, step.lse)
+            if evs:
+                evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush_buf.fill_(1)
+        one_step()
+    torch.cuda.synchronize()
+
+    per_step = []
+    stage = [[], [], [], []]
+    t_wall0 = time.perf_counter()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        if not args.no_flush:
+            flush_buf.fill_(1)          # evict the last-level cache, outside the events
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        one_step(evs)
+        per_step.append(evs)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    for evs in per_step:
+        for i in range(4):
+            stage[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
+    step_us = [sum(s[i] for s in stage) for i in range(args.steps)]
+    step_us_sorted = sorted(step_us)
+    med = step_us_sorted[len(step_us_sorted) // 2]
+    mean_us = sum(step_us) / len(step_us)
+    stage_mean = [sum(s) / len(s) for s in stage]
+
+    ab = algorithmic_bytes(wl.seq_lens, wl.q_per_seq, wl.topk)
+    value = ab["total"] / (mean_us * 1e-6) / 1e9
+    idx_bytes = index_score_bytes(wl.seq_lens)
+    idx_gbps = idx_bytes / (stage_mean[0] * 1e-6) / 1e9
+    traffic = _traffic_from_profile("index_score.hip")
+    ceiling = stream_read_ceiling(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del flush_buf
+        rows = list(range(0, wl.n_q, max(1, wl.n_q // 8)))
+        cpu = cpu_baseline(batch, rows, budget_s=args.cpu_budget)
+
+    rec = {
+        "metric": "DSA decode µs/layer & HBM GB/s (%peak) at 128K ctx, batch 32",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_us / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 MFMA, fp32 accumulate, bf16 in/out",
+        "data": "synthetic (seeded N(0,1) queries/keys/latents, E4M3-quantised caches, "
+                "shuffled 64-token pages)",
+        "config": {"workload": wl.name, "batch": wl.num_seqs, "query_rows": wl.n_q,
+                   "context": wl.max_seq_len if len(set(wl.seq_lens)) == 1 else "ragged",
+                   "topk": wl.topk, "num_splits": S, "page_size": PAGE,
+                   "flush_llc_between_steps": not args.no_flush},
+        "us_per_layer": round(mean_us, 2),
+        "us_per_layer_median": round(med, 2),
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "stage_us": {"index_score": round(stage_mean[0], 2), "topk": round(stage_mean[1], 2),
+                     "sparse_mla": round(stage_mean[2], 2), "lse_combine": round(stage_mean[3], 2)},
+        "algorithmic_bytes": ab,
+        "dsa_vs_dense_mla_bytes": round(ab["total"] / dense_mla_bytes(wl.seq_lens, wl.q_per_seq), 4),
+        "roofline": {"kernel": "dsa_index_score", "bound": "hbm", "achieved": round(idx_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": idx_bytes,
+                     "avg_launch_us": round(stage_mean[0], 2)},
+        "stream_read_ceiling_GBps": round(ceiling, 1),
+        "wall_s_timed_loop": round(t_wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec, ensure_ascii=False))
+
+
+if __name__ == "__main__":
+    main()

@@ -14,6 +14,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdsa.so")
 SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "lse_combine.hip", "capi.cpp"]
+# measurement kernels used by the benchmark only (streaming-read ceiling, page-read rate)
+PROBE_LIB = os.path.join(LIBDIR, "libdsa_probe.so")
+PROBE_SOURCES = ["bandwidth_probe.hip"]
 
 
 def hipcc() -> str:
@@ -38,21 +41,27 @@ def _compile(src: str, obj: str) -> None:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
 
 
+def _link(sources, out, tmp):
+    objs = [os.path.join(tmp, s + ".o") for s in sources]
+    with cf.ThreadPoolExecutor(max_workers=min(len(sources), os.cpu_count() or 4)) as ex:
+        list(ex.map(_compile, sources, objs))
+    out_tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(out_tmp, out)
+
+
 def build(verbose: bool = False) -> str:
-    """Compiles every source for gfx950 and links lib/libdsa.so; returns its path."""
+    """Compiles every source for gfx950 and links lib/libdsa.so (and the benchmark's
+    measurement library lib/libdsa_probe.so); returns the path of libdsa.so."""
     os.makedirs(LIBDIR, exist_ok=True)
     with tempfile.TemporaryDirectory() as tmp:
-        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
-        with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-            list(ex.map(_compile, SOURCES, objs))
-        out_tmp = LIB + ".tmp"
-        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed:\n{r.stderr}")
-        os.replace(out_tmp, LIB)
+        _link(SOURCES, LIB, tmp)
+        _link(PROBE_SOURCES, PROBE_LIB, tmp)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
