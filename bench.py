@@ -129,16 +129,33 @@ def cpu_baseline(batch, rows, budget_s=20.0):
                       f"share of the algorithmic bytes / time"}
 
 
+def _probe_lib():
+    import ctypes
+    import sparse_attention_decode_score_amd as dsa
+    path = os.path.join(dsa.PKG, "lib", "libdsa_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the package first")
+    L = ctypes.CDLL(path)
+    L.dsa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
+    L.dsa_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
 def stream_read_ceiling(torch, n_bytes=4 << 30):
-    """Achievable streaming-read rate of this GPU: a large fp32 sum (read-bound)."""
-    x = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    """Achievable streaming-read rate of this GPU with ordinary loads (our probe kernel)."""
+    L = _probe_lib()
+    x = torch.ones(n_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
     for _ in range(2):
-        x.sum()
+        L.dsa_probe_stream_read(x.data_ptr(), n_bytes, sink.data_ptr(), 8192, st)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(5):
-        x.sum()
+        L.dsa_probe_stream_read(x.data_ptr(), n_bytes, sink.data_ptr(), 8192, st)
     e1.record()
     torch.cuda.synchronize()
     gbps = 5 * n_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
@@ -156,6 +173,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep the 256 MB last-level cache warm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 512 MiB device copy (reference dispatch for counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -172,8 +191,16 @@ def main():
     torch.cuda.set_device(0)
     batch = synth.make_batch(wl, "cuda")
     step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    probe = _probe_lib()
+    flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    flush_sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def flush():
+        # evict the 256 MB last-level cache by streaming 1 GiB of reads: clean lines, so the
+        # next kernel pays no write-back for the flush
+        probe.dsa_probe_stream_read(flush_buf.data_ptr(), flush_buf.numel(), flush_sink.data_ptr(),
+                                    8192, stream.cuda_stream)
 
     def one_step(evs=None):
         if evs:
@@ -190,14 +217,14 @@ def main():
         if S == 1:
             dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale,
                                       step.topk_slot, batch.softmax_scale, 1, out=step.out,
-                                      lse=step.lse)
+                                      lse=step.lse, workspace=step.mla_workspace)
             if evs:
                 evs[3].record(stream)
                 evs[4].record(stream)
         else:
             dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale,
                                       step.topk_slot, batch.softmax_scale, S, o_part=step.o_part,
-                                      lse_part=step.lse_part)
+                                      lse_part=step.lse_part, workspace=step.mla_workspace)
             if evs:
                 evs[3].record(stream)
             dsa.dsa_lse_combine(step.o_part, step.lse_part, step.out, step.lse)
@@ -206,7 +233,7 @@ def main():
 
     for _ in range(args.warmup):
         if not args.no_flush:
-            flush_buf.fill_(1)
+            flush()
         one_step()
     torch.cuda.synchronize()
 
@@ -216,7 +243,7 @@ def main():
     torch.cuda.synchronize()
     for _ in range(args.steps):
         if not args.no_flush:
-            flush_buf.fill_(1)          # evict the last-level cache, outside the events
+            flush()                     # outside the events
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         one_step(evs)
         per_step.append(evs)
@@ -237,6 +264,12 @@ def main():
     idx_gbps = idx_bytes / (stage_mean[0] * 1e-6) / 1e9
     traffic = _traffic_from_profile("index_score.hip")
     ceiling = stream_read_ceiling(torch)
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

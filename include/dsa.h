@@ -18,7 +18,7 @@
  *
  * Conventions shared by every call
  *  - Every pointer is a DEVICE pointer on the current HIP device unless marked (host).
- *    The caller owns and allocates all memory, including the top-k workspace.
+ *    The caller owns and allocates all memory, including the workspaces.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work
  *    on it: no allocation, no host synchronisation, no device-to-host reads.
  *  - Host scalars and pointer nullness/alignment are validated before anything is
@@ -62,7 +62,7 @@ typedef enum {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or inconsistent host scalars */
   DSA_ERR_UNSUPPORTED = 2,   /* shape the library does not implement */
-  DSA_ERR_WORKSPACE = 3,     /* workspace smaller than dsa_topk_workspace_size() */
+  DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than its *_workspace_size() */
   DSA_ERR_LAUNCH = 4         /* the HIP runtime rejected a launch */
 } dsa_status;
 
@@ -139,12 +139,17 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
  *   S > 1:  o_part fp32 [S][n_q][96][512] (each split normalised by its own sum) and
  *           lse_part fp32 [S][n_q][96] are written (out_bf16 / lse unused); an empty
  *           split has O = 0 and LSE = -inf.  Merge them with dsa_lse_combine.
+ *   workspace: device memory of at least dsa_sparse_mla_workspace_size(n_q) bytes,
+ *   256-byte aligned, scratch for the call (it receives the FP8 query codes and scales
+ *   that every split of a row shares, so the query is quantised once per row).
  */
+size_t dsa_sparse_mla_workspace_size(int32_t n_q);
 dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* latent_pages,
                                  int64_t latent_page_stride, float latent_scale,
                                  const int32_t* topk_slot, int32_t k, float softmax_scale,
                                  int32_t num_splits, float* o_part, float* lse_part,
-                                 void* out_bf16, float* lse, void* stream);
+                                 void* out_bf16, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Stage 4 — log-sum-exp merge of split partials:

@@ -51,8 +51,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ, _P]
+        L.dsa_sparse_mla_workspace_size.argtypes = [_I32]
+        L.dsa_sparse_mla_workspace_size.restype = _SZ
         L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _I64, _F32, _P, _I32, _F32, _I32, _P, _P,
-                                            _P, _P, _P]
+                                            _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -150,11 +152,24 @@ def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k
                           _stream(stream)))
 
 
+def dsa_sparse_mla_workspace_size(n_q: int) -> int:
+    return int(lib().dsa_sparse_mla_workspace_size(int(n_q)))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A 256-byte aligned uint8 device buffer of nbytes (torch's allocator is aligned)."""
+    t = torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+    if t.data_ptr() % 256:
+        raise RuntimeError("allocator returned a buffer that is not 256-byte aligned")
+    return t
+
+
 def dsa_sparse_mla_decode(q_mla: torch.Tensor, latent_pages: torch.Tensor, latent_scale: float,
                           topk_slot: torch.Tensor, softmax_scale: float, num_splits: int, *,
                           o_part: Optional[torch.Tensor] = None,
                           lse_part: Optional[torch.Tensor] = None,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None,
                           latent_page_stride: Optional[int] = None, stream=None) -> None:
     """MLA over the selected slots: (out, lse) when num_splits == 1, else (o_part, lse_part)."""
     n_q = q_mla.shape[0]
@@ -169,10 +184,14 @@ def dsa_sparse_mla_decode(q_mla: torch.Tensor, latent_pages: torch.Tensor, laten
         _expect(lse_part, "lse_part", torch.float32, (num_splits, n_q, MLA_HEADS))
     stride = (latent_page_stride if latent_page_stride is not None
               else latent_pages.stride(0) * latent_pages.element_size())
+    if workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_mla_workspace_size(n_q), q_mla.device)
+    _expect(workspace, "workspace", torch.uint8)
     _check(lib().dsa_sparse_mla_decode(n_q, _ptr(q_mla), _ptr(latent_pages), int(stride),
                                        float(latent_scale), _ptr(topk_slot), int(k),
                                        float(softmax_scale), int(num_splits), _ptr(o_part),
-                                       _ptr(lse_part), _ptr(out), _ptr(lse), _stream(stream)))
+                                       _ptr(lse_part), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
 
 
 def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
@@ -200,10 +219,8 @@ class DecodeStep:
         self.scores = torch.empty((n_q, max_seq_len), dtype=torch.float32, device=dev)
         self.topk_idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
         self.topk_slot = torch.empty((n_q, k), dtype=torch.int32, device=dev)
-        ws = dsa_topk_workspace_size(n_q, max_seq_len, k)
-        self.workspace = torch.empty((ws + 256,), dtype=torch.uint8, device=dev)
-        off = (-self.workspace.data_ptr()) % 256
-        self.workspace = self.workspace[off:off + ws]
+        self.workspace = workspace(dsa_topk_workspace_size(n_q, max_seq_len, k), dev)
+        self.mla_workspace = workspace(dsa_sparse_mla_workspace_size(n_q), dev)
         self.out = torch.empty((n_q, MLA_HEADS, V_DIM), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)
         if num_splits > 1:
@@ -220,10 +237,11 @@ class DecodeStep:
                  self.workspace, max_seq_len=self.max_seq_len, stream=stream)
         if self.num_splits == 1:
             dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
-                                  1, out=self.out, lse=self.lse, stream=stream)
+                                  1, out=self.out, lse=self.lse, workspace=self.mla_workspace,
+                                  stream=stream)
         else:
             dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
                                   self.num_splits, o_part=self.o_part, lse_part=self.lse_part,
-                                  stream=stream)
+                                  workspace=self.mla_workspace, stream=stream)
             dsa_lse_combine(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
         return self.out, self.lse

@@ -131,11 +131,17 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
                   "dsa_topk");
 }
 
+size_t dsa_sparse_mla_workspace_size(int32_t n_q) {
+  if (n_q < 1) return 0;
+  return dsa::sparse_mla_workspace_bytes(n_q);
+}
+
 dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* latent_pages,
                                  int64_t latent_page_stride, float latent_scale,
                                  const int32_t* topk_slot, int32_t k, float softmax_scale,
                                  int32_t num_splits, float* o_part, float* lse_part,
-                                 void* out_bf16, float* lse, void* stream) {
+                                 void* out_bf16, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
   if (num_splits < 1 || num_splits > DSA_MAX_SPLITS)
@@ -155,11 +161,16 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* la
     DSA_REQUIRE(o_part && lse_part, "num_splits > 1 needs o_part and lse_part");
     DSA_REQUIRE(aligned(o_part, 16), "o_part must be 16-byte aligned");
   }
+  const size_t need = dsa::sparse_mla_workspace_bytes(n_q);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
   return launched(dsa::launch_sparse_mla(n_q, static_cast<const uint16_t*>(q_bf16),
                                          static_cast<const uint8_t*>(latent_pages),
                                          latent_page_stride, latent_scale, topk_slot, k,
                                          softmax_scale, num_splits, o_part, lse_part,
-                                         static_cast<uint16_t*>(out_bf16), lse,
+                                         static_cast<uint16_t*>(out_bf16), lse, workspace,
                                          static_cast<hipStream_t>(stream)),
                   "dsa_sparse_mla_decode");
 }

@@ -30,11 +30,12 @@ hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu
                        const int32_t* block_table, int bt_stride, int32_t* topk_idx,
                        int32_t* topk_slot, void* workspace, hipStream_t st);
 
+size_t sparse_mla_workspace_bytes(int n_q);
 hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* latent_pages,
                              int64_t latent_page_stride, float latent_scale,
                              const int32_t* topk_slot, int k, float softmax_scale, int num_splits,
                              float* o_part, float* lse_part, uint16_t* out_bf16, float* lse,
-                             hipStream_t st);
+                             void* workspace, hipStream_t st);
 
 hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
                               uint16_t* out_bf16, float* lse, hipStream_t st);

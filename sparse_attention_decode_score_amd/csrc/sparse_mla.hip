@@ -9,20 +9,21 @@
 // here that is the split index s of a (split, row) workgroup.
 //
 // Workgroup = 8 waves on one CU.  Waves 6, 7 gather 64-token latent tiles (slot -> page ->
-// 576 bytes) into a double-buffered LDS ring.  Waves 0..5 each own 32 heads x 256 value dims
-// of the row (the two waves of a head tile both form that tile's logits); the FP8 query
-// sits in LDS as the B operand of
-//   S[token][head] = L8[64 tokens x 576] * Q8^T          (9 x v_mfma 32x32x64 per 32 tokens)
-// The A rows are permuted so that lane l ends up holding head l%32's logits for tokens
-// 32*(l/32) .. +31 in order; after an online softmax in the log2 domain those 32
-// probabilities are converted to E4M3 in place and are directly the A operand of
-//   O[head][dim] += P8[32 heads x 64 tokens] * V8[64 tokens x 512]   (16 x v_mfma 32x32x64)
+// 576 bytes, non-temporal loads) into a double-buffered LDS ring.  Waves 0..5 each own 32
+// heads x 256 value dims of the row.  The query is quantised once per row (E4M3 codes and
+// power-of-two scales in the workspace) and copied to LDS, where it is the B operand of
+//   S[token][head] = L8[32 tokens x 576] * Q8^T          (9 x v_mfma 32x32x64 per 32 tokens)
+// The two waves of a head tile each form the logits of one 32-token half of a tile; the A
+// rows are permuted so that lane l holds head l%32's logits for tokens 32*(l/32) + 16*half
+// + i.  They exchange per-head maxima and the probabilities through LDS, so each wave gets
+// the E4M3 A operand of
+//   O[head][dim] += P8[32 heads x 64 tokens] * V8[64 tokens x 256 dims]   (8 x v_mfma 32x32x64)
 // whose B operand comes from the same LDS tile through ds_read_b64_tr_b8 (8 tokens of one
 // dim per lane), so the value matrix is never transposed in memory.  Each compute wave keeps
-// its 32x256 fp32 accumulator in AGPRs.  The running max is only raised when a tile's max
-// exceeds it by more than 2^4, so the accumulator rescale is rare; probabilities stay below
-// 2^4 and are scaled by 2^4 before conversion to a two-term E4M3 pair (hi + residual), which
-// keeps about 8 significant bits through the value product.
+// its 32x256 fp32 accumulator in registers.  The running max is only raised when a tile's
+// max exceeds it by more than 2^4, so the accumulator rescale is rare; probabilities stay
+// below 2^4 and are scaled by 2^4 before conversion to a two-term E4M3 pair (hi + residual),
+// which keeps about 8 significant bits through the value product.
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
 
@@ -45,14 +46,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ lat_pages, int64_t page_stride,
-    float lat_scale, const int32_t* __restrict__ topk_slot, int k, float sm_scale, int num_splits,
-    int n_q, float* __restrict__ o_part, float* __restrict__ lse_part,
-    uint16_t* __restrict__ out_bf16, float* __restrict__ lse_out) {
+    const uint8_t* __restrict__ q8, const float* __restrict__ qscale,
+    const uint8_t* __restrict__ lat_pages, int64_t page_stride, float lat_scale,
+    const int32_t* __restrict__ topk_slot, int k, float sm_scale, int num_splits, int n_q,
+    float* __restrict__ o_part, float* __restrict__ lse_part, uint16_t* __restrict__ out_bf16,
+    float* __restrict__ lse_out) {
   __shared__ __attribute__((aligned(16))) uint8_t lat[2][kTile * kRowStride];
   __shared__ __attribute__((aligned(16))) uint8_t q8s[kMlaHeads * kRowStride];
-  __shared__ uint64_t valid_mask[2];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[3][2][32][64];  // [head tile][hi/lo][head][token]
+  __shared__ __attribute__((aligned(16))) float xmax[3][2][32];
   __shared__ __attribute__((aligned(16))) float xfer[6][32];
+  __shared__ uint64_t valid_mask[2];
 
   const int s = blockIdx.x, row = blockIdx.y;
   const int beg = (int)((int64_t)s * k / num_splits);
@@ -82,7 +86,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 #pragma unroll
         for (int c = 0; c < 9; ++c) {
           const int piece = (lane & 3) + 4 * c;
-          data[qq][c] = slot >= 0 ? *reinterpret_cast<const v4i*>(src + piece * 16) : v4i{0, 0, 0, 0};
+          data[qq][c] = slot >= 0
+                            ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + piece * 16))
+                            : v4i{0, 0, 0, 0};
         }
       }
 #pragma unroll
@@ -100,106 +106,83 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         if (lane == 0) valid_mask[buf] = m;
       }
     };
-    // every wave executes the same barriers: one before the loop and one per tile
+    // every wave executes the same barriers: one before the loop, three per tile and the
+    // two of the compute waves' finalize step
     if (n_tiles > 0) load_tile(0, 0);
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
       if (t + 1 < n_tiles) load_tile(t + 1, (t + 1) & 1);
       __syncthreads();
+      __syncthreads();
+      __syncthreads();
     }
+    __syncthreads();
+    __syncthreads();
     return;
   }
 
   // ------------------------------------------------------------------ compute waves
   const int ht = wave >> 1;  // head tile: heads 32*ht .. +31
-  const int dh = wave & 1;   // value-dim half: dims 256*dh .. +255
-  // B operand of the logits: FP8 query of head 32*ht + n in LDS
-  uint8_t* qrow = q8s + (32 * ht + n) * kRowStride + 32 * g;
-  float mult;  // sq * latent_scale * softmax_scale * log2(e) for that head
+  const int hf = wave & 1;   // token half of each tile for the logits, value-dim half for O
+  // FP8 query of the row -> LDS (rows padded to kRowStride), coalesced 16-byte pieces
   {
-    // fused query prep: E4M3 codes with one power-of-two scale per (row, head); both
-    // waves of a head tile compute the same codes, the dh == 0 wave stores them
-    const uint16_t* src = q + ((int64_t)row * kMlaHeads + 32 * ht + n) * kLatDim + 32 * g;
-    float am = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 9; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i u = *reinterpret_cast<const v4i*>(src + 64 * kb + 8 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          am = fmaxf(am, fabsf(bf16_lo((uint32_t)u[e])));
-          am = fmaxf(am, fabsf(bf16_hi((uint32_t)u[e])));
-        }
-      }
-    am = fmaxf(am, __shfl_xor(am, 32, 64));
-    const int ex = pow2_scale_exp(am);
-    const float inv = ldexpf(1.0f, -ex);
-    if (dh == 0) {
-#pragma unroll
-      for (int kb = 0; kb < 9; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v4i u = *reinterpret_cast<const v4i*>(src + 64 * kb + 8 * j);
-          v2i c;
-          c[0] = (int)cvt4_e4m3(bf16_lo((uint32_t)u[0]) * inv, bf16_hi((uint32_t)u[0]) * inv,
-                                bf16_lo((uint32_t)u[1]) * inv, bf16_hi((uint32_t)u[1]) * inv);
-          c[1] = (int)cvt4_e4m3(bf16_lo((uint32_t)u[2]) * inv, bf16_hi((uint32_t)u[2]) * inv,
-                                bf16_lo((uint32_t)u[3]) * inv, bf16_hi((uint32_t)u[3]) * inv);
-          *reinterpret_cast<v2i*>(qrow + 64 * kb + 8 * j) = c;
-        }
+    const uint8_t* src = q8 + (int64_t)row * kMlaHeads * kLatDim;
+    for (int i = threadIdx.x; i < kMlaHeads * (kLatDim / 16); i += 384) {
+      const int h = i / (kLatDim / 16), pc = i % (kLatDim / 16);
+      *reinterpret_cast<v4i*>(&q8s[h * kRowStride + pc * 16]) =
+          *reinterpret_cast<const v4i*>(src + (int64_t)i * 16);
     }
-    mult = ldexpf(1.0f, ex) * lat_scale * sm_scale * kLog2e;
   }
-  v16f acc[8];  // O[32 heads][256 dims] of this wave; acc[dt] covers dims 256*dh + 32*dt .. +31
+  const float mult = qscale[(int64_t)row * kMlaHeads + 32 * ht + n] * lat_scale * sm_scale * kLog2e;
+  const uint8_t* qrow = q8s + (32 * ht + n) * kRowStride + 32 * g;
+  v16f acc[8];  // O[32 heads][256 dims] of this wave; acc[dt] covers dims 256*hf + 32*dt .. +31
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc[dt] = v16f{};
-  float m_run = -INFINITY;  // running max (log2 units) of head n
+  float m_run = -INFINITY;  // running max (log2 units) of head n, identical in both waves
   float z_run = 0.f;        // this lane's share of the running sum of head n
   bool started = false;
   __syncthreads();
 
   const int grp = lane >> 4, li = lane & 15;
+  // MFMA row n -> tile token 32*((n>>2)&1) + 16*hf + 4*(n>>3) + (n&3)
+  const int tok = 32 * ((n >> 2) & 1) + 16 * hf + 4 * (n >> 3) + (n & 3);
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const uint8_t* tile = lat[buf];
     const uint64_t vm = valid_mask[buf];
+    // ---- logits of this wave's token half: lane holds head n, tokens 32*g + 16*hf + i
+    float x[16];
+    float mx = -INFINITY;
     if (vm != 0ull) {
-      // ---- logits: lane holds head n, tokens 32*g + 16*T + i
-      float x[32];
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        // MFMA row n -> tile token 32*((n>>2)&1) + 16*T + 4*(n>>3) + (n&3)
-        const int tok = 32 * ((n >> 2) & 1) + 16 * T + 4 * (n >> 3) + (n & 3);
-        const uint8_t* arow = tile + tok * kRowStride + 32 * g;
-        v16f d = {};
-        // k-block loop kept rolled (register budget) with the next block's operands
-        // fetched from LDS before the current MFMA issues
-        v4i a0 = *reinterpret_cast<const v4i*>(arow);
-        v4i a1 = *reinterpret_cast<const v4i*>(arow + 16);
-        v4i b0 = *reinterpret_cast<const v4i*>(qrow);
-        v4i b1 = *reinterpret_cast<const v4i*>(qrow + 16);
+      const uint8_t* arow = tile + tok * kRowStride + 32 * g;
+      v16f d = {};
+      v4i a0 = *reinterpret_cast<const v4i*>(arow);
+      v4i a1 = *reinterpret_cast<const v4i*>(arow + 16);
+      v4i b0 = *reinterpret_cast<const v4i*>(qrow);
+      v4i b1 = *reinterpret_cast<const v4i*>(qrow + 16);
 #pragma unroll 1
-        for (int kb = 0; kb < 9; ++kb) {
-          const v8i A = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          const v8i B = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          const int nx = kb < 8 ? 64 * (kb + 1) : 64 * kb;
-          a0 = *reinterpret_cast<const v4i*>(arow + nx);
-          a1 = *reinterpret_cast<const v4i*>(arow + nx + 16);
-          b0 = *reinterpret_cast<const v4i*>(qrow + nx);
-          b1 = *reinterpret_cast<const v4i*>(qrow + nx + 16);
-          d = mfma_32x32x64_fp8(A, B, d);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tk = 32 * g + 16 * T + i;
-          x[16 * T + i] = ((vm >> tk) & 1ull) ? d[i] * mult : -INFINITY;
-        }
+      for (int kb = 0; kb < 9; ++kb) {
+        const v8i A = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const v8i B = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        const int nx = kb < 8 ? 64 * (kb + 1) : 64 * kb;
+        a0 = *reinterpret_cast<const v4i*>(arow + nx);
+        a1 = *reinterpret_cast<const v4i*>(arow + nx + 16);
+        b0 = *reinterpret_cast<const v4i*>(qrow + nx);
+        b1 = *reinterpret_cast<const v4i*>(qrow + nx + 16);
+        d = mfma_32x32x64_fp8(A, B, d);
       }
-      float mx = x[0];
 #pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int tk = 32 * g + 16 * hf + i;
+        x[i] = ((vm >> tk) & 1ull) ? d[i] * mult : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (g == 0) xmax[ht][hf][n] = mx;
+    }
+    __syncthreads();
+    if (vm != 0ull) {
+      mx = fmaxf(mx, xmax[ht][hf ^ 1][n]);  // the tile max of head n, same in both waves
       if (!started) {
         m_run = mx;
         started = true;
@@ -224,12 +207,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
           for (int i = 0; i < 16; ++i) acc[dt][i] *= fr[i];
         wave_lds_sync();
       }
-      // ---- probabilities -> two E4M3 A operands (byte j = token 32*g + j): hi = E4M3(p),
-      // lo = E4M3(p - hi), so hi + lo carries p to ~2^-8 relative in the value product
-      v8i pa, pl;
+      // ---- probabilities of this half -> two E4M3 terms (hi = E4M3(p), lo = E4M3(p - hi)),
+      // stored as bytes 32*g + 16*hf + i of head n's row
+      v4i phi, plo;
       float zsum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         float p4[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -240,14 +223,26 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         const uint32_t hi = cvt4_e4m3(p4[0], p4[1], p4[2], p4[3]);
         const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
         const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-        pa[j] = (int)hi;
-        pl[j] = (int)cvt4_e4m3(p4[0] - d01[0], p4[1] - d01[1], p4[2] - d23[0], p4[3] - d23[1]);
+        phi[j] = (int)hi;
+        plo[j] = (int)cvt4_e4m3(p4[0] - d01[0], p4[1] - d01[1], p4[2] - d23[0], p4[3] - d23[1]);
       }
       z_run += zsum;
+      *reinterpret_cast<v4i*>(&pbuf[ht][0][n][32 * g + 16 * hf]) = phi;
+      *reinterpret_cast<v4i*>(&pbuf[ht][1][n][32 * g + 16 * hf]) = plo;
+    }
+    __syncthreads();
+    if (vm != 0ull) {
+      // ---- A operands: head n, tokens 32*g .. +31 of the tile (both halves)
+      const v4i h0 = *reinterpret_cast<const v4i*>(&pbuf[ht][0][n][32 * g]);
+      const v4i h1 = *reinterpret_cast<const v4i*>(&pbuf[ht][0][n][32 * g + 16]);
+      const v4i l0 = *reinterpret_cast<const v4i*>(&pbuf[ht][1][n][32 * g]);
+      const v4i l1 = *reinterpret_cast<const v4i*>(&pbuf[ht][1][n][32 * g + 16]);
+      const v8i pa = v8i{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      const v8i pl = v8i{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
       // ---- O += P8 * V8: B operand via LDS transpose reads.  In each 16-lane group,
       // lanes 2r, 2r+1 address the two 8-byte halves of token row r (8 rows), and lane i
       // then receives dim (group base + i) of those 8 tokens.
-      const uint8_t* vb = tile + (32 * (grp >> 1) + (li >> 1)) * kRowStride + 256 * dh +
+      const uint8_t* vb = tile + (32 * (grp >> 1) + (li >> 1)) * kRowStride + 256 * hf +
                           16 * (grp & 1) + 8 * (li & 1);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -267,11 +262,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   }
 
   // ------------------------------------------------------------------ finalize
-  const float z = z_run + __shfl_xor(z_run, 32, 64);
+  // each wave summed the probabilities of its own token halves: add the partner's
+  const float zl = z_run + __shfl_xor(z_run, 32, 64);
+  if (g == 0) xfer[wave][n] = zl;
+  __syncthreads();
+  const float z = zl + xfer[wave ^ 1][n];
   const bool empty = !(z > 0.f);
   const float lse = empty ? -INFINITY : (m_run + log2f(z)) * kLn2;
   // values are latent_scale * L8; probabilities entered the product scaled by 2^4
   const float invz = empty ? 0.f : lat_scale / (z * kPScale);
+  __syncthreads();
   if (g == 0) xfer[wave][n] = invz;
   wave_lds_sync();
   float fr[16];
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     for (int c = 0; c < 4; ++c) fr[4 * a + c] = v[c];
   }
   const int head0 = 32 * ht;
-  const int dim0 = 256 * dh + n;
+  const int dim0 = 256 * hf + n;
   if (num_splits == 1) {
     uint16_t* ob = out_bf16 + (int64_t)row * kMlaHeads * kVDim;
 #pragma unroll
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         u += 0x7FFFu + ((u >> 16) & 1u);
         ob[(int64_t)h * kVDim + dim0 + 32 * dt] = (uint16_t)(u >> 16);
       }
-    if (g == 0 && dh == 0) lse_out[(int64_t)row * kMlaHeads + head0 + n] = lse;
+    if (g == 0 && hf == 0) lse_out[(int64_t)row * kMlaHeads + head0 + n] = lse;
   } else {
     float* op = o_part + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
 #pragma unroll
@@ -304,20 +304,30 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         const int h = head0 + 8 * (i / 4) + 4 * g + (i % 4);
         op[(int64_t)h * kVDim + dim0 + 32 * dt] = acc[dt][i] * fr[i];
       }
-    if (g == 0 && dh == 0) lse_part[((int64_t)s * n_q + row) * kMlaHeads + head0 + n] = lse;
+    if (g == 0 && hf == 0) lse_part[((int64_t)s * n_q + row) * kMlaHeads + head0 + n] = lse;
   }
 }
 
 }  // namespace
 
+size_t sparse_mla_workspace_bytes(int n_q) {
+  const size_t codes = ((size_t)n_q * kMlaHeads * kLatDim + 255) / 256 * 256;
+  return codes + (size_t)n_q * kMlaHeads * sizeof(float);
+}
+
 hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* latent_pages,
                              int64_t latent_page_stride, float latent_scale,
                              const int32_t* topk_slot, int k, float softmax_scale, int num_splits,
                              float* o_part, float* lse_part, uint16_t* out_bf16, float* lse,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)num_splits, (unsigned)n_q), dim3(kThreads), 0, st,
-                     q, latent_pages, latent_page_stride, latent_scale, topk_slot, k, softmax_scale,
-                     num_splits, n_q, o_part, lse_part, out_bf16, lse);
+                             void* workspace, hipStream_t st) {
+  // query prep once per row: E4M3 codes + power-of-two scales shared by all splits
+  uint8_t* q8 = static_cast<uint8_t*>(workspace);
+  float* qs = reinterpret_cast<float*>(q8 + ((size_t)n_q * kMlaHeads * kLatDim + 255) / 256 * 256);
+  hipError_t e = launch_quantize_q(n_q, kMlaHeads, kLatDim, q, q8, qs, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)num_splits, (unsigned)n_q), dim3(kThreads), 0,
+                     st, q8, qs, latent_pages, latent_page_stride, latent_scale, topk_slot, k,
+                     softmax_scale, num_splits, n_q, o_part, lse_part, out_bf16, lse);
   return hipGetLastError();
 }
 

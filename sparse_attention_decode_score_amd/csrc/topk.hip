@@ -26,6 +26,7 @@ constexpr int kNT = 256;       // threads per workgroup
 constexpr int kE = 8;          // consecutive elements per thread per compaction round
 constexpr int kChunk = 8192;   // tokens per first-pass chunk
 constexpr uint32_t kSentinel = 0u;  // below every real key (NaN maps to 1)
+constexpr int kFinalLds = 12288;    // candidates the final pass keeps in LDS
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   const uint32_t k = order_key(f);
@@ -179,15 +180,20 @@ __device__ int ordered_compact(const Get& get, int n, uint32_t K, int r, int lim
   return out_base;
 }
 
+// Request and absolute position of query row `row`: one wave-wide ballot over cu_q per 64
+// requests (rows are grouped by request and are its last tokens).
 __device__ __forceinline__ void row_of(const int32_t* cu_q, const int32_t* seq_lens, int num_seqs,
                                        int row, int& b, int& pos) {
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {  // last b with cu_q[b] <= row
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= row) lo = mid; else hi = mid - 1;
+  const int lane = lane_id();
+  int count = 0;
+  for (int base = 0; base < num_seqs; base += 64) {  // uniform loop
+    const int i = base + lane;
+    const bool le = i < num_seqs && cu_q[i] <= row;
+    count += __popcll(__ballot(le));
   }
-  b = lo;
-  pos = seq_lens[b] - (cu_q[b + 1] - cu_q[b]) + (row - cu_q[b]);
+  b = count - 1;
+  const int c0 = cu_q[b], c1 = cu_q[b + 1];
+  pos = seq_lens[b] - (c1 - c0) + (row - c0);
 }
 
 // Candidates kept per chunk for a row with n_vis visible tokens: 1.5x the winners a full
@@ -269,6 +275,8 @@ __global__ __launch_bounds__(kNT) void topk_final_kernel(
   __shared__ uint32_t hist[2048];
   __shared__ int sh[8];
   __shared__ int redo;
+  __shared__ __attribute__((aligned(16))) uint32_t lkey[kFinalLds];
+  __shared__ __attribute__((aligned(16))) int32_t lidx[kFinalLds];
   const int row = blockIdx.x, tid = threadIdx.x;
   int b, pos;
   row_of(cu_q, seq_lens, num_seqs, row, b, pos);
@@ -288,14 +296,29 @@ __global__ __launch_bounds__(kNT) void topk_final_kernel(
     const int n_cand = n_chunks * m;  // >= 1.5 k by construction of m
     const uint32_t* ck = cand_key + (int64_t)row * row_cap;
     const int32_t* ci = cand_idx + (int64_t)row * row_cap;
-    auto getc = [&](int i) { return ck[i]; };
     uint32_t K;
     int r;
-    radix_threshold(getc, n_cand, k, hist, sh, K, r);
     int last_eq;
-    auto emitc = [&](int p, int i, uint32_t) { out[p] = ci[i]; };
-    ordered_compact(getc, n_cand, K, r, k, emitc, sh, &last_eq);
-    const int I = last_eq >= 0 ? ci[last_eq] : 0x7FFFFFFF;
+    int I;
+    if (n_cand <= kFinalLds) {
+      // candidates fit in LDS: one coalesced read, then every pass runs on-chip
+      for (int i = tid; i < n_cand; i += kNT) {
+        lkey[i] = ck[i];
+        lidx[i] = ci[i];
+      }
+      __syncthreads();
+      auto getc = [&](int i) { return lkey[i]; };
+      radix_threshold(getc, n_cand, k, hist, sh, K, r);
+      auto emitc = [&](int p, int i, uint32_t) { out[p] = lidx[i]; };
+      ordered_compact(getc, n_cand, K, r, k, emitc, sh, &last_eq);
+      I = last_eq >= 0 ? lidx[last_eq] : 0x7FFFFFFF;
+    } else {
+      auto getc = [&](int i) { return ck[i]; };
+      radix_threshold(getc, n_cand, k, hist, sh, K, r);
+      auto emitc = [&](int p, int i, uint32_t) { out[p] = ci[i]; };
+      ordered_compact(getc, n_cand, K, r, k, emitc, sh, &last_eq);
+      I = last_eq >= 0 ? ci[last_eq] : 0x7FFFFFFF;
+    }
     if (tid == 0) redo = 0;
     __syncthreads();
     const ChunkInfo* inf = info + (int64_t)row * num_chunks;

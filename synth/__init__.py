@@ -96,7 +96,7 @@ def workload(name: str) -> Workload:
     if name == "spec":
         return Workload("spec", _spec_lens(1), (5,) * 32, 2048, 4, seed=1)
     if name == "long":
-        return Workload("long", (131072,) * 32, (1,) * 32, 2048, 16, seed=2)
+        return Workload("long", (131072,) * 32, (1,) * 32, 2048, 8, seed=2)
     if name == "million":
         return Workload("million", (1048576,), (5,), 2048, 32, seed=3)
     if name == "prefill":

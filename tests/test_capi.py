@@ -29,7 +29,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"dsa_index_score", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_lse_combine", "dsa_quantize_q", "dsa_last_error", "dsa_version"} <= set(names)
+            "dsa_sparse_mla_workspace_size", "dsa_lse_combine", "dsa_quantize_q", "dsa_last_error",
+            "dsa_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -80,10 +81,13 @@ def test_topk_rejects_bad_host_args(L):
 
 def test_sparse_mla_and_combine_reject_bad_host_args(L):
     f = L.dsa_sparse_mla_decode
+    need = L.dsa_sparse_mla_workspace_size(4)
+    assert need >= 4 * 96 * 576
     base = [4, FAKE, FAKE, 36864, ctypes.c_float(0.01), FAKE, 2048, ctypes.c_float(0.04), 4, FAKE,
-            FAKE, None, None, None]
+            FAKE, None, None, ctypes.c_void_p(0x10000), need, None]
     for patch, status in [({0: 0}, 1), ({6: 0}, 2), ({8: 0}, 2), ({8: 65}, 2), ({3: 36863}, 1),
-                          ({4: ctypes.c_float(0.0)}, 1), ({9: None}, 1), ({2: FAKE_ODD}, 1)]:
+                          ({4: ctypes.c_float(0.0)}, 1), ({9: None}, 1), ({2: FAKE_ODD}, 1),
+                          ({14: need - 1}, 3), ({13: None}, 3), ({13: ctypes.c_void_p(0x10010)}, 1)]:
         args = list(base)
         for i, v in patch.items():
             args[i] = v

@@ -62,13 +62,15 @@ def run_mla(batch, slots, num_splits):
         out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
         lse = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
         dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale, slots,
-                                  batch.softmax_scale, 1, out=out, lse=lse)
+                                  batch.softmax_scale, 1, out=out, lse=lse,
+                                  workspace=dsa.workspace(dsa.dsa_sparse_mla_workspace_size(n_q)))
         torch.cuda.synchronize()
         return out, lse, None, None
     op = torch.full((num_splits, n_q, 96, 512), float("nan"), device=DEV)
     lp = torch.full((num_splits, n_q, 96), float("nan"), device=DEV)
     dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale, slots,
-                              batch.softmax_scale, num_splits, o_part=op, lse_part=lp)
+                              batch.softmax_scale, num_splits, o_part=op, lse_part=lp,
+                              workspace=dsa.workspace(dsa.dsa_sparse_mla_workspace_size(n_q)))
     out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
     dsa.dsa_lse_combine(op, lp, out, lse)
