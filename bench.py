@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--splits", type=int, default=0, help="sparse-attention splits (0 = workload default)")
     ap.add_argument("--no-flush", action="store_true", help="keep the 256 MB last-level cache warm")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run stage 2 as both top-k passes instead of taking the indexer's "
+                         "per-chunk candidates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -190,7 +193,7 @@ def main():
     S = args.splits or wl.num_splits
     torch.cuda.set_device(0)
     batch = synth.make_batch(wl, "cuda")
-    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S)
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
     flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -205,13 +208,11 @@ def main():
     def one_step(evs=None):
         if evs:
             evs[0].record(stream)
-        dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
-                            batch.block_table, step.scores, max_seq_len=wl.max_seq_len,
-                            max_q_per_seq=max(wl.q_per_seq))
+        step.index(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                   batch.block_table, max(wl.q_per_seq))
         if evs:
             evs[1].record(stream)
-        dsa.dsa_topk(batch.cu_q, batch.seq_lens, step.scores, wl.topk, batch.block_table,
-                     step.topk_idx, step.topk_slot, step.workspace, max_seq_len=wl.max_seq_len)
+        step.select(batch.cu_q, batch.seq_lens, batch.block_table)
         if evs:
             evs[2].record(stream)
         if S == 1:
@@ -294,6 +295,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.num_seqs, "query_rows": wl.n_q,
                    "context": wl.max_seq_len if len(set(wl.seq_lens)) == 1 else "ragged",
                    "topk": wl.topk, "num_splits": S, "page_size": PAGE,
+                   "indexer_emits_topk_candidates": not args.unfused,
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),
         "us_per_layer_median": round(med, 2),

@@ -8,6 +8,9 @@
  *
  *   dsa_index_score       stage 1  indexer scores           ("What changed in Kimi K3.1 Pro")
  *   dsa_topk              stage 2  exact top-k select       ("Exact top-k merge with ~10x less traffic")
+ *                         Stage 1 can also emit each 256-token group's top-k candidates while
+ *                         its scores are on chip; stage 2 then only runs its final pass (the
+ *                         scorer + exact top-k pair of "Fused low-latency decode for DSA layers").
  *   dsa_sparse_mla_decode stage 3  MLA over selected tokens ("Sparse attention cuts long-context
  *                                                             decode bandwidth")
  *   dsa_lse_combine       stage 4  LSE merge of splits      ("Decode context parallelism with the
@@ -95,33 +98,45 @@ typedef enum {
  *   scores   fp32 [n_q][score_stride], score_stride >= max_seq_len.  Row i's columns
  *            0 .. seq_lens[b]-1 are written; columns past its position hold scores of
  *            keys it may not see (ignored by dsa_topk); other columns are not touched.
+ *   cand_k, cand_workspace, cand_workspace_bytes: if cand_workspace is not NULL the
+ *            scoring waves also write, for a top-k of cand_k (1..4096), every 256-token
+ *            group's best candidates (3x the winners a full group holds on average, in
+ *            token order) and the group's boundary element into it; it must hold
+ *            dsa_topk_workspace_size(n_q, max_seq_len, cand_k) bytes, 256-byte aligned.
+ *            Pass it to dsa_topk with from_candidates = 1.  NULL: scores only.
  */
 dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
                            int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
                            const void* q_bf16, const float* head_w, const void* key_pages,
                            int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
-                           float* scores, int64_t score_stride, void* stream);
+                           float* scores, int64_t score_stride, int32_t cand_k,
+                           void* cand_workspace, size_t cand_workspace_bytes, void* stream);
 
 /*
  * Stage 2 — exact top-k over each row's visible scores (tokens 0..position).
  * Order: score descending, then token index ascending (-0.0 == +0.0; NaN ranks lowest).
- * Two passes: every 8,192-token chunk keeps its best m candidates, then one workgroup
- * per row selects from the candidates; if a chunk could have held more of the winners
- * than it sent (the detection rule of the K3.1 page's exact one-round merge), that row
- * is re-selected from all of its scores, so the result is always exact.
+ * Two passes: every 256-token group keeps its best m candidates (3x the winners a full
+ * group holds on average), then one workgroup per row selects from the candidates; the
+ * groups that could have held more of the winners than they sent (the detection rule of
+ * the K3.1 page's exact one-round merge) are re-read in full from the scores and the row is
+ * selected again, so the result is always exact.  from_candidates = 0: this call runs both
+ * passes.  from_candidates = 1: the workspace already holds the candidates dsa_index_score
+ * wrote for the same batch, scores and k, and only the final pass runs.
  *
  *   k in 1..4096.  topk_idx int32 [n_q][k]: the min(k, position+1) selected logical
  *   token indices in increasing index order, then -1.  topk_slot int32 [n_q][k]: the
  *   physical slots of the same tokens (page*64 + offset via block_table), -1 padded;
  *   pass block_table = NULL and topk_slot = NULL to skip slots.
- *   workspace: device memory of at least dsa_topk_workspace_size() bytes, 256-byte
- *   aligned; its contents need no initialisation and are scratch after the call.
+ *   workspace: device memory of at least dsa_topk_workspace_size(n_q, max_seq_len, k)
+ *   bytes, 256-byte aligned; with from_candidates = 0 its contents need no
+ *   initialisation.  It is scratch after the call.
  */
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k);
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
                     const int32_t* seq_lens, const float* scores, int64_t score_stride, int32_t k,
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
-                    int32_t* topk_slot, void* workspace, size_t workspace_bytes, void* stream);
+                    int32_t* topk_slot, void* workspace, size_t workspace_bytes,
+                    int32_t from_candidates, void* stream);
 
 /*
  * Stage 3 — exact MLA (NoPE) over the selected slots, one query row at a time.

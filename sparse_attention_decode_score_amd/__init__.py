@@ -47,10 +47,11 @@ def lib() -> ctypes.CDLL:
                                "`python sparse_attention_decode_score_amd/build.py`")
         L = ctypes.CDLL(LIB_PATH)
         L.dsa_index_score.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32,
-                                      _P, _I64, _P]
+                                      _P, _I64, _I32, _P, _SZ, _P]
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
-        L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ, _P]
+        L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
+                               _I32, _P]
         L.dsa_sparse_mla_workspace_size.argtypes = [_I32]
         L.dsa_sparse_mla_workspace_size.restype = _SZ
         L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _I64, _F32, _P, _I32, _F32, _I32, _P, _P,
@@ -110,8 +111,11 @@ def dsa_quantize_q(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, s
 def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Tensor,
                     head_w: torch.Tensor, key_pages: torch.Tensor, block_table: torch.Tensor,
                     scores: torch.Tensor, *, max_seq_len: int, max_q_per_seq: int,
-                    key_page_stride: Optional[int] = None, stream=None) -> None:
-    """Indexer scores into scores [n_q, score_stride] (fp32)."""
+                    key_page_stride: Optional[int] = None, cand_k: int = 0,
+                    cand_workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Indexer scores into scores [n_q, score_stride] (fp32); with cand_workspace, also the
+    per-chunk top-k candidates for a top-k of cand_k (consumed by dsa_topk with
+    from_candidates=True)."""
     num_seqs = seq_lens.shape[0]
     n_q = q_idx.shape[0]
     _expect(cu_q, "cu_q", torch.int32, (num_seqs + 1,))
@@ -123,10 +127,15 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
     if scores.dim() != 2 or scores.shape[0] != n_q:
         raise ValueError("scores must be [n_q, score_stride]")
     stride = key_page_stride if key_page_stride is not None else key_pages.stride(0) * key_pages.element_size()
+    if cand_workspace is not None:
+        _expect(cand_workspace, "cand_workspace", torch.uint8)
     _check(lib().dsa_index_score(num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q),
                                  _ptr(seq_lens), _ptr(q_idx), _ptr(head_w), _ptr(key_pages),
                                  int(stride), _ptr(block_table), block_table.shape[1],
-                                 _ptr(scores), scores.shape[1], _stream(stream)))
+                                 _ptr(scores), scores.shape[1], int(cand_k),
+                                 _ptr(cand_workspace),
+                                 cand_workspace.numel() if cand_workspace is not None else 0,
+                                 _stream(stream)))
 
 
 def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
@@ -136,7 +145,7 @@ def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
 def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,
              block_table: Optional[torch.Tensor], topk_idx: torch.Tensor,
              topk_slot: Optional[torch.Tensor], workspace: torch.Tensor, *, max_seq_len: int,
-             stream=None) -> None:
+             from_candidates: bool = False, stream=None) -> None:
     """Exact top-k token indices (and physical slots) of every row's visible scores."""
     num_seqs = seq_lens.shape[0]
     n_q = scores.shape[0]
@@ -149,7 +158,7 @@ def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k
                           scores.shape[1], int(k), _ptr(block_table),
                           block_table.shape[1] if block_table is not None else 0,
                           _ptr(topk_idx), _ptr(topk_slot), _ptr(workspace), workspace.numel(),
-                          _stream(stream)))
+                          int(bool(from_candidates)), _stream(stream)))
 
 
 def dsa_sparse_mla_workspace_size(n_q: int) -> int:
@@ -213,8 +222,10 @@ class DecodeStep:
     run() then issues the four library calls on the current stream.
     """
 
-    def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda"):
+    def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
+                 fused: bool = True):
         self.n_q, self.max_seq_len, self.k, self.num_splits = n_q, max_seq_len, k, num_splits
+        self.fused = fused
         dev = torch.device(device)
         self.scores = torch.empty((n_q, max_seq_len), dtype=torch.float32, device=dev)
         self.topk_idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
@@ -229,12 +240,22 @@ class DecodeStep:
         else:
             self.o_part = self.lse_part = None
 
-    def run(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, q_mla, latent_pages,
-            latent_scale, softmax_scale, max_q_per_seq, stream=None):
+    def index(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq,
+              stream=None):
+        """Stage 1 (with the fused first top-k pass when self.fused)."""
         dsa_index_score(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, self.scores,
-                        max_seq_len=self.max_seq_len, max_q_per_seq=max_q_per_seq, stream=stream)
+                        max_seq_len=self.max_seq_len, max_q_per_seq=max_q_per_seq,
+                        cand_k=self.k, cand_workspace=self.workspace if self.fused else None,
+                        stream=stream)
+
+    def select(self, cu_q, seq_lens, block_table, stream=None):
+        """Stage 2."""
         dsa_topk(cu_q, seq_lens, self.scores, self.k, block_table, self.topk_idx, self.topk_slot,
-                 self.workspace, max_seq_len=self.max_seq_len, stream=stream)
+                 self.workspace, max_seq_len=self.max_seq_len, from_candidates=self.fused,
+                 stream=stream)
+
+    def attend(self, q_mla, latent_pages, latent_scale, softmax_scale, stream=None):
+        """Stages 3 and 4."""
         if self.num_splits == 1:
             dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
                                   1, out=self.out, lse=self.lse, workspace=self.mla_workspace,
@@ -245,3 +266,9 @@ class DecodeStep:
                                   workspace=self.mla_workspace, stream=stream)
             dsa_lse_combine(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
         return self.out, self.lse
+
+    def run(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, q_mla, latent_pages,
+            latent_scale, softmax_scale, max_q_per_seq, stream=None):
+        self.index(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq, stream)
+        self.select(cu_q, seq_lens, block_table, stream)
+        return self.attend(q_mla, latent_pages, latent_scale, softmax_scale, stream)

@@ -75,7 +75,8 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
                            int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
                            const void* q_bf16, const float* head_w, const void* key_pages,
                            int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
-                           float* scores, int64_t score_stride, void* stream) {
+                           float* scores, int64_t score_stride, int32_t cand_k,
+                           void* cand_workspace, size_t cand_workspace_bytes, void* stream) {
   dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(max_q_per_seq >= 1 && max_q_per_seq <= n_q,
@@ -92,11 +93,20 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
               "bt_stride (%d) must cover max_seq_len (%d) in pages of 64", bt_stride, max_seq_len);
   DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
               (long long)score_stride, max_seq_len);
+  if (cand_workspace) {
+    if (cand_k < 1 || cand_k > DSA_MAX_TOPK)
+      return fail(DSA_ERR_UNSUPPORTED, "cand_k must be in 1..4096 (got %d)", cand_k);
+    const size_t need = dsa::topk_workspace_bytes(n_q, max_seq_len, cand_k);
+    if (cand_workspace_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "candidate workspace of %zu bytes is smaller than the %zu needed",
+                  cand_workspace_bytes, need);
+    DSA_REQUIRE(aligned(cand_workspace, 256), "cand_workspace must be 256-byte aligned");
+  }
   return launched(dsa::launch_index_score(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens,
                                           static_cast<const uint16_t*>(q_bf16), head_w,
                                           static_cast<const uint8_t*>(key_pages), key_page_stride,
-                                          block_table, bt_stride, scores, score_stride,
-                                          static_cast<hipStream_t>(stream)),
+                                          block_table, bt_stride, scores, score_stride, cand_k,
+                                          cand_workspace, static_cast<hipStream_t>(stream)),
                   "dsa_index_score");
 }
 
@@ -108,7 +118,8 @@ size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k) {
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
                     const int32_t* seq_lens, const float* scores, int64_t score_stride, int32_t k,
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
-                    int32_t* topk_slot, void* workspace, size_t workspace_bytes, void* stream) {
+                    int32_t* topk_slot, void* workspace, size_t workspace_bytes,
+                    int32_t from_candidates, void* stream) {
   dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
   if (st != DSA_OK) return st;
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
@@ -125,9 +136,15 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 workspace ? workspace_bytes : (size_t)0, need);
   DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (from_candidates) {
+    const dsa::TopkBuffers t = dsa::topk_buffers(workspace, n_q, max_seq_len, k);
+    return launched(dsa::launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k,
+                                           t, block_table, bt_stride, topk_idx, topk_slot, hs),
+                    "dsa_topk");
+  }
   return launched(dsa::launch_topk(num_seqs, n_q, max_seq_len, cu_q, seq_lens, scores, score_stride,
-                                   k, block_table, bt_stride, topk_idx, topk_slot, workspace,
-                                   static_cast<hipStream_t>(stream)),
+                                   k, block_table, bt_stride, topk_idx, topk_slot, workspace, hs),
                   "dsa_topk");
 }
 

@@ -8,22 +8,37 @@
 namespace dsa {
 
 struct TopkPlan {
-  int chunk;        // tokens per chunk of the first pass
-  int num_chunks;   // chunks covering max_seq_len
+  int num_groups;   // 256-token first-pass groups covering max_seq_len
   int row_cap;      // candidate slots reserved per row
+};
+
+struct ChunkInfo;
+struct TopkBuffers {
+  TopkPlan plan;
+  uint32_t* cand_key;
+  int32_t* cand_idx;
+  ChunkInfo* info;
 };
 
 TopkPlan topk_plan(int max_seq_len, int k);
 size_t topk_workspace_bytes(int n_q, int max_seq_len, int k);
+TopkBuffers topk_buffers(void* workspace, int n_q, int max_seq_len, int k);
+// Final pass only: the workspace already holds every group's candidates.
+hipError_t launch_topk_final(int num_seqs, int n_q, const int32_t* cu_q, const int32_t* seq_lens,
+                             const float* scores, int64_t score_stride, int k,
+                             const TopkBuffers& t, const int32_t* block_table, int bt_stride,
+                             int32_t* topk_idx, int32_t* topk_slot, hipStream_t st);
 
 hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, uint8_t* codes,
                              float* scales, hipStream_t st);
 
+// topk_ws == nullptr: scores only.  Otherwise the kernel also writes every 256-token group's
+// top-k candidates for a top-k of k into topk_ws (see topk_buffers).
 hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_per_seq,
                               const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
                               const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
                               const int32_t* block_table, int bt_stride, float* scores,
-                              int64_t score_stride, hipStream_t st);
+                              int64_t score_stride, int k, void* topk_ws, hipStream_t st);
 
 hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu_q,
                        const int32_t* seq_lens, const float* scores, int64_t score_stride, int k,

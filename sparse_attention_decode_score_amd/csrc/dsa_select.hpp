@@ -1,0 +1,386 @@
+// Exact selection primitives of the top-k stage: order-preserving keys, the per-group
+// candidate rule, one wave's top-m of a 256-token group (ballots only, keys in registers)
+// and one 1,024-thread workgroup's top-k of up to 16,384 keys (bitwise threshold search).
+//
+// Total order everywhere: larger key first, equal keys by lower element index (token order).
+#pragma once
+
+#include "dsa_device.hpp"
+
+namespace dsa {
+
+constexpr uint32_t kSentinel = 0u;  // below every real key (NaN maps to 1)
+constexpr int kGroupTok = 256;      // tokens per first-pass group (one wave, 4 pages)
+#ifndef DSA_FINAL_THREADS
+#define DSA_FINAL_THREADS 512
+#endif
+constexpr int kFinalThreads = DSA_FINAL_THREADS;  // threads of the final pass
+constexpr int kFinalWaves = kFinalThreads / 64;
+constexpr int kFinalPerThread = 32;  // at most, in registers
+constexpr int kBucketMax = 512;      // keys of the last search bucket, finished by one wave
+constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds on chip
+
+// Per-group record of the first selection pass.
+struct ChunkInfo {
+  int count;      // real candidates written (<= m); the rest of the m slots are sentinels
+  int saturated;  // the group had more than m visible tokens
+  uint32_t key;   // its m-th element (when saturated): key and token index
+  int idx;
+};
+
+// Score -> key: larger score = larger key, -0.0 == +0.0, NaN just above the sentinel.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t k = order_key(f);
+  return k == 0u ? 1u : k;
+}
+
+// Candidates a first-pass group keeps: four times the winners a full group holds on
+// average (k * 256 / n_vis; the on-chip form of the 1.5 x 2048 / W per-shard rule of the
+// exact top-k merge, with more slack because a group is small), rounded up to 4, at least
+// 4 and at most the group.  At 131,072 visible tokens and k = 2,048: 16 of 256 (a group
+// holds 4 winners on average; more than 16 happens about once in 10^6 groups for
+// independent scores, and is then caught and resent).
+__host__ __device__ __forceinline__ int group_cand_count(int n_vis, int k) {
+  const int64_t num = 4 * (int64_t)k * kGroupTok;
+  int64_t m = (num + n_vis - 1) / n_vis;
+  m = (m + 3) / 4 * 4;
+  if (m < 4) m = 4;
+  if (m > kGroupTok) m = kGroupTok;
+  return (int)m;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// One wave's top-m of a group: lane l holds element 64*j + l in keys[j] (element i is token
+// t0 + i; elements i >= n are not visible).  Writes the min(n, m) chosen keys and token
+// indices in token order to ck / ci, sentinels (key 0, index INT_MAX) after them, and the
+// group's record.  Wave-uniform control flow only; no LDS.
+__device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, int m, int t0,
+                                             uint32_t* ck, int32_t* ci, ChunkInfo* inf) {
+  const int lane = lane_id();
+  uint32_t kv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kv[j] = (64 * j + lane < n) ? keys[j] : kSentinel;
+  if (n <= m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 64 * j + lane;
+      if (i < m) {
+        ck[i] = kv[j];
+        ci[i] = i < n ? t0 + i : 0x7FFFFFFF;
+      }
+    }
+    if (lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
+    return;
+  }
+  // K = the m-th largest key: the largest T with #{keys >= T} >= m, one bit at a time
+  // (every T tried is >= 1, so the sentinel of an invisible element never counts)
+  uint32_t K = 0;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t T = K | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c += __popcll(__ballot(kv[j] >= T));
+    if (c >= m) K = T;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gt += __popcll(__ballot(kv[j] > K));
+  const int r = m - gt;  // equal keys taken, the first r in token order
+  int base = 0, eq_seen = 0, last = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool eq = kv[j] == K;
+    const uint64_t eqm = __ballot(eq);
+    const int rank = eq_seen + lanes_below(eqm);
+    const bool take = kv[j] > K || (eq && rank < r);
+    if (eq && rank == r - 1) last = 64 * j + lane;
+    const uint64_t tm = __ballot(take);
+    if (take) {
+      const int pos = base + lanes_below(tm);
+      ck[pos] = kv[j];
+      ci[pos] = t0 + 64 * j + lane;
+    }
+    base += __popcll(tm);
+    eq_seen += __popcll(eqm);
+  }
+  const uint64_t who = __ballot(last >= 0);
+  const int last_i = __shfl(last, (int)__builtin_ctzll(who), 64);
+  if (lane == 0) *inf = ChunkInfo{m, 1, K, t0 + last_i};
+}
+
+// ----------------------------------------------------------------------------------------
+// Workgroup (kFinalThreads threads) primitives.
+
+// Sum of v over the wave, returned wave-uniform: DPP butterflies inside each row of 16 lanes
+// (quad swaps, half-row and row mirrors), then the four row sums.
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
+// Sum over the workgroup of a per-wave value (wave-uniform v).  red: 2 x 4 ints of LDS used
+// alternately (parity flips), so one barrier per call suffices.
+__device__ __forceinline__ int block_sum_waves(int v, int* red, int& parity) {
+  int* buf = red + kFinalWaves * parity;
+  parity ^= 1;
+  if (lane_id() == 0) buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kFinalWaves; i += 4) {
+    const v4i a = *reinterpret_cast<const v4i*>(buf + i);
+    t += (a[0] + a[1]) + (a[2] + a[3]);
+  }
+  return t;
+}
+
+// Sum over the workgroup of a per-thread value.  Same LDS rule.
+__device__ __forceinline__ int block_sum(int v, int* red, int& parity) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return block_sum_waves(v, red, parity);
+}
+
+// Exclusive prefix sum over thread order; *total gets the workgroup sum.  Same LDS rule.
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* red, int& parity) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  int* buf = red + kFinalWaves * parity;
+  parity ^= 1;
+  if (lane == 63) buf[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kFinalWaves; ++i) {
+    const int s = buf[i];
+    before += i < w ? s : 0;
+    tot += s;
+  }
+  *total = tot;
+  return before + x - v;
+}
+
+// Exact top-k (1 <= k <= number of real keys) of up to kFinalThreads * E keys held in
+// registers: thread t holds elements t*E .. t*E+E-1 (keys kv, values vv; elements past the
+// end hold the sentinel key).  Writes the values of the chosen elements, in element order,
+// to out[0..k) (LDS) and returns the k-th element's key (*K_out) and value (*I_out).
+//
+// K (the k-th largest key) is found one bit at a time as the largest T with #{keys >= T} >=
+// k, by the whole workgroup (one barrier per bit) while the keys still in play are many.
+// The counts already give the size of the remaining bucket [K, K_hi) (#{>= K} - #{>= K_hi});
+// once it holds at most kBucketMax keys they are compacted to LDS and one wave resolves the
+// remaining bits with no barriers (#{>= T} = #{>= K_hi} + #{bucket keys >= T}).  Every T
+// tried is >= 1, so sentinels never count.
+// red: >= 2 * kFinalWaves ints of LDS (16-byte aligned); note: 1 int; bucket: kBucketMax.
+template <int E>
+__device__ void block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int k, int* out,
+                                int* red, int* note, uint32_t* bucket, uint32_t* K_out,
+                                int* I_out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int parity = 0;
+  // this wave's #{keys > T} (strict) or #{keys >= T}, wave-uniform (vector counts in four
+  // accumulators, then one DPP reduction)
+  auto count = [&](uint32_t T, bool strict) {
+    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+    for (int j = 0; j < E; j += 4) {
+      c0 += (strict ? kv[j] > T : kv[j] >= T) ? 1 : 0;
+      c1 += (strict ? kv[j + 1] > T : kv[j + 1] >= T) ? 1 : 0;
+      c2 += (strict ? kv[j + 2] > T : kv[j + 2] >= T) ? 1 : 0;
+      c3 += (strict ? kv[j + 3] > T : kv[j + 3] >= T) ? 1 : 0;
+    }
+    return wave_sum((c0 + c1) + (c2 + c3));
+  };
+  uint32_t K = 0, K_hi = 0;
+  bool has_hi = false;
+  int c_K = kFinalThreads * E, c_hi = 0;  // #{>= K} (an upper bound until K moves), #{>= K_hi}
+  int bit = 31;
+#pragma unroll 1
+  for (; bit >= 0; --bit) {
+    const uint32_t T = K | (1u << bit);
+    const int c = block_sum_waves(count(T, false), red, parity);
+    if (c >= k) {
+      K = T;
+      c_K = c;
+    } else {
+      K_hi = T;
+      has_hi = true;
+      c_hi = c;
+    }
+    if (c_K - c_hi <= kBucketMax) {  // uniform
+      --bit;
+      break;
+    }
+  }
+  if (bit >= 0) {
+    const uint32_t lo = K > 1u ? K : 1u;
+    auto in_bucket = [&](uint32_t x) { return x >= lo && (!has_hi || x < K_hi); };
+    int na = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) na += in_bucket(kv[j]) ? 1 : 0;
+    int n_bucket;
+    int at = block_excl_scan(na, &n_bucket, red, parity);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (in_bucket(kv[j])) bucket[at++] = kv[j];
+    __syncthreads();
+    if (tid < 64) {
+      constexpr int BE = kBucketMax / 64;
+      uint32_t bk[BE];
+#pragma unroll
+      for (int j = 0; j < BE; ++j) {
+        const int e = lane * BE + j;
+        bk[j] = e < n_bucket ? bucket[e] : kSentinel;
+      }
+#pragma unroll 1
+      for (; bit >= 0; --bit) {
+        const uint32_t T = K | (1u << bit);
+        int c = c_hi;
+#pragma unroll
+        for (int j = 0; j < BE; ++j) c += __popcll(__ballot(bk[j] >= T));
+        if (c >= k) K = T;
+      }
+      if (tid == 0) *note = (int)K;
+    }
+    __syncthreads();
+    K = (uint32_t)*note;
+  }
+  const int r = k - block_sum_waves(count(K, true), red, parity);  // equal keys taken (>= 1)
+  if (tid == 0) *note = -1;
+  int n_eq = 0, n_gt = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    n_eq += kv[j] == K ? 1 : 0;
+    n_gt += kv[j] > K ? 1 : 0;
+  }
+  int eq_tot, take_tot;
+  const int eq_before = block_excl_scan(n_eq, &eq_tot, red, parity);
+  const int eq_take = min(max(r - eq_before, 0), n_eq);
+  int pos = block_excl_scan(n_gt + eq_take, &take_tot, red, parity);
+  int e_rank = eq_before;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    bool take = kv[j] > K;
+    if (kv[j] == K) {
+      take = e_rank < r;
+      if (e_rank == r - 1) *note = vv[j];
+      ++e_rank;
+    }
+    if (take) out[pos++] = vv[j];
+  }
+  __syncthreads();
+  *K_out = K;
+  *I_out = *note;
+  __syncthreads();
+}
+
+// Smallest per-thread count E in {8, 16, 32} with kFinalThreads * E >= n.
+__host__ __device__ __forceinline__ int final_per_thread(int n) {
+  return n <= 8 * kFinalThreads ? 8 : n <= 16 * kFinalThreads ? 16 : 32;
+}
+
+// The same selection over get(0 .. n-1) / val(0 .. n-1) (1 <= k <= real keys, any n): up to
+// kFinalTile elements go through registers, more are re-read tile by tile (slow; only the
+// exact fallbacks of the final pass come here).
+template <int E, class Get, class Val>
+__device__ void block_topk_e(const Get& get, const Val& val, int n, int k, int* out, int* red,
+                             int* note, uint32_t* bucket, uint32_t* K_out, int* I_out) {
+  const int tid = threadIdx.x;
+  uint32_t kv[E];
+  int vv[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int e = tid * E + j;
+    kv[j] = e < n ? get(e) : kSentinel;
+    vv[j] = e < n ? val(e) : 0;
+  }
+  block_topk_regs<E>(kv, vv, k, out, red, note, bucket, K_out, I_out);
+}
+
+template <class Get, class Val>
+__device__ void block_topk(const Get& get, const Val& val, int n, int k, int* out, int* red,
+                           int* note, uint32_t* bucket, uint32_t* K_out, int* I_out) {
+  const int tid = threadIdx.x;
+  if (n <= kFinalTile) {
+    switch (final_per_thread(n)) {
+      case 8: block_topk_e<8>(get, val, n, k, out, red, note, bucket, K_out, I_out); return;
+      case 16: block_topk_e<16>(get, val, n, k, out, red, note, bucket, K_out, I_out); return;
+      default: block_topk_e<32>(get, val, n, k, out, red, note, bucket, K_out, I_out); return;
+    }
+  }
+  constexpr int E = 16;  // tile of the re-read path
+  constexpr int kTile = kFinalThreads * E;
+  int parity = 0;
+  const int n_tiles = (n + kTile - 1) / kTile;
+  auto count = [&](uint32_t T, bool strict) {
+    int c = 0;
+    for (int tile = 0; tile < n_tiles; ++tile)
+#pragma unroll 4
+      for (int j = 0; j < E; ++j) {
+        const int e = tile * kTile + tid * E + j;
+        const uint32_t x = e < n ? get(e) : kSentinel;
+        c += __popcll(__ballot(strict ? x > T : x >= T));
+      }
+    return c;
+  };
+  uint32_t K = 0;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t T = K | (1u << bit);
+    if (block_sum_waves(count(T, false), red, parity) >= k) K = T;
+  }
+  const int r = k - block_sum_waves(count(K, true), red, parity);
+  if (tid == 0) *note = -1;
+  int eq_base = 0, out_base = 0;
+#pragma unroll 1
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    uint32_t tk[E];
+    int n_eq = 0, n_gt = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = tile * kTile + tid * E + j;
+      tk[j] = e < n ? get(e) : kSentinel;
+      n_eq += tk[j] == K ? 1 : 0;
+      n_gt += tk[j] > K ? 1 : 0;
+    }
+    int eq_tot, take_tot;
+    const int eq_before = eq_base + block_excl_scan(n_eq, &eq_tot, red, parity);
+    const int eq_take = min(max(r - eq_before, 0), n_eq);
+    int pos = out_base + block_excl_scan(n_gt + eq_take, &take_tot, red, parity);
+    int e_rank = eq_before;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = tile * kTile + tid * E + j;
+      bool take = tk[j] > K;
+      if (tk[j] == K) {
+        take = e_rank < r;
+        if (e_rank == r - 1) *note = val(e);
+        ++e_rank;
+      }
+      if (take) out[pos++] = val(e);
+    }
+    eq_base += eq_tot;
+    out_base += take_tot;
+    if (out_base >= k) break;  // uniform
+  }
+  __syncthreads();
+  *K_out = K;
+  *I_out = *note;
+  __syncthreads();
+}
+
+}  // namespace dsa

@@ -6,10 +6,13 @@
 // "Native MXFP4 indexer" section).  The per-(row, head) power-of-two query scale sq is
 // folded into the head weight, so the FP8 product needs no rescaling inside the loop.
 //
-// Work split: one workgroup per (request, chunk of 16 pages, group of up to R query rows).
-// Every workgroup streams its keys exactly once from HBM and reuses them for all R rows of
-// the request (keys are shared by the verification rows of a speculative step, as the
-// page's MI355X indexer does), so the grid is balanced by keys, not by requests.
+// Work split: one workgroup per (request, segment of 16 G pages, group of up to R query
+// rows); each of its 4 waves owns G groups of 4 consecutive pages (256 tokens).  Every
+// workgroup streams its keys exactly once from HBM and reuses them for all R rows of the
+// request (keys are shared by the verification rows of a speculative step, as the page's
+// MI355X indexer does), so the grid is balanced by keys, not by requests.  A wave keeps a
+// ring of pages in flight across its groups, so the fused first top-k pass of a group (see
+// dsa_select.hpp) runs while the next group's keys stream in.
 //
 // One wave handles one 64-token page at a time as two 32-token halves:
 //   D[head][token] = Q8[32 heads x 128] * K8^T[128 x 32 tokens]  (2 x v_mfma 32x32x64 fp8)
@@ -17,14 +20,18 @@
 // keys in 16-byte column blocks so each of the 8 loads per lane is a fully coalesced 1 KB
 // wave access.  The head reduction is 16 in-register FMAs, then one permlane32 swap that
 // also places token l of the page in lane l for a coalesced 256-byte score store.
+#include <algorithm>
+
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
+#include "dsa_select.hpp"
 
 namespace dsa {
 
 namespace {
 
-constexpr int kPagesPerWg = 16;
+constexpr int kWaves = 4;
+constexpr int kGroupPages = kGroupTok / kPage;  // 4
 constexpr int kQRowStride = 144;  // LDS row stride of the FP8 query (128 + 16 pad: no bank conflicts)
 
 struct KeyPage {
@@ -50,28 +57,54 @@ __device__ __forceinline__ void load_key_page(KeyPage& kp, const uint8_t* base, 
   kp.s = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + kIdxPageKeyBytes + 4 * lane));
 }
 
-// Pages each wave keeps in flight: all of its pages for one or two rows per group, two at a
-// time for larger groups (register budget).
+// Pages each wave keeps in flight: four for one or two rows, two for larger row groups
+// (register budget).  Groups per wave at most: the staged scores of a workgroup are
+// 16 KB of LDS for up to four rows; eight rows store directly.
 template <int R>
 struct IdxCfg {
   static constexpr int kInFlight = R <= 2 ? 4 : 2;
+  static constexpr bool kStage = R <= 4;
+  static constexpr int kMaxGroups = R == 1 ? 4 : (R == 2 ? 2 : 1);
+  static constexpr int kSegTok = kWaves * kGroupTok * kMaxGroups;  // tokens per workgroup
+  static constexpr int kCandSlots = kWaves * kMaxGroups * kGroupTok;  // worst case (m = 256)
 };
-// pages of one wave per workgroup (all rounds)
-template <int R>
-__device__ constexpr int kRoundsPages() { return kPagesPerWg / 4; }
 
-template <int R>
+// Candidate output of the fused first top-k pass.
+struct CandOut {
+  uint32_t* key;
+  int32_t* idx;
+  ChunkInfo* info;
+  int64_t row_cap;
+  int num_groups;
+  int k;
+};
+
+// Why the structure below: the key loads of a wave's ring are issued unconditionally
+// (page indices past the segment are clamped to a visible page, and the last group issues
+// no loads past itself), and nothing is stored to global memory until every load has
+// returned (scores and candidates are staged in LDS for up to four rows).  gfx950 counts
+// loads and stores in one counter that may complete out of order, so a store in flight,
+// or loads under data-dependent branches, would force a full drain of the ring at every
+// wait instead of a wait for the oldest page only.
+template <int R, bool CAND>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ head_w,
     const uint8_t* __restrict__ key_pages, int64_t page_stride,
     const int32_t* __restrict__ block_table, int bt_stride, float* __restrict__ scores,
-    int64_t score_stride) {
-  constexpr int NF = IdxCfg<R>::kInFlight;
-  constexpr int kRounds = kPagesPerWg / (4 * NF);
+    int64_t score_stride, int groups_per_wave, CandOut cand) {
+  using Cfg = IdxCfg<R>;
+  constexpr int NF = Cfg::kInFlight;
+  constexpr bool STAGE = Cfg::kStage;
+  constexpr bool CSTAGE = CAND && STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t q8s[R][kIdxHeads][kQRowStride];
   __shared__ __attribute__((aligned(16))) float wps[R][kIdxHeads];
+  __shared__ __attribute__((aligned(16))) float sbuf[STAGE ? R : 1][STAGE ? Cfg::kSegTok : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t cbuf_key[CSTAGE ? R : 1][CSTAGE ? Cfg::kCandSlots : 1];
+  __shared__ __attribute__((aligned(16))) int32_t cbuf_idx[CSTAGE ? R : 1][CSTAGE ? Cfg::kCandSlots : 1];
+  __shared__ __attribute__((aligned(16))) ChunkInfo cbuf_info[CSTAGE ? R : 1][CSTAGE ? kWaves * Cfg::kMaxGroups : 1];
 
+  const int G = groups_per_wave;  // <= Cfg::kMaxGroups (host-checked)
   const int b = blockIdx.y;
   const int q0 = cu_q[b], q1 = cu_q[b + 1];
   const int r0 = q0 + (int)blockIdx.z * R;
@@ -79,123 +112,190 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int nr = min(R, q1 - r0);
   const int L = seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
-  const int p0 = (int)blockIdx.x * kPagesPerWg;
+  const int p0 = (int)blockIdx.x * kWaves * kGroupPages * G;
   // the last position any row of this group may see
   const int max_pos = L - (q1 - q0) + (r0 + nr - 1 - q0);
   if (p0 >= n_pages || p0 * kPage > max_pos) return;
-  const int p_end = min(min(n_pages, p0 + kPagesPerWg), max_pos / kPage + 1);
+  const int p_end = min(min(n_pages, p0 + kWaves * kGroupPages * G), max_pos / kPage + 1);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int32_t* bt = block_table + (int64_t)b * bt_stride;
+  // the wave's s-th page (s = 0 .. 4G-1): page s % 4 of its group s / 4
+  auto page_of = [&](int s) { return p0 + kGroupPages * (kWaves * (s >> 2) + wave) + (s & 3); };
+  // groups of this wave that hold a visible page
+  const int seg_groups = (p_end - p0 + kGroupPages - 1) / kGroupPages;
+  const int ng = max(0, (seg_groups - wave + kWaves - 1) / kWaves);
 
   // 1. query loads first (older than the key loads, so waiting for them does not wait
-  //    for the keys): 32 heads x 8 parts of 16 dims per row
+  //    for the keys): 32 heads x 8 parts of 16 dims per row; rows past the group repeat
+  //    its last row
   const int qh = tid >> 3, qpart = tid & 7;
   v4i qraw[R][2];
   float hw[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r < nr) {
-      const uint16_t* src = q + ((int64_t)(r0 + r) * kIdxHeads + qh) * kIdxDim + qpart * 16;
-      qraw[r][0] = *reinterpret_cast<const v4i*>(src);
-      qraw[r][1] = *reinterpret_cast<const v4i*>(src + 8);
-      hw[r] = head_w[(int64_t)(r0 + r) * kIdxHeads + qh];
-    }
+    const int row = r0 + min(r, nr - 1);
+    const uint16_t* src = q + ((int64_t)row * kIdxHeads + qh) * kIdxDim + qpart * 16;
+    qraw[r][0] = *reinterpret_cast<const v4i*>(src);
+    qraw[r][1] = *reinterpret_cast<const v4i*>(src + 8);
+    hw[r] = head_w[(int64_t)row * kIdxHeads + qh];
   }
-  // 2. this wave's first NF pages (page indices past the end are clamped to a valid page:
-  //    the loads stay unconditional and the extra results are never stored)
-  // one vector load fetches the wave's block-table entries (lane j: page j, clamped)
-  int bt_lane = bt[min(p0 + wave + 4 * (lane % kRoundsPages<R>()), p_end - 1)];
+  // 2. one vector load fetches the wave's block-table entries (lane s: its s-th page,
+  //    clamped to a visible page), then the first NF pages of the ring
+  const int bt_lane = bt[min(page_of(lane % (kGroupPages * G)), p_end - 1)];
+  auto page_ptr = [&](int s) {
+    return key_pages + (int64_t)__builtin_amdgcn_readlane(bt_lane, s) * page_stride;
+  };
+  // (unconditional, also for a wave without groups in a request's last segment: a branch
+  // here would leave the block-table load in doubt at every later wait)
   KeyPage kp[NF];
 #pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    const int phys = __builtin_amdgcn_readlane(bt_lane, j);
-    load_key_page(kp[j], key_pages + (int64_t)phys * page_stride, lane);
-  }
+  for (int j = 0; j < NF; ++j) load_key_page(kp[j], page_ptr(j), lane);
   // 3. fused query prep while the keys stream in: E4M3 codes, one power-of-two scale per
   //    (row, head), the scale folded into the head weight
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r < nr) {
-      float x[16];
+    float x[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = bf16_lo((uint32_t)qraw[r][0][j]);
-        x[2 * j + 1] = bf16_hi((uint32_t)qraw[r][0][j]);
-        x[8 + 2 * j] = bf16_lo((uint32_t)qraw[r][1][j]);
-        x[8 + 2 * j + 1] = bf16_hi((uint32_t)qraw[r][1][j]);
-      }
-      float am = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
-      am = fmaxf(am, __shfl_xor(am, 1, 64));
-      am = fmaxf(am, __shfl_xor(am, 2, 64));
-      am = fmaxf(am, __shfl_xor(am, 4, 64));
-      const int e = pow2_scale_exp(am);
-      const float inv = ldexpf(1.0f, -e);
-      v4i c;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        c[j] = (int)cvt4_e4m3(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv,
-                              x[4 * j + 3] * inv);
-      *reinterpret_cast<v4i*>(&q8s[r][qh][qpart * 16]) = c;
-      if (qpart == 0) wps[r][qh] = hw[r] * ldexpf(1.0f, e);
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo((uint32_t)qraw[r][0][j]);
+      x[2 * j + 1] = bf16_hi((uint32_t)qraw[r][0][j]);
+      x[8 + 2 * j] = bf16_lo((uint32_t)qraw[r][1][j]);
+      x[8 + 2 * j + 1] = bf16_hi((uint32_t)qraw[r][1][j]);
     }
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    am = fmaxf(am, __shfl_xor(am, 4, 64));
+    const int e = pow2_scale_exp(am);
+    const float inv = ldexpf(1.0f, -e);
+    v4i c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c[j] = (int)cvt4_e4m3(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv,
+                            x[4 * j + 3] * inv);
+    *reinterpret_cast<v4i*>(&q8s[r][qh][qpart * 16]) = c;
+    if (qpart == 0) wps[r][qh] = hw[r] * ldexpf(1.0f, e);
   }
   __syncthreads();
 
-  // 4. score the pages in load order
+  // 4. the wave's groups: score each ring slot, refill it at once, and after four pages
+  //    select the group's candidates while the next group's keys stream in
+  uint32_t keys[R][4];
+  auto score_page = [&](int s, int jj, const KeyPage& cur) {
+    const int p = page_of(s);
+    const bool valid = p < p_end;
+    const int t = p * kPage + lane;
 #pragma unroll
-  for (int round = 0; round < kRounds; ++round) {
+    for (int r = 0; r < R; ++r) {
+      const uint8_t* qa = &q8s[r][n][64 * g];
+      const v4i a0 = *reinterpret_cast<const v4i*>(qa);
+      const v4i a1 = *reinterpret_cast<const v4i*>(qa + 16);
+      const v4i a2 = *reinterpret_cast<const v4i*>(qa + 32);
+      const v4i a3 = *reinterpret_cast<const v4i*>(qa + 48);
+      const v8i A0 = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const v8i A1 = v8i{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+      const v16f z = {};
+      v16f d0 = mfma_32x32x64_fp8(A0, cur.k[0][0], z);
+      d0 = mfma_32x32x64_fp8(A1, cur.k[0][1], d0);
+      v16f d1 = mfma_32x32x64_fp8(A0, cur.k[1][0], z);
+      d1 = mfma_32x32x64_fp8(A1, cur.k[1][1], d1);
+      // output register i of lane l is head 8*(i/4) + 4*g + i%4 for token l%32
+      float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const int p = p0 + wave + 4 * (round * NF + j);
-      if (p < p_end) {
-        const KeyPage& cur = kp[j];
-        const int t = p * kPage + lane;
+      for (int a = 0; a < 4; ++a) {
+        const v4f w = *reinterpret_cast<const v4f*>(&wps[r][8 * a + 4 * g]);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (r < nr) {
-            const uint8_t* qa = &q8s[r][n][64 * g];
-            const v4i a0 = *reinterpret_cast<const v4i*>(qa);
-            const v4i a1 = *reinterpret_cast<const v4i*>(qa + 16);
-            const v4i a2 = *reinterpret_cast<const v4i*>(qa + 32);
-            const v4i a3 = *reinterpret_cast<const v4i*>(qa + 48);
-            const v8i A0 = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            const v8i A1 = v8i{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-            const v16f z = {};
-            v16f d0 = mfma_32x32x64_fp8(A0, cur.k[0][0], z);
-            d0 = mfma_32x32x64_fp8(A1, cur.k[0][1], d0);
-            v16f d1 = mfma_32x32x64_fp8(A0, cur.k[1][0], z);
-            d1 = mfma_32x32x64_fp8(A1, cur.k[1][1], d1);
-            // output register i of lane l is head 8*(i/4) + 4*g + i%4 for token l%32
-            float acc0 = 0.f, acc1 = 0.f;
+        for (int c = 0; c < 4; ++c) {
+          acc0 = fmaf(w[c], fmaxf(d0[4 * a + c], 0.f), acc0);
+          acc1 = fmaf(w[c], fmaxf(d1[4 * a + c], 0.f), acc1);
+        }
+      }
+      // lanes 0..31: (half-0 partial, partner's half-0 partial); lanes 32..63: half 1
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0),
+                                                       __float_as_uint(acc1), false, false);
+      const float score = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * cur.s;
+      if constexpr (STAGE) {
+        if (valid) sbuf[r][(p - p0) * kPage + lane] = score;
+      } else {
+        if (valid && r < nr && t < L) scores[(int64_t)(r0 + r) * score_stride + t] = score;
+      }
+      keys[r][jj] = valid ? score_key(score) : kSentinel;
+    }
+  };
+  auto select_group = [&](int gi) {
+    if constexpr (CAND) {
+      const int grp = p0 / kGroupPages + kWaves * gi + wave;  // group index in the request
+      const int t0 = grp * kGroupTok;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-              const v4f w = *reinterpret_cast<const v4f*>(&wps[r][8 * a + 4 * g]);
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                acc0 = fmaf(w[c], fmaxf(d0[4 * a + c], 0.f), acc0);
-                acc1 = fmaf(w[c], fmaxf(d1[4 * a + c], 0.f), acc1);
-              }
-            }
-            // lanes 0..31: (half-0 partial, partner's half-0 partial); lanes 32..63: half 1
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0),
-                                                             __float_as_uint(acc1), false, false);
-            const float score = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * cur.s;
-            if (t < L) scores[(int64_t)(r0 + r) * score_stride + t] = score;
+      for (int r = 0; r < R; ++r) {
+        const int row = r0 + r;
+        const int n_vis = L - (q1 - q0) + (row - q0) + 1;
+        if (r < nr && n_vis > cand.k && t0 < n_vis) {
+          const int m = group_cand_count(n_vis, cand.k);
+          const int gl = kWaves * gi + wave;  // group index in the workgroup
+          if constexpr (CSTAGE) {
+            group_select(keys[r], min(kGroupTok, n_vis - t0), m, t0, &cbuf_key[r][gl * m],
+                         &cbuf_idx[r][gl * m], &cbuf_info[r][gl]);
+          } else {
+            const int64_t base = (int64_t)row * cand.row_cap + (int64_t)grp * m;
+            group_select(keys[r], min(kGroupTok, n_vis - t0), m, t0, cand.key + base,
+                         cand.idx + base, cand.info + (int64_t)row * cand.num_groups + grp);
           }
         }
       }
     }
-    if (round + 1 < kRounds) {
+  };
+#pragma unroll 1
+  for (int gi = 0; gi + 1 < ng; ++gi) {
 #pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        const int phys = __builtin_amdgcn_readlane(bt_lane, (round + 1) * NF + j);
-        load_key_page(kp[j], key_pages + (int64_t)phys * page_stride, lane);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int s = 4 * gi + jj;
+      score_page(s, jj, kp[jj % NF]);
+      load_key_page(kp[jj % NF], page_ptr(s + NF), lane);
+    }
+    select_group(gi);
+  }
+  if (ng > 0) {  // the last group loads nothing past itself
+    const int gi = ng - 1;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int s = 4 * gi + jj;
+      score_page(s, jj, kp[jj % NF]);
+      if (jj + NF < 4) load_key_page(kp[jj % NF], page_ptr(s + NF), lane);
+    }
+    select_group(gi);
+  }
+
+  // 5. write what was staged: scores (and candidates) of the workgroup, coalesced
+  if constexpr (STAGE) {
+    __syncthreads();
+    const int seg_tok = min(p_end * kPage, L) - p0 * kPage;
+    for (int r = 0; r < nr; ++r) {
+      float* dst = scores + (int64_t)(r0 + r) * score_stride + p0 * kPage;
+      for (int i = tid; i < seg_tok; i += 256) dst[i] = sbuf[r][i];
+    }
+    if constexpr (CAND) {
+      const int g_lo = p0 / kGroupPages;
+      for (int r = 0; r < nr; ++r) {
+        const int row = r0 + r;
+        const int n_vis = L - (q1 - q0) + (row - q0) + 1;
+        if (n_vis <= cand.k) continue;
+        const int n_grp = min(g_lo + seg_groups, (n_vis + kGroupTok - 1) / kGroupTok) - g_lo;
+        if (n_grp <= 0) continue;
+        const int m = group_cand_count(n_vis, cand.k);
+        const int64_t base = (int64_t)row * cand.row_cap + (int64_t)g_lo * m;
+        for (int i = tid; i < n_grp * m; i += 256) {
+          cand.key[base + i] = cbuf_key[r][i];
+          cand.idx[base + i] = cbuf_idx[r][i];
+        }
+        for (int i = tid; i < n_grp; i += 256)
+          cand.info[(int64_t)row * cand.num_groups + g_lo + i] = cbuf_info[r][i];
       }
     }
   }
@@ -231,25 +331,47 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
                               const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
                               const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
                               const int32_t* block_table, int bt_stride, float* scores,
-                              int64_t score_stride, hipStream_t st) {
-  (void)n_q;
+                              int64_t score_stride, int k, void* topk_ws, hipStream_t st) {
   const int max_pages = (max_seq_len + kPage - 1) / kPage;
-  const unsigned gx = (unsigned)((max_pages + kPagesPerWg - 1) / kPagesPerWg);
   int R = 8;
   if (max_q_per_seq <= 1) R = 1;
   else if (max_q_per_seq <= 2) R = 2;
   else if (max_q_per_seq <= 4) R = 4;
   const unsigned gz = (unsigned)((max_q_per_seq + R - 1) / R);
+  // groups per wave: the longest segments (up to the staging limit of R) that still give
+  // >= 1,024 workgroups (4 per CU)
+  int G = R == 1 ? 4 : (R == 2 ? 2 : 1);
+  while (G > 1 && (int64_t)num_seqs * gz *
+                          ((max_pages + kWaves * kGroupPages * G - 1) / (kWaves * kGroupPages * G)) <
+                      1024)
+    G >>= 1;
+#ifdef DSA_INDEX_GROUPS_PER_WAVE  // build-time override for tuning sweeps (at most the limit)
+  G = std::min(DSA_INDEX_GROUPS_PER_WAVE, R == 1 ? 4 : (R == 2 ? 2 : 1));
+#endif
+  const unsigned gx = (unsigned)((max_pages + kWaves * kGroupPages * G - 1) / (kWaves * kGroupPages * G));
   const dim3 grid(gx, (unsigned)num_seqs, gz), block(256);
-#define DSA_LAUNCH_IDX(RR)                                                                       \
-  hipLaunchKernelGGL(index_score_kernel<RR>, grid, block, 0, st, cu_q, seq_lens, q, head_w,      \
-                     key_pages, key_page_stride, block_table, bt_stride, scores, score_stride)
-  switch (R) {
-    case 1: DSA_LAUNCH_IDX(1); break;
-    case 2: DSA_LAUNCH_IDX(2); break;
-    case 4: DSA_LAUNCH_IDX(4); break;
-    default: DSA_LAUNCH_IDX(8); break;
+  CandOut cand{nullptr, nullptr, nullptr, 0, 0, k};
+  if (topk_ws) {
+    const TopkBuffers t = topk_buffers(topk_ws, n_q, max_seq_len, k);
+    cand = CandOut{t.cand_key, t.cand_idx, t.info, (int64_t)t.plan.row_cap, t.plan.num_groups, k};
   }
+#define DSA_LAUNCH_IDX(RR, CC)                                                                   \
+  hipLaunchKernelGGL((index_score_kernel<RR, CC>), grid, block, 0, st, cu_q, seq_lens, q, head_w, \
+                     key_pages, key_page_stride, block_table, bt_stride, scores, score_stride, G,  \
+                     cand)
+#define DSA_LAUNCH_R(CC)                 \
+  switch (R) {                           \
+    case 1: DSA_LAUNCH_IDX(1, CC); break; \
+    case 2: DSA_LAUNCH_IDX(2, CC); break; \
+    case 4: DSA_LAUNCH_IDX(4, CC); break; \
+    default: DSA_LAUNCH_IDX(8, CC); break; \
+  }
+  if (topk_ws) {
+    DSA_LAUNCH_R(true)
+  } else {
+    DSA_LAUNCH_R(false)
+  }
+#undef DSA_LAUNCH_R
 #undef DSA_LAUNCH_IDX
   return hipGetLastError();
 }

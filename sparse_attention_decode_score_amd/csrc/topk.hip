@@ -5,180 +5,31 @@
 // Pro", with exact selection and a consistent tie rule, "Exact top-k merge with ~10x less
 // traffic" and "Inter-GPU communication").
 //
-// Two passes, the on-chip form of the page's exact one-round merge:
-//  pass 1  one workgroup per (row, 8,192-token chunk) selects the chunk's best m candidates
-//          (radix select on order-preserving uint32 keys in LDS, 11+11+10-bit digits) and
-//          writes them in token order, padded with sentinels, plus the chunk's m-th element.
-//  pass 2  one workgroup per row radix-selects the top k of the candidates.  A chunk that
-//          had more than m visible tokens could hold more winners than it sent exactly when
-//          its m-th element beats the selection's k-th; then the row is re-selected from all
-//          of its scores ("detect and resend"), so the output is always exact.
+// Two passes, the on-chip form of the page's exact one-round merge, with 256-token groups in
+// the role of the page's per-GPU shards:
+//  pass 1  one wave per (row, group) keeps the group's best m candidates (m from
+//          group_cand_count) in token order, plus the group's m-th element.  The fused
+//          indexer runs this pass while the scores are still in registers; the kernel below
+//          runs it from stored scores.
+//  pass 2  one 1,024-thread workgroup per row selects the top k of the candidates.  A group
+//          that had more than m visible tokens can hide winners exactly when its m-th
+//          element beats the selection's k-th; those groups (only) are re-read in full from
+//          the scores and the row is selected again, which is exact (every unsent token of
+//          an unflagged group ranks below the candidates' k-th, hence below the true k-th).
 // Selections are written in increasing token order; no float atomics, so the result does
 // not depend on how rows are batched.
+#include <algorithm>
+#include <type_traits>
+
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
+#include "dsa_select.hpp"
 
 namespace dsa {
 
 namespace {
 
-constexpr int kNT = 256;       // threads per workgroup
-constexpr int kE = 8;          // consecutive elements per thread per compaction round
-constexpr int kChunk = 8192;   // tokens per first-pass chunk
-constexpr uint32_t kSentinel = 0u;  // below every real key (NaN maps to 1)
-constexpr int kFinalLds = 12288;    // candidates the final pass keeps in LDS
-
-__device__ __forceinline__ uint32_t score_key(float f) {
-  const uint32_t k = order_key(f);
-  return k == 0u ? 1u : k;
-}
-
-// Block-wide exclusive prefix sum over thread order; *total gets the block sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh /*>= 5 ints*/) {
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kNT / 64; ++i) {
-    const int s = sh[i];
-    before += (i < w) ? s : 0;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + x - v;
-}
-
-// Block-wide sum of v over threads with a larger index than this one.
-__device__ __forceinline__ int block_suffix_excl(int v, int* sh) {
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_down(x, o, 64);
-    if (lane + o < 64) x += y;
-  }
-  if (lane == 0) sh[w] = x;
-  __syncthreads();
-  int after = 0;
-#pragma unroll
-  for (int i = 0; i < kNT / 64; ++i) after += (i > w) ? sh[i] : 0;
-  __syncthreads();
-  return after + x - v;
-}
-
-// Finds the key K of the want-th largest element (1 <= want <= n) among get(0..n-1) and
-// the number r >= 1 of elements equal to K that belong to the top `want` (the first r
-// equal ones in index order).  hist: 2048 LDS counters.  sh: >= 8 LDS ints.
-template <class Get>
-__device__ void radix_threshold(const Get& get, int n, int want, uint32_t* hist, int* sh,
-                                uint32_t& K, int& r) {
-  uint32_t prefix = 0, mask = 0;
-  const int tid = threadIdx.x;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int bits = pass == 2 ? 10 : 11;
-    const uint32_t dmask = (1u << bits) - 1u;
-    for (int i = tid; i < 2048; i += kNT) hist[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < n; i += kNT) {
-      const uint32_t k = get(i);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    int local = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) local += (int)hist[tid * 8 + j];
-    const int above = block_suffix_excl(local, sh);
-    if (above < want && above + local >= want) {
-      int c = above;
-      for (int j = 7; j >= 0; --j) {
-        const int hcount = (int)hist[tid * 8 + j];
-        if (c + hcount >= want) {
-          sh[4] = tid * 8 + j;
-          sh[5] = want - c;
-          break;
-        }
-        c += hcount;
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = (uint32_t)sh[4];
-    want = sh[5];
-    __syncthreads();
-    prefix |= bin << shift;
-    mask |= dmask << shift;
-  }
-  K = prefix;
-  r = want;
-}
-
-// Visits, in index order, every element with key > K plus the first r with key == K,
-// calling emit(position, index, key); positions are 0, 1, ... in index order.  `limit` is
-// the number that will be emitted (elements above K plus r).  Returns the number emitted;
-// *last_eq gets the index of the r-th equal element (-1 if r == 0).
-template <class Get, class Emit>
-__device__ int ordered_compact(const Get& get, int n, uint32_t K, int r, int limit,
-                               const Emit& emit, int* sh, int* last_eq) {
-  const int tid = threadIdx.x;
-  int out_base = 0, eq_base = 0;
-  if (tid == 0) sh[6] = -1;
-#pragma unroll 1
-  for (int base = 0; base < n; base += kNT * kE) {
-    uint32_t keys[kE];
-    int n_eq = 0, n_gt = 0;
-    const int i0 = base + tid * kE;
-#pragma unroll
-    for (int j = 0; j < kE; ++j) {
-      keys[j] = (i0 + j < n) ? get(i0 + j) : 0u;
-      const bool valid = i0 + j < n;
-      n_eq += (valid && keys[j] == K) ? 1 : 0;
-      n_gt += (valid && keys[j] > K) ? 1 : 0;
-    }
-    int eq_tot;
-    const int eq_before = eq_base + block_excl_scan(n_eq, &eq_tot, sh);
-    int n_take = n_gt;
-    {
-      int e = eq_before;
-#pragma unroll
-      for (int j = 0; j < kE; ++j)
-        if (i0 + j < n && keys[j] == K) { n_take += (e < r) ? 1 : 0; ++e; }
-    }
-    int take_tot;
-    int pos = out_base + block_excl_scan(n_take, &take_tot, sh);
-    {
-      int e = eq_before;
-#pragma unroll
-      for (int j = 0; j < kE; ++j) {
-        if (i0 + j >= n) break;
-        const bool gt = keys[j] > K;
-        const bool eq = keys[j] == K;
-        bool take = gt;
-        if (eq) {
-          take = e < r;
-          if (e == r - 1) sh[6] = i0 + j;
-          ++e;
-        }
-        if (take) emit(pos++, i0 + j, keys[j]);
-      }
-    }
-    out_base += take_tot;
-    eq_base += eq_tot;
-    if (out_base >= limit) break;  // block-uniform: everything selected has been emitted
-  }
-  __syncthreads();
-  *last_eq = sh[6];
-  __syncthreads();
-  return out_base;
-}
+constexpr int kMaxTopk = 4096;
 
 // Request and absolute position of query row `row`: one wave-wide ballot over cu_q per 64
 // requests (rows are grouped by request and are its last tokens).
@@ -196,87 +47,84 @@ __device__ __forceinline__ void row_of(const int32_t* cu_q, const int32_t* seq_l
   pos = seq_lens[b] - (c1 - c0) + (row - c0);
 }
 
-// Candidates kept per chunk for a row with n_vis visible tokens: 1.5x the winners a full
-// chunk holds on average (the page's exact merge sends 1.5 x 2048 / W per shard), rounded
-// up to 64, at least 64 and at most a whole chunk.
-__host__ __device__ __forceinline__ int cand_per_chunk(int n_vis, int k) {
-  const int64_t num = (int64_t)3 * k * kChunk;
-  const int64_t den = (int64_t)2 * n_vis;
-  int64_t m = (num + den - 1) / den;
-  m = (m + 63) / 64 * 64;
-  if (m < 64) m = 64;
-  if (m > kChunk) m = kChunk;
-  return (int)m;
-}
-
-struct ChunkInfo {
-  int count;      // candidates written (<= m), rest are sentinels
-  int saturated;  // the chunk had more than m visible tokens
-  uint32_t key;   // its m-th element (when saturated)
-  int idx;
-};
-
-// ---------------------------------------------------------------- pass 1
-__global__ __launch_bounds__(kNT) void topk_chunk_kernel(
+// ---------------------------------------------------------------- pass 1 from stored scores
+// grid (ceil(groups / 4), n_q), 4 waves: wave w takes group 4 * blockIdx.x + w of the row.
+__global__ __launch_bounds__(256) void topk_group_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int num_seqs,
-    const float* __restrict__ scores, int64_t score_stride, int k, int num_chunks,
+    const float* __restrict__ scores, int64_t score_stride, int k, int num_groups,
     int64_t row_cap, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx,
     ChunkInfo* __restrict__ info) {
-  __shared__ __attribute__((aligned(16))) uint32_t keys[kChunk];
-  __shared__ uint32_t hist[2048];
-  __shared__ int sh[8];
-  const int row = blockIdx.y, c = blockIdx.x;
+  const int row = blockIdx.y;
   int b, pos;
   row_of(cu_q, seq_lens, num_seqs, row, b, pos);
   const int n_vis = pos + 1;
-  if (n_vis <= k) return;  // pass 2 takes every visible token
-  const int start = c * kChunk;
-  if (start >= n_vis) return;
-  const int n = min(kChunk, n_vis - start);
-  const int m = cand_per_chunk(n_vis, k);
-  const float* src = scores + (int64_t)row * score_stride + start;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < n; i += kNT) keys[i] = score_key(src[i]);
-  __syncthreads();
+  const int g = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t0 = g * kGroupTok;
+  if (n_vis <= k || t0 >= n_vis) return;  // wave-uniform; no barriers in this kernel
+  const int lane = lane_id();
+  const float* src = scores + (int64_t)row * score_stride + t0;
+  const int n = min(kGroupTok, n_vis - t0);
+  uint32_t keys[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) keys[j] = 64 * j + lane < n ? score_key(src[64 * j + lane]) : kSentinel;
+  const int m = group_cand_count(n_vis, k);
+  const int64_t base = (int64_t)row * row_cap + (int64_t)g * m;
+  group_select(keys, n, m, t0, cand_key + base, cand_idx + base,
+               info + (int64_t)row * num_groups + g);
+}
 
-  const int64_t cbase = (int64_t)row * row_cap + (int64_t)c * m;
-  uint32_t* ck = cand_key + cbase;
-  int32_t* ci = cand_idx + cbase;
-  ChunkInfo* inf = info + (int64_t)row * num_chunks + c;
-  if (n <= m) {
-    for (int i = tid; i < m; i += kNT) {
-      ck[i] = i < n ? keys[i] : kSentinel;
-      ci[i] = i < n ? start + i : 0x7FFFFFFF;
+// Copies, in element order, every element of get(0 .. n-1) whose key is >= K into
+// lkey / lidx (key, element index) while they fit in kFinalTile slots.  Returns the number of
+// such elements (more than kFinalTile: the copy is incomplete).
+template <class Get>
+__device__ int gather_at_least(const Get& get, int n, uint32_t K, uint32_t* lkey, int32_t* lidx,
+                               int* red, int& parity) {
+  const int tid = threadIdx.x;
+  constexpr int E = 16;
+  constexpr int kTile = kFinalThreads * E;
+  int kept = 0;
+#pragma unroll 1
+  for (int base = 0; base < n; base += kTile) {
+    uint32_t tk[E];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = base + tid * E + j;
+      tk[j] = e < n ? get(e) : kSentinel;
+      c += tk[j] >= K ? 1 : 0;
     }
-    if (tid == 0) *inf = ChunkInfo{n, 0, 0u, -1};
-    return;
+    int tot;
+    int pos = kept + block_excl_scan(c, &tot, red, parity);
+    if (kept + tot <= kFinalTile) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if (tk[j] >= K) {
+          lkey[pos] = tk[j];
+          lidx[pos] = base + tid * E + j;
+          ++pos;
+        }
+      }
+    }
+    kept += tot;
+    if (kept > kFinalTile) break;  // uniform
   }
-  auto get = [&](int i) { return keys[i]; };
-  uint32_t K;
-  int r;
-  radix_threshold(get, n, m, hist, sh, K, r);
-  int last_eq;
-  auto emit = [&](int p, int i, uint32_t key) {
-    ck[p] = key;
-    ci[p] = start + i;
-  };
-  ordered_compact(get, n, K, r, m, emit, sh, &last_eq);
-  if (tid == 0) *inf = ChunkInfo{m, 1, K, start + last_eq};
+  __syncthreads();
+  return kept;
 }
 
 // ---------------------------------------------------------------- pass 2
-__global__ __launch_bounds__(kNT) void topk_final_kernel(
+__global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int num_seqs,
-    const float* __restrict__ scores, int64_t score_stride, int k, int num_chunks,
+    const float* __restrict__ scores, int64_t score_stride, int k, int num_groups,
     int64_t row_cap, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
     const ChunkInfo* __restrict__ info, const int32_t* __restrict__ block_table, int bt_stride,
     int32_t* __restrict__ topk_idx, int32_t* __restrict__ topk_slot) {
-  __shared__ int out[4096];
-  __shared__ uint32_t hist[2048];
-  __shared__ int sh[8];
-  __shared__ int redo;
-  __shared__ __attribute__((aligned(16))) uint32_t lkey[kFinalLds];
-  __shared__ __attribute__((aligned(16))) int32_t lidx[kFinalLds];
+  __shared__ __attribute__((aligned(16))) uint32_t lkey[kFinalTile];
+  __shared__ __attribute__((aligned(16))) int32_t lidx[kFinalTile];
+  __shared__ int out[kMaxTopk];
+  __shared__ __attribute__((aligned(16))) int red[2 * kFinalWaves];
+  __shared__ int note;
+  __shared__ uint32_t bucket[kBucketMax];
   const int row = blockIdx.x, tid = threadIdx.x;
   int b, pos;
   row_of(cu_q, seq_lens, num_seqs, row, b, pos);
@@ -284,61 +132,129 @@ __global__ __launch_bounds__(kNT) void topk_final_kernel(
   int32_t* oi = topk_idx + (int64_t)row * k;
   int32_t* os = topk_slot ? topk_slot + (int64_t)row * k : nullptr;
   const int32_t* bt = block_table ? block_table + (int64_t)b * bt_stride : nullptr;
+  const float* src = scores + (int64_t)row * score_stride;
+  auto score_get = [&](int i) { return score_key(src[i]); };
+  auto ident = [](int i) { return i; };
 
   int n_out;
   if (n_vis <= k) {
-    for (int i = tid; i < n_vis; i += kNT) out[i] = i;
+    for (int i = tid; i < n_vis; i += kFinalThreads) out[i] = i;
     n_out = n_vis;
-    __syncthreads();
   } else {
-    const int n_chunks = (n_vis + kChunk - 1) / kChunk;
-    const int m = cand_per_chunk(n_vis, k);
-    const int n_cand = n_chunks * m;  // >= 1.5 k by construction of m
+    const int n_groups = (n_vis + kGroupTok - 1) / kGroupTok;
+    const int m = group_cand_count(n_vis, k);
+    const int n_cand = n_groups * m;
     const uint32_t* ck = cand_key + (int64_t)row * row_cap;
     const int32_t* ci = cand_idx + (int64_t)row * row_cap;
+    const ChunkInfo* inf = info + (int64_t)row * num_groups;
     uint32_t K;
-    int r;
-    int last_eq;
     int I;
-    if (n_cand <= kFinalLds) {
-      // candidates fit in LDS: one coalesced read, then every pass runs on-chip
-      for (int i = tid; i < n_cand; i += kNT) {
-        lkey[i] = ck[i];
-        lidx[i] = ci[i];
+    if (n_cand <= kFinalTile) {
+      // this thread's E consecutive candidates straight into registers (n_cand and the
+      // row's slots are multiples of 4 and 16-byte aligned)
+      auto run = [&](auto e_tag) {
+        constexpr int E = decltype(e_tag)::value;
+        uint32_t kv[E];
+        int vv[E];
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const int e = tid * E + 4 * q;
+          v4i a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+          if (e < n_cand) {
+            a = *reinterpret_cast<const v4i*>(ck + e);
+            c = *reinterpret_cast<const v4i*>(ci + e);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kv[4 * q + j] = (uint32_t)a[j];
+            vv[4 * q + j] = c[j];
+          }
+        }
+        block_topk_regs<E>(kv, vv, k, out, red, &note, bucket, &K, &I);
+      };
+      switch (final_per_thread(n_cand)) {
+        case 8: run(std::integral_constant<int, 8>()); break;
+        case 16: run(std::integral_constant<int, 16>()); break;
+        default: run(std::integral_constant<int, 32>()); break;
+      }
+    } else {
+      block_topk([&](int i) { return ck[i]; }, [&](int i) { return ci[i]; }, n_cand, k, out, red,
+                 &note, bucket, &K, &I);
+    }
+    // groups whose m-th element beats the k-th selected may hide winners
+    auto flagged = [&](int g) {
+      const ChunkInfo ic = inf[g];
+      return ic.saturated && (ic.key > K || (ic.key == K && ic.idx < I));
+    };
+    int any = 0;
+#pragma unroll 4
+    for (int g = tid; g < n_groups; g += kFinalThreads) any |= flagged(g) ? 1 : 0;
+    int parity = 0;
+    if (block_sum(any, red, parity) > 0) {
+      // Rebuild the candidate list in token order, flagged groups in full and the others as
+      // sent: group starts go to LDS (`out` is free until the next selection), then every
+      // thread fills its own elements, locating each one's group by binary search.
+      int total = 0;
+      if (n_groups <= kMaxTopk) {
+        constexpr int GPT = kMaxTopk / kFinalThreads;  // groups per thread
+        int len[GPT], sum = 0;
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+          const int g = GPT * tid + q;
+          len[q] = g >= n_groups ? 0
+                                 : (flagged(g) ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
+          sum += len[q];
+        }
+        int at = block_excl_scan(sum, &total, red, parity);
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+          const int g = GPT * tid + q;
+          if (g < n_groups) out[g] = at;  // every group has >= 1 element: starts increase
+          at += len[q];
+        }
+      } else {
+        total = kFinalTile + 1;
       }
       __syncthreads();
-      auto getc = [&](int i) { return lkey[i]; };
-      radix_threshold(getc, n_cand, k, hist, sh, K, r);
-      auto emitc = [&](int p, int i, uint32_t) { out[p] = lidx[i]; };
-      ordered_compact(getc, n_cand, K, r, k, emitc, sh, &last_eq);
-      I = last_eq >= 0 ? lidx[last_eq] : 0x7FFFFFFF;
-    } else {
-      auto getc = [&](int i) { return ck[i]; };
-      radix_threshold(getc, n_cand, k, hist, sh, K, r);
-      auto emitc = [&](int p, int i, uint32_t) { out[p] = ci[i]; };
-      ordered_compact(getc, n_cand, K, r, k, emitc, sh, &last_eq);
-      I = last_eq >= 0 ? ci[last_eq] : 0x7FFFFFFF;
-    }
-    if (tid == 0) redo = 0;
-    __syncthreads();
-    const ChunkInfo* inf = info + (int64_t)row * num_chunks;
-    for (int c = tid; c < n_chunks; c += kNT) {
-      const ChunkInfo ic = inf[c];
-      // a saturated chunk whose m-th element beats the k-th selected may hide winners
-      if (ic.saturated && (ic.key > K || (ic.key == K && ic.idx < I))) redo = 1;
-    }
-    __syncthreads();
-    if (redo) {
-      const float* src = scores + (int64_t)row * score_stride;
-      auto gets = [&](int i) { return score_key(src[i]); };
-      radix_threshold(gets, n_vis, k, hist, sh, K, r);
-      auto emits = [&](int p, int i, uint32_t) { out[p] = i; };
-      ordered_compact(gets, n_vis, K, r, k, emits, sh, &last_eq);
+      if (total <= kFinalTile) {
+#pragma unroll 8
+        for (int e = tid; e < total; e += kFinalThreads) {
+          int lo = 0, hi = n_groups - 1;  // the last group starting at or before e
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (out[mid] <= e) lo = mid;
+            else hi = mid - 1;
+          }
+          const int i = e - out[lo];
+          if (flagged(lo)) {
+            const int t = lo * kGroupTok + i;
+            lkey[e] = score_key(src[t]);
+            lidx[e] = t;
+          } else {
+            lkey[e] = ck[(int64_t)lo * m + i];
+            lidx[e] = ci[(int64_t)lo * m + i];
+          }
+        }
+        __syncthreads();
+        block_topk([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, total, k,
+                   out, red, &note, bucket, &K, &I);
+      } else {
+        // Too many to hold: every winner has a key >= K (the candidates' k-th is a lower
+        // bound of the true k-th), so keep those, in token order, if they fit on chip.
+        const int kept = gather_at_least(score_get, n_vis, K, lkey, lidx, red, parity);
+        if (kept <= kFinalTile) {
+          block_topk([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, kept, k,
+                     out, red, &note, bucket, &K, &I);
+        } else {
+          block_topk(score_get, ident, n_vis, k, out, red, &note, bucket, &K, &I);
+        }
+      }
     }
     n_out = k;
-    __syncthreads();
   }
-  for (int i = tid; i < k; i += kNT) {
+  __syncthreads();
+#pragma unroll 8
+  for (int i = tid; i < k; i += kFinalThreads) {
     const int t = i < n_out ? out[i] : -1;
     oi[i] = t;
     if (os) os[i] = t < 0 ? -1 : bt[t >> 6] * kPage + (t & (kPage - 1));
@@ -347,19 +263,21 @@ __global__ __launch_bounds__(kNT) void topk_final_kernel(
 
 }  // namespace
 
+// Candidate slots reserved per row: the worst case over rows of groups x candidates; for c
+// groups the smallest visible length with candidates is max(k + 1, (c - 1) * 256 + 1).
 TopkPlan topk_plan(int max_seq_len, int k) {
   TopkPlan p;
-  p.chunk = kChunk;
-  p.num_chunks = (max_seq_len + kChunk - 1) / kChunk;
-  if (p.num_chunks < 1) p.num_chunks = 1;
-  // worst case over rows: for c chunks the smallest visible length is (c-1)*chunk + 1
+  p.num_groups = (max_seq_len + kGroupTok - 1) / kGroupTok;
+  if (p.num_groups < 1) p.num_groups = 1;
   int64_t cap = 0;
-  for (int c = 1; c <= p.num_chunks; ++c) {
-    const int n_vis = c == 1 ? k + 1 : (c - 1) * kChunk + 1;
-    const int64_t need = (int64_t)c * cand_per_chunk(n_vis, k);
+  for (int c = 1; c <= p.num_groups; ++c) {
+    const int lo = std::max(k + 1, (c - 1) * kGroupTok + 1);
+    if (lo > c * kGroupTok) continue;
+    const int64_t need = (int64_t)c * group_cand_count(lo, k);
     if (need > cap) cap = need;
   }
   p.row_cap = (cap + 63) / 64 * 64;
+  if (p.row_cap < 64) p.row_cap = 64;
   return p;
 }
 
@@ -368,28 +286,44 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t topk_workspace_bytes(int n_q, int max_seq_len, int k) {
   const TopkPlan p = topk_plan(max_seq_len, k);
   const size_t nc = (size_t)n_q * p.row_cap;
-  return align256(nc * 4) * 2 + align256((size_t)n_q * p.num_chunks * sizeof(ChunkInfo));
+  return align256(nc * 4) * 2 + align256((size_t)n_q * p.num_groups * sizeof(ChunkInfo));
+}
+
+TopkBuffers topk_buffers(void* workspace, int n_q, int max_seq_len, int k) {
+  const TopkPlan p = topk_plan(max_seq_len, k);
+  const size_t nc = (size_t)n_q * p.row_cap;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  TopkBuffers t;
+  t.plan = p;
+  t.cand_key = reinterpret_cast<uint32_t*>(ws);
+  t.cand_idx = reinterpret_cast<int32_t*>(ws + align256(nc * 4));
+  t.info = reinterpret_cast<ChunkInfo*>(ws + 2 * align256(nc * 4));
+  return t;
+}
+
+hipError_t launch_topk_final(int num_seqs, int n_q, const int32_t* cu_q, const int32_t* seq_lens,
+                             const float* scores, int64_t score_stride, int k,
+                             const TopkBuffers& t, const int32_t* block_table, int bt_stride,
+                             int32_t* topk_idx, int32_t* topk_slot, hipStream_t st) {
+  hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)n_q), dim3(kFinalThreads), 0, st, cu_q,
+                     seq_lens, num_seqs, scores, score_stride, k, t.plan.num_groups,
+                     (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info, block_table,
+                     bt_stride, topk_idx, topk_slot);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu_q,
                        const int32_t* seq_lens, const float* scores, int64_t score_stride, int k,
                        const int32_t* block_table, int bt_stride, int32_t* topk_idx,
                        int32_t* topk_slot, void* workspace, hipStream_t st) {
-  const TopkPlan p = topk_plan(max_seq_len, k);
-  const size_t nc = (size_t)n_q * p.row_cap;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint32_t* cand_key = reinterpret_cast<uint32_t*>(ws);
-  int32_t* cand_idx = reinterpret_cast<int32_t*>(ws + align256(nc * 4));
-  ChunkInfo* info = reinterpret_cast<ChunkInfo*>(ws + 2 * align256(nc * 4));
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)p.num_chunks, (unsigned)n_q), dim3(kNT), 0,
-                     st, cu_q, seq_lens, num_seqs, scores, score_stride, k, p.num_chunks,
-                     (int64_t)p.row_cap, cand_key, cand_idx, info);
+  const TopkBuffers t = topk_buffers(workspace, n_q, max_seq_len, k);
+  hipLaunchKernelGGL(topk_group_kernel, dim3((unsigned)((t.plan.num_groups + 3) / 4), (unsigned)n_q),
+                     dim3(256), 0, st, cu_q, seq_lens, num_seqs, scores, score_stride, k,
+                     t.plan.num_groups, (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)n_q), dim3(kNT), 0, st, cu_q, seq_lens,
-                     num_seqs, scores, score_stride, k, p.num_chunks, (int64_t)p.row_cap,
-                     cand_key, cand_idx, info, block_table, bt_stride, topk_idx, topk_slot);
-  return hipGetLastError();
+  return launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k, t, block_table,
+                           bt_stride, topk_idx, topk_slot, st);
 }
 
 }  // namespace dsa

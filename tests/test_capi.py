@@ -49,13 +49,18 @@ def _err():
 
 def test_index_score_rejects_bad_host_args(L):
     f = L.dsa_index_score
-    ok_args = [2, 3, 1000, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 8448, FAKE, 16, FAKE, 1000, None]
+    cand_need = L.dsa_topk_workspace_size(3, 1000, 2048)
+    assert cand_need > 0
+    ok_args = [2, 3, 1000, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 8448, FAKE, 16, FAKE, 1000, 2048,
+               ctypes.c_void_p(0x10000), cand_need, None]
     bad = dict(enumerate(ok_args))
     cases = [({0: 0}, 1, "num_seqs"), ({1: 1}, 1, "n_q"), ({2: 0}, 1, "max_seq_len"),
              ({3: 0}, 1, "max_q_per_seq"), ({4: None}, 1, "cu_q"), ({8: None}, 1, "key_pages"),
              ({9: 8447}, 1, "key_page_stride"), ({9: 8456}, 1, "key_page_stride"),
              ({11: 15}, 1, "bt_stride"), ({13: 999}, 1, "score_stride"),
-             ({6: FAKE_ODD}, 1, "aligned")]
+             ({6: FAKE_ODD}, 1, "aligned"), ({14: 0}, 2, "cand_k"), ({14: 4097}, 2, "cand_k"),
+             ({16: cand_need - 1}, 3, "workspace"),
+             ({15: ctypes.c_void_p(0x10010)}, 1, "aligned")]
     for patch, status, word in cases:
         args = list(ok_args)
         for i, v in patch.items():
@@ -66,15 +71,18 @@ def test_index_score_rejects_bad_host_args(L):
 
 def test_topk_rejects_bad_host_args(L):
     f = L.dsa_topk
-    need = L.dsa_topk_workspace_size(3, 1000, 2048)
-    assert need > 0
-    base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE, ctypes.c_void_p(0x10000), need, None]
-    for patch, status in [({7: 0}, 2), ({7: 4097}, 2), ({8: None}, 1), ({6: 10}, 1),
-                          ({13: need - 1}, 3), ({12: None}, 3), ({12: ctypes.c_void_p(0x10010)}, 1)]:
-        args = list(base)
-        for i, v in patch.items():
-            args[i] = v
-        assert f(*args) == status, (patch, _err())
+    for fused in (0, 1):
+        need = L.dsa_topk_workspace_size(3, 1000, 2048)
+        assert need > 0
+        base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE,
+                ctypes.c_void_p(0x10000), need, fused, None]
+        for patch, status in [({7: 0}, 2), ({7: 4097}, 2), ({8: None}, 1), ({6: 10}, 1),
+                              ({13: need - 1}, 3), ({12: None}, 3),
+                              ({12: ctypes.c_void_p(0x10010)}, 1)]:
+            args = list(base)
+            for i, v in patch.items():
+                args[i] = v
+            assert f(*args) == status, (fused, patch, _err())
     assert L.dsa_topk_workspace_size(0, 10, 10) == 0
     assert L.dsa_topk_workspace_size(4, 10, 5000) == 0
 

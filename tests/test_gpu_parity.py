@@ -1,6 +1,6 @@
 """GPU parity: every stage of the HIP path against the CPU oracle on the same seeded inputs.
 
-Small ragged batches span several tiles and chunk tails; the named workloads run at full
+Small ragged batches span several tiles and group tails; the named workloads run at full
 size with sampled rows.  Top-k is compared bit for bit on identical fp32 scores (scores the
 oracle computed, uploaded to both sides); the indexer within 1e-3 relative; attention
 outputs within 2e-2 abs + 1e-2 rel and the LSE within 1e-4.
@@ -49,7 +49,8 @@ def run_topk(batch, scores, k, with_slots=True):
     wl = batch.wl
     idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
     slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV) if with_slots else None
-    ws = torch.empty(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k), dtype=torch.uint8,
+                     device=DEV)
     dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table if with_slots else None,
                  idx, slot, ws, max_seq_len=wl.max_seq_len)
     torch.cuda.synchronize()
@@ -178,14 +179,29 @@ def test_topk_bit_exact_on_identical_scores(lens, q_per, k, kind):
         assert (slot[row, n:] == -1).all()
 
 
-def test_topk_all_winners_in_one_chunk_forces_exact_reselect():
-    # every one of the top 2048 sits in chunk 3 of 16: that chunk can only send ~192
-    # candidates, so the exactness check must trigger the full re-selection
+def test_topk_winners_in_few_groups_are_resent_in_full():
+    # the top 2,048 sit in ~10 consecutive 256-token groups, each of which may send only 16
+    # candidates: the exactness check flags them and they are re-read in full
     L = 131072
     wl = synth.custom([L], [1], topk=2048, seed=31)
     batch = synth.make_batch(wl, DEV)
     sc = torch.randn((1, L), generator=torch.Generator().manual_seed(3))
     sc[0, 3 * 8192: 3 * 8192 + 2500] += 100.0
+    idx, _ = run_topk(batch, sc.to(DEV), 2048)
+    ref = np.sort(O.topk_indices(sc[0].numpy(), 2048))
+    assert np.array_equal(idx[0].cpu().numpy(), ref)
+
+
+def test_topk_too_many_flagged_groups_falls_back_to_all_scores():
+    # 40 boosted tokens in each of 128 groups: the groups hold 2,048 winners between them,
+    # ~16 each, and send their best 16; all but one are flagged, and re-reading them would
+    # not fit on chip: the row is filtered by the candidates' k-th key and re-selected
+    L = 131072
+    wl = synth.custom([L], [1], topk=2048, seed=33)
+    batch = synth.make_batch(wl, DEV)
+    sc = torch.randn((1, L), generator=torch.Generator().manual_seed(4))
+    for g in range(0, 512, 4):
+        sc[0, g * 256: g * 256 + 40] += 100.0
     idx, _ = run_topk(batch, sc.to(DEV), 2048)
     ref = np.sort(O.topk_indices(sc[0].numpy(), 2048))
     assert np.array_equal(idx[0].cpu().numpy(), ref)
@@ -375,3 +391,68 @@ def test_batch_composition_does_not_change_a_row():
                          big.softmax_scale, 5)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+# ------------------------------------------------------------------------ fused stages 1 + 2
+FUSED = SMALL + [
+    synth.custom([20000, 9000, 2049], [5, 1, 3], topk=2048, seed=61, name="fused-spec"),
+    synth.custom([131072], [1], topk=2048, seed=62, name="fused-128k"),
+    synth.custom([3000], [1], topk=4096, seed=63, name="fused-k-above-context"),
+]
+
+
+def _stage_by_stage(batch, k):
+    wl = batch.wl
+    scores = run_scores(batch)
+    idx, slot = run_topk(batch, scores, k)
+    return scores, idx, slot
+
+
+def _fused(batch, k):
+    wl = batch.wl
+    scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    ws = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k))
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, scores, max_seq_len=wl.max_seq_len,
+                        max_q_per_seq=max(wl.q_per_seq), cand_k=k, cand_workspace=ws)
+    dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, idx, slot, ws,
+                 max_seq_len=wl.max_seq_len, from_candidates=True)
+    torch.cuda.synchronize()
+    return scores, idx, slot
+
+
+@pytest.mark.parametrize("wl", FUSED, ids=lambda w: w.name)
+def test_fused_index_topk_is_bitwise_the_stage_by_stage_path(wl):
+    say("fused", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    s1, i1, t1 = _stage_by_stage(batch, wl.topk)
+    s2, i2, t2 = _fused(batch, wl.topk)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        assert torch.equal(s1[row, : pos + 1], s2[row, : pos + 1]), row
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+
+
+def test_fused_topk_resends_groups_that_hold_the_winners():
+    wl = synth.custom([40000], [2], topk=2048, seed=64, name="fused-skew")
+    batch = synth.make_batch(wl, DEV)
+    # multiply the key scales of tokens 5,120 .. 6,143 (four 256-token groups) by 1000: the
+    # groups then hold ~500 of the best scores but may send only 56 candidates each
+    bt = batch.block_table.cpu().numpy()
+    for page in range(80, 96):
+        phys = int(bt[0, page])
+        sc = batch.key_pool[phys, 8192:].view(torch.float32)
+        sc.mul_(1000.0)
+    torch.cuda.synchronize()
+    s1, i1, t1 = _stage_by_stage(batch, 2048)
+    s2, i2, t2 = _fused(batch, 2048)
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+    h = host(batch)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref, mag = oracle_scores(batch, row, keys=request_keys(batch, b, h["key_pool"], h["bt"]))
+        got = s2[row, : pos + 1].cpu().numpy()
+        check_scores(got, ref, mag, f"skew row {row}")
+        assert topk_is_valid_for(got, i2[row].cpu().numpy(), 2048)
+        in_groups = ((i2[row] >= 5120) & (i2[row] < 6144)).sum().item()
+        assert in_groups > 200, in_groups
