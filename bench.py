@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="run stage 2 as both top-k passes instead of taking the indexer's "
                          "per-chunk candidates")
+    ap.add_argument("--query-side-stream", action="store_true",
+                    help="quantise the MLA query on a side stream during stages 1-2 instead of "
+                         "inside the attention kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -193,7 +196,8 @@ def main():
     S = args.splits or wl.num_splits
     torch.cuda.set_device(0)
     batch = synth.make_batch(wl, "cuda")
-    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused)
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
+                          query_on_side_stream=args.query_side_stream)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
     flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -206,31 +210,27 @@ def main():
                                     8192, stream.cuda_stream)
 
     def one_step(evs=None):
+        # stage 3's query quantisation runs on a side stream while stages 1 and 2 run; the
+        # step starts at evs[0] on the main stream, which the side stream waits for
         if evs:
             evs[0].record(stream)
+        if step.query_on_side_stream:
+            step._ev_start.record(stream)
+            step.side.wait_event(step._ev_start)
+            step.prepare_query(batch.q_mla, stream=step.side)
+            step._ev_query.record(step.side)
         step.index(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
-                   batch.block_table, max(wl.q_per_seq))
+                   batch.block_table, max(wl.q_per_seq), stream)
         if evs:
             evs[1].record(stream)
-        step.select(batch.cu_q, batch.seq_lens, batch.block_table)
+        step.select(batch.cu_q, batch.seq_lens, batch.block_table, stream)
         if evs:
             evs[2].record(stream)
-        if S == 1:
-            dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale,
-                                      step.topk_slot, batch.softmax_scale, 1, out=step.out,
-                                      lse=step.lse, workspace=step.mla_workspace)
-            if evs:
-                evs[3].record(stream)
-                evs[4].record(stream)
-        else:
-            dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale,
-                                      step.topk_slot, batch.softmax_scale, S, o_part=step.o_part,
-                                      lse_part=step.lse_part, workspace=step.mla_workspace)
-            if evs:
-                evs[3].record(stream)
-            dsa.dsa_lse_combine(step.o_part, step.lse_part, step.out, step.lse)
-            if evs:
-                evs[4].record(stream)
+        if step.query_on_side_stream:
+            stream.wait_event(step._ev_query)
+        step.attend(batch.q_mla, batch.latent_pool, batch.latent_scale, batch.softmax_scale, stream)
+        if evs:
+            evs[3].record(stream)
 
     for _ in range(args.warmup):
         if not args.no_flush:
@@ -239,19 +239,19 @@ def main():
     torch.cuda.synchronize()
 
     per_step = []
-    stage = [[], [], [], []]
+    stage = [[], [], []]
     t_wall0 = time.perf_counter()
     torch.cuda.synchronize()
     for _ in range(args.steps):
         if not args.no_flush:
             flush()                     # outside the events
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         one_step(evs)
         per_step.append(evs)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     for evs in per_step:
-        for i in range(4):
+        for i in range(3):
             stage[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
     step_us = [sum(s[i] for s in stage) for i in range(args.steps)]
     step_us_sorted = sorted(step_us)
@@ -301,7 +301,7 @@ def main():
         "us_per_layer_median": round(med, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "stage_us": {"index_score": round(stage_mean[0], 2), "topk": round(stage_mean[1], 2),
-                     "sparse_mla": round(stage_mean[2], 2), "lse_combine": round(stage_mean[3], 2)},
+                     "sparse_mla_and_merge": round(stage_mean[2], 2)},
         "algorithmic_bytes": ab,
         "dsa_vs_dense_mla_bytes": round(ab["total"] / dense_mla_bytes(wl.seq_lens, wl.q_per_seq), 4),
         "roofline": {"kernel": "dsa_index_score", "bound": "hbm", "achieved": round(idx_gbps, 1),

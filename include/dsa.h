@@ -146,25 +146,32 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
  * The query is E4M3-quantised per (row, head) as dsa_quantize_q does.  Both
  * contractions run on FP8 MFMA; the probabilities enter the value product as E4M3.
  *
- *   q_bf16 [n_q][96][576] bf16.  topk_slot int32 [n_q][k]; -1 entries are skipped.
- *   num_splits S in 1..64, S <= k: split s of a row covers entries
- *   [s*k/S, (s+1)*k/S) of its slot list.
- *   S == 1: out_bf16 [n_q][96][512] bf16 and lse [n_q][96] fp32 are written
- *           (o_part / lse_part unused, may be NULL).
- *   S > 1:  o_part fp32 [S][n_q][96][512] (each split normalised by its own sum) and
- *           lse_part fp32 [S][n_q][96] are written (out_bf16 / lse unused); an empty
- *           split has O = 0 and LSE = -inf.  Merge them with dsa_lse_combine.
- *   workspace: device memory of at least dsa_sparse_mla_workspace_size(n_q) bytes,
- *   256-byte aligned, scratch for the call (it receives the FP8 query codes and scales
- *   that every split of a row shares, so the query is quantised once per row).
+ *   Query: q8 (uint8 E4M3 codes [n_q][96][576]) and q_scale (fp32 [n_q][96]) as
+ *   dsa_quantize_q(n_q, 96, 576, ...) writes them, when both are given (the caller can
+ *   prepare them on another stream while stages 1 and 2 run); otherwise q_bf16
+ *   [n_q][96][576] bf16, quantised inside the call.
+ *   topk_slot int32 [n_q][k]; -1 entries are skipped.
+ *   num_splits S in 1..64, S <= k: split s of a row covers entries [s*k/S, (s+1)*k/S)
+ *   of its slot list (splits add workgroups for small batches).
+ *   Outputs, one of:
+ *   - o_part and lse_part given: o_part fp32 [S][n_q][96][512] (each split normalised by
+ *     its own sum) and lse_part fp32 [S][n_q][96] are written; an empty split has O = 0
+ *     and LSE = -inf.  Merge them with dsa_lse_combine.  out_bf16 / lse are unused.
+ *   - otherwise out_bf16 [n_q][96][512] bf16 and lse [n_q][96] fp32 are written.  With
+ *     S > 1 the splits pass through the workspace as fp16 partials (O_s / latent_scale,
+ *     bounded by 448) and are merged by log-sum-exp inside the call (stage 4).
+ *   workspace: with S > 1 and no o_part, device memory of at least
+ *   dsa_sparse_mla_workspace_size(n_q, S) bytes, 256-byte aligned, scratch for the call;
+ *   unused (may be NULL) otherwise.
  */
-size_t dsa_sparse_mla_workspace_size(int32_t n_q);
-dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* latent_pages,
+size_t dsa_sparse_mla_workspace_size(int32_t n_q, int32_t num_splits);
+dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8,
+                                 const float* q_scale, const void* latent_pages,
                                  int64_t latent_page_stride, float latent_scale,
                                  const int32_t* topk_slot, int32_t k, float softmax_scale,
-                                 int32_t num_splits, float* o_part, float* lse_part,
-                                 void* out_bf16, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 int32_t num_splits, void* out_bf16, float* lse, float* o_part,
+                                 float* lse_part, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Stage 4 — log-sum-exp merge of split partials:

@@ -52,10 +52,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
                                _I32, _P]
-        L.dsa_sparse_mla_workspace_size.argtypes = [_I32]
+        L.dsa_sparse_mla_workspace_size.argtypes = [_I32, _I32]
         L.dsa_sparse_mla_workspace_size.restype = _SZ
-        L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _I64, _F32, _P, _I32, _F32, _I32, _P, _P,
-                                            _P, _P, _P, _SZ, _P]
+        L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _P, _P, _I64, _F32, _P, _I32, _F32, _I32,
+                                            _P, _P, _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -161,8 +161,8 @@ def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k
                           int(bool(from_candidates)), _stream(stream)))
 
 
-def dsa_sparse_mla_workspace_size(n_q: int) -> int:
-    return int(lib().dsa_sparse_mla_workspace_size(int(n_q)))
+def dsa_sparse_mla_workspace_size(n_q: int, num_splits: int) -> int:
+    return int(lib().dsa_sparse_mla_workspace_size(int(n_q), int(num_splits)))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -173,34 +173,45 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return t
 
 
-def dsa_sparse_mla_decode(q_mla: torch.Tensor, latent_pages: torch.Tensor, latent_scale: float,
-                          topk_slot: torch.Tensor, softmax_scale: float, num_splits: int, *,
+def dsa_sparse_mla_decode(q_mla: Optional[torch.Tensor], latent_pages: torch.Tensor,
+                          latent_scale: float, topk_slot: torch.Tensor, softmax_scale: float,
+                          num_splits: int, *, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None,
                           o_part: Optional[torch.Tensor] = None,
                           lse_part: Optional[torch.Tensor] = None,
-                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          q8: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None,
                           latent_page_stride: Optional[int] = None, stream=None) -> None:
-    """MLA over the selected slots: (out, lse) when num_splits == 1, else (o_part, lse_part)."""
-    n_q = q_mla.shape[0]
-    _expect(q_mla, "q_mla", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
-    _expect(topk_slot, "topk_slot", torch.int32)
-    k = topk_slot.shape[1]
-    if num_splits == 1:
-        _expect(out, "out", torch.bfloat16, (n_q, MLA_HEADS, V_DIM))
-        _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
+    """MLA over the selected slots.  Query: q8/q_scale (from dsa_quantize_q) if given, else
+    q_mla (bf16).  Output: fp32 split partials (o_part, lse_part) if given, else (out, lse),
+    merged inside the call when num_splits > 1."""
+    n_q, k = topk_slot.shape
+    _expect(topk_slot, "topk_slot", torch.int32, (n_q, k))
+    if q8 is not None:
+        _expect(q8, "q8", torch.uint8, (n_q, MLA_HEADS, LATENT_DIM))
+        _expect(q_scale, "q_scale", torch.float32, (n_q, MLA_HEADS))
     else:
+        _expect(q_mla, "q_mla", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+    if o_part is not None:
         _expect(o_part, "o_part", torch.float32, (num_splits, n_q, MLA_HEADS, V_DIM))
         _expect(lse_part, "lse_part", torch.float32, (num_splits, n_q, MLA_HEADS))
+    else:
+        _expect(out, "out", torch.bfloat16, (n_q, MLA_HEADS, V_DIM))
+        _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
+        if num_splits > 1 and workspace is None:
+            workspace = globals()["workspace"](dsa_sparse_mla_workspace_size(n_q, num_splits),
+                                               topk_slot.device)
+    if workspace is not None:
+        _expect(workspace, "workspace", torch.uint8)
     stride = (latent_page_stride if latent_page_stride is not None
               else latent_pages.stride(0) * latent_pages.element_size())
-    if workspace is None:
-        workspace = globals()["workspace"](dsa_sparse_mla_workspace_size(n_q), q_mla.device)
-    _expect(workspace, "workspace", torch.uint8)
-    _check(lib().dsa_sparse_mla_decode(n_q, _ptr(q_mla), _ptr(latent_pages), int(stride),
-                                       float(latent_scale), _ptr(topk_slot), int(k),
-                                       float(softmax_scale), int(num_splits), _ptr(o_part),
-                                       _ptr(lse_part), _ptr(out), _ptr(lse), _ptr(workspace),
-                                       workspace.numel(), _stream(stream)))
+    _check(lib().dsa_sparse_mla_decode(n_q, _ptr(q_mla), _ptr(q8), _ptr(q_scale),
+                                       _ptr(latent_pages), int(stride), float(latent_scale),
+                                       _ptr(topk_slot), int(k), float(softmax_scale),
+                                       int(num_splits), _ptr(out), _ptr(lse), _ptr(o_part),
+                                       _ptr(lse_part), _ptr(workspace),
+                                       workspace.numel() if workspace is not None else 0,
+                                       _stream(stream)))
 
 
 def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
@@ -218,27 +229,29 @@ def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Ten
 class DecodeStep:
     """Device buffers for one pass of the whole path over a fixed batch shape.
 
-    Allocates (through torch) the scores, top-k outputs, workspace and partials once;
-    run() then issues the four library calls on the current stream.
+    Allocates (through torch) the scores, top-k outputs, workspaces and the prepared MLA
+    query once; run() issues the library calls on the current stream, with the MLA query
+    quantised on a side stream while stages 1 and 2 run.
     """
 
     def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
-                 fused: bool = True):
+                 fused: bool = True, query_on_side_stream: bool = False):
         self.n_q, self.max_seq_len, self.k, self.num_splits = n_q, max_seq_len, k, num_splits
         self.fused = fused
+        self.query_on_side_stream = query_on_side_stream
         dev = torch.device(device)
         self.scores = torch.empty((n_q, max_seq_len), dtype=torch.float32, device=dev)
         self.topk_idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
         self.topk_slot = torch.empty((n_q, k), dtype=torch.int32, device=dev)
         self.workspace = workspace(dsa_topk_workspace_size(n_q, max_seq_len, k), dev)
-        self.mla_workspace = workspace(dsa_sparse_mla_workspace_size(n_q), dev)
+        self.mla_workspace = workspace(dsa_sparse_mla_workspace_size(n_q, num_splits), dev)
+        self.q8 = torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.uint8, device=dev)
+        self.q_scale = torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)
         self.out = torch.empty((n_q, MLA_HEADS, V_DIM), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)
-        if num_splits > 1:
-            self.o_part = torch.empty((num_splits, n_q, MLA_HEADS, V_DIM), dtype=torch.float32, device=dev)
-            self.lse_part = torch.empty((num_splits, n_q, MLA_HEADS), dtype=torch.float32, device=dev)
-        else:
-            self.o_part = self.lse_part = None
+        self.side = torch.cuda.Stream(device=dev)  # default priority
+        self._ev_start = torch.cuda.Event()
+        self._ev_query = torch.cuda.Event()
 
     def index(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq,
               stream=None):
@@ -254,21 +267,34 @@ class DecodeStep:
                  self.workspace, max_seq_len=self.max_seq_len, from_candidates=self.fused,
                  stream=stream)
 
+    def prepare_query(self, q_mla, stream=None):
+        """E4M3 codes and scales of the MLA query (stage 3's own quantisation)."""
+        dsa_quantize_q(q_mla, self.q8, self.q_scale, stream=stream)
+
     def attend(self, q_mla, latent_pages, latent_scale, softmax_scale, stream=None):
-        """Stages 3 and 4."""
-        if self.num_splits == 1:
-            dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
-                                  1, out=self.out, lse=self.lse, workspace=self.mla_workspace,
+        """Stages 3 and 4: on the query prepared by prepare_query when the step quantises it
+        on the side stream, else on q_mla (quantised inside the call)."""
+        if self.query_on_side_stream:
+            dsa_sparse_mla_decode(None, latent_pages, latent_scale, self.topk_slot, softmax_scale,
+                                  self.num_splits, out=self.out, lse=self.lse, q8=self.q8,
+                                  q_scale=self.q_scale, workspace=self.mla_workspace,
                                   stream=stream)
         else:
-            dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot, softmax_scale,
-                                  self.num_splits, o_part=self.o_part, lse_part=self.lse_part,
+            dsa_sparse_mla_decode(q_mla, latent_pages, latent_scale, self.topk_slot,
+                                  softmax_scale, self.num_splits, out=self.out, lse=self.lse,
                                   workspace=self.mla_workspace, stream=stream)
-            dsa_lse_combine(self.o_part, self.lse_part, self.out, self.lse, stream=stream)
         return self.out, self.lse
 
     def run(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, q_mla, latent_pages,
             latent_scale, softmax_scale, max_q_per_seq, stream=None):
-        self.index(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq, stream)
-        self.select(cu_q, seq_lens, block_table, stream)
-        return self.attend(q_mla, latent_pages, latent_scale, softmax_scale, stream)
+        main = torch.cuda.current_stream() if stream is None else stream
+        if self.query_on_side_stream:
+            self._ev_start.record(main)
+            self.side.wait_event(self._ev_start)
+            self.prepare_query(q_mla, stream=self.side)
+            self._ev_query.record(self.side)
+        self.index(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq, main)
+        self.select(cu_q, seq_lens, block_table, main)
+        if self.query_on_side_stream:
+            main.wait_event(self._ev_query)
+        return self.attend(q_mla, latent_pages, latent_scale, softmax_scale, main)

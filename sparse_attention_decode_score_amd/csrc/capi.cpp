@@ -66,6 +66,7 @@ dsa_status dsa_quantize_q(int32_t rows, int32_t heads, int32_t dim, const void* 
   if (dim != DSA_IDX_DIM && dim != DSA_LATENT_DIM)
     return fail(DSA_ERR_UNSUPPORTED, "dim must be 128 or 576 (got %d)", dim);
   DSA_REQUIRE(q_bf16 && codes && scales, "q_bf16, codes and scales must be non-null");
+  DSA_REQUIRE(aligned(q_bf16, 16) && aligned(codes, 16), "q_bf16 and codes must be 16-byte aligned");
   return launched(dsa::launch_quantize_q(rows, heads, dim, static_cast<const uint16_t*>(q_bf16),
                                          codes, scales, static_cast<hipStream_t>(stream)),
                   "dsa_quantize_q");
@@ -148,42 +149,52 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
                   "dsa_topk");
 }
 
-size_t dsa_sparse_mla_workspace_size(int32_t n_q) {
-  if (n_q < 1) return 0;
-  return dsa::sparse_mla_workspace_bytes(n_q);
+size_t dsa_sparse_mla_workspace_size(int32_t n_q, int32_t num_splits) {
+  if (n_q < 1 || num_splits < 1 || num_splits > DSA_MAX_SPLITS) return 0;
+  return dsa::sparse_mla_workspace_bytes(n_q, num_splits);
 }
 
-dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* latent_pages,
+dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8,
+                                 const float* q_scale, const void* latent_pages,
                                  int64_t latent_page_stride, float latent_scale,
                                  const int32_t* topk_slot, int32_t k, float softmax_scale,
-                                 int32_t num_splits, float* o_part, float* lse_part,
-                                 void* out_bf16, float* lse, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 int32_t num_splits, void* out_bf16, float* lse, float* o_part,
+                                 float* lse_part, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
   if (num_splits < 1 || num_splits > DSA_MAX_SPLITS)
     return fail(DSA_ERR_UNSUPPORTED, "num_splits must be in 1..64 (got %d)", num_splits);
   DSA_REQUIRE(num_splits <= k, "num_splits (%d) must be <= k (%d)", num_splits, k);
-  DSA_REQUIRE(q_bf16 && latent_pages && topk_slot, "q_bf16, latent_pages and topk_slot must be non-null");
-  DSA_REQUIRE(aligned(q_bf16, 16) && aligned(latent_pages, 16),
-              "q_bf16 and latent_pages must be 16-byte aligned");
+  const bool prepared = q8 != nullptr && q_scale != nullptr;
+  DSA_REQUIRE((q8 == nullptr) == (q_scale == nullptr), "q8 and q_scale must both be given or both be NULL");
+  DSA_REQUIRE(prepared || q_bf16, "the query is missing: give q_bf16 or q8 and q_scale");
+  DSA_REQUIRE(latent_pages && topk_slot, "latent_pages and topk_slot must be non-null");
+  DSA_REQUIRE(prepared ? aligned(q8, 16) : aligned(q_bf16, 16), "the query must be 16-byte aligned");
+  DSA_REQUIRE(aligned(latent_pages, 16), "latent_pages must be 16-byte aligned");
   DSA_REQUIRE(latent_page_stride >= DSA_LATENT_PAGE_BYTES && latent_page_stride % 16 == 0,
               "latent_page_stride must be >= 36864 and a multiple of 16 (got %lld)",
               (long long)latent_page_stride);
   DSA_REQUIRE(latent_scale > 0.f, "latent_scale must be > 0");
   DSA_REQUIRE(softmax_scale > 0.f, "softmax_scale must be > 0");
-  if (num_splits == 1) {
-    DSA_REQUIRE(out_bf16 && lse, "num_splits == 1 needs out_bf16 and lse");
-  } else {
-    DSA_REQUIRE(o_part && lse_part, "num_splits > 1 needs o_part and lse_part");
+  DSA_REQUIRE((o_part == nullptr) == (lse_part == nullptr),
+              "o_part and lse_part must both be given or both be NULL");
+  if (o_part) {
     DSA_REQUIRE(aligned(o_part, 16), "o_part must be 16-byte aligned");
+  } else {
+    DSA_REQUIRE(out_bf16 && lse, "out_bf16 and lse are needed when o_part is NULL");
+    DSA_REQUIRE(aligned(out_bf16, 16), "out_bf16 must be 16-byte aligned");
+    if (num_splits > 1) {
+      const size_t need = dsa::sparse_mla_workspace_bytes(n_q, num_splits);
+      if (workspace == nullptr || workspace_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                    workspace ? workspace_bytes : (size_t)0, need);
+      DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+    }
   }
-  const size_t need = dsa::sparse_mla_workspace_bytes(n_q);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                workspace ? workspace_bytes : (size_t)0, need);
-  DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
   return launched(dsa::launch_sparse_mla(n_q, static_cast<const uint16_t*>(q_bf16),
+                                         prepared ? static_cast<const uint8_t*>(q8) : nullptr,
+                                         prepared ? q_scale : nullptr,
                                          static_cast<const uint8_t*>(latent_pages),
                                          latent_page_stride, latent_scale, topk_slot, k,
                                          softmax_scale, num_splits, o_part, lse_part,

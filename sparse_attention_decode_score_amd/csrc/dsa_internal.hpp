@@ -45,14 +45,21 @@ hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu
                        const int32_t* block_table, int bt_stride, int32_t* topk_idx,
                        int32_t* topk_slot, void* workspace, hipStream_t st);
 
-size_t sparse_mla_workspace_bytes(int n_q);
-hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* latent_pages,
-                             int64_t latent_page_stride, float latent_scale,
-                             const int32_t* topk_slot, int k, float softmax_scale, int num_splits,
-                             float* o_part, float* lse_part, uint16_t* out_bf16, float* lse,
-                             void* workspace, hipStream_t st);
+// workspace: fp16 split partials (num_splits > 1 and no o_part)
+size_t sparse_mla_workspace_bytes(int n_q, int num_splits);
+// q8 / q_scale: the prepared query (both non-null) or nullptr to quantise q in the kernel.
+// o_part != nullptr: fp32 partials of every split; else out/lse, merged through the
+// workspace when num_splits > 1.
+hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, const float* q_scale,
+                             const uint8_t* latent_pages, int64_t latent_page_stride,
+                             float latent_scale, const int32_t* topk_slot, int k,
+                             float softmax_scale, int num_splits, float* o_part, float* lse_part,
+                             uint16_t* out_bf16, float* lse, void* workspace, hipStream_t st);
 
 hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
                               uint16_t* out_bf16, float* lse, hipStream_t st);
+hipError_t launch_lse_combine_f16(int num_splits, int n_q, const uint16_t* o_part,
+                                  const float* lse_part, float scale, uint16_t* out_bf16,
+                                  float* lse, hipStream_t st);
 
 }  // namespace dsa

@@ -301,20 +301,46 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   }
 }
 
+// Per-(row, head) query quantisation: 8 lanes per head, each converting dim/8 consecutive
+// values (16-byte loads), the head's absmax reduced across its 8 lanes.  One 64-lane
+// workgroup covers 8 heads.
+template <int PPL>  // 16-byte pieces per lane = dim / 64
 __global__ __launch_bounds__(64) void quantize_q_kernel(const uint16_t* __restrict__ q,
                                                         uint8_t* __restrict__ codes,
-                                                        float* __restrict__ scales, int dim) {
-  const int64_t rh = blockIdx.x;  // (row, head)
+                                                        float* __restrict__ scales,
+                                                        int64_t rows_heads) {
+  constexpr int dim = PPL * 64;
   const int lane = threadIdx.x;
-  const uint16_t* src = q + rh * dim;
+  const int64_t rh = (int64_t)blockIdx.x * 8 + (lane >> 3);
+  const bool live = rh < rows_heads;
+  const int64_t base = (live ? rh : 0) * dim + (lane & 7) * (PPL * 8);
+  v4i raw[PPL];
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) raw[i] = *reinterpret_cast<const v4i*>(q + base + 8 * i);
   float am = 0.f;
-  for (int d = lane; d < dim; d += 64) am = fmaxf(am, fabsf(__uint_as_float((uint32_t)src[d] << 16)));
-  am = wave_max(am);
+#pragma unroll
+  for (int i = 0; i < PPL; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      am = fmaxf(am, fmaxf(fabsf(bf16_lo((uint32_t)raw[i][j])), fabsf(bf16_hi((uint32_t)raw[i][j]))));
+  am = fmaxf(am, __shfl_xor(am, 1, 64));
+  am = fmaxf(am, __shfl_xor(am, 2, 64));
+  am = fmaxf(am, __shfl_xor(am, 4, 64));
   const int e = pow2_scale_exp(am);
   const float inv = ldexpf(1.0f, -e);
-  for (int d = lane; d < dim; d += 64)
-    codes[rh * dim + d] = (uint8_t)cvt2_e4m3(__uint_as_float((uint32_t)src[d] << 16) * inv, 0.f);
-  if (lane == 0) scales[rh] = ldexpf(1.0f, e);
+  if (!live) return;
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) {
+    v2i c;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w0 = (uint32_t)raw[i][2 * j], w1 = (uint32_t)raw[i][2 * j + 1];
+      c[j] = (int)cvt4_e4m3(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
+                            bf16_hi(w1) * inv);
+    }
+    *reinterpret_cast<v2i*>(codes + base + 8 * i) = c;
+  }
+  if ((lane & 7) == 0) scales[rh] = ldexpf(1.0f, e);
 }
 
 }  // namespace
@@ -323,7 +349,13 @@ hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, ui
                              float* scales, hipStream_t st) {
   const int64_t n = (int64_t)rows * heads;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)n), dim3(64), 0, st, q, codes, scales, dim);
+  const dim3 grid((unsigned)((n + 7) / 8));
+  if (dim == kIdxDim)
+    hipLaunchKernelGGL(quantize_q_kernel<kIdxDim / 64>, grid, dim3(64), 0, st, q, codes, scales, n);
+  else if (dim == kLatDim)
+    hipLaunchKernelGGL(quantize_q_kernel<kLatDim / 64>, grid, dim3(64), 0, st, q, codes, scales, n);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

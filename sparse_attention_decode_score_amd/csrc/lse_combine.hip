@@ -45,6 +45,42 @@ __global__ __launch_bounds__(128) void lse_combine_kernel(const float* __restric
   if (t == 0) lse_out[rh] = (m == -INFINITY) ? -INFINITY : m + logf(tot);
 }
 
+// The same merge over fp16 partials that hold O_s / latent_scale; the result is scaled back.
+__global__ __launch_bounds__(128) void lse_combine_f16_kernel(const uint16_t* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part,
+                                                              int num_splits, int64_t rows_heads,
+                                                              float scale,
+                                                              uint16_t* __restrict__ out,
+                                                              float* __restrict__ lse_out) {
+  const int64_t rh = blockIdx.x;
+  const int t = threadIdx.x;
+  float m = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) m = fmaxf(m, lse_part[s * rows_heads + rh]);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < num_splits; ++s) {
+      const float l = lse_part[s * rows_heads + rh];
+      const float w = l == -INFINITY ? 0.f : expf(l - m);
+      tot += w;
+      const v2i raw = *reinterpret_cast<const v2i*>(o_part + (s * rows_heads + rh) * kVDim + 4 * t);
+      const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
+      acc += w * v4f{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    }
+  }
+  const float inv = tot > 0.f ? scale / tot : 0.f;
+  uint32_t u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t b = __float_as_uint(acc[j] * inv);  // round to nearest even bf16
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    u[j] = b >> 16;
+  }
+  v2i packed = {(int)(u[0] | (u[1] << 16)), (int)(u[2] | (u[3] << 16))};
+  *reinterpret_cast<v2i*>(out + rh * kVDim + 4 * t) = packed;
+  if (t == 0) lse_out[rh] = (m == -INFINITY) ? -INFINITY : m + logf(tot);
+}
+
 }  // namespace
 
 hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
@@ -53,6 +89,16 @@ hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, cons
   if (rh == 0) return hipSuccess;
   hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)rh), dim3(128), 0, st, o_part, lse_part,
                      num_splits, rh, out_bf16, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_combine_f16(int num_splits, int n_q, const uint16_t* o_part,
+                                  const float* lse_part, float scale, uint16_t* out_bf16,
+                                  float* lse, hipStream_t st) {
+  const int64_t rh = (int64_t)n_q * kMlaHeads;
+  if (rh == 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_combine_f16_kernel, dim3((unsigned)rh), dim3(128), 0, st, o_part,
+                     lse_part, num_splits, rh, scale, out_bf16, lse);
   return hipGetLastError();
 }
 

@@ -9,9 +9,13 @@
 // here that is the split index s of a (split, row) workgroup.
 //
 // Workgroup = 8 waves on one CU.  Waves 6, 7 gather 64-token latent tiles (slot -> page ->
-// 576 bytes, non-temporal loads) into a double-buffered LDS ring.  Waves 0..5 each own 32
-// heads x 256 value dims of the row.  The query is quantised once per row (E4M3 codes and
-// power-of-two scales in the workspace) and copied to LDS, where it is the B operand of
+// 576 bytes, non-temporal loads): they keep three tiles in flight in registers and write
+// each into a double-buffered LDS ring one tile ahead of the compute waves.  Every gather is
+// issued unconditionally (a slot of -1 or a token past the split reads a zero row), so the
+// compiler's wait counts stay exact and only the oldest tile is ever waited for.  Waves
+// 0..5 each own 32 heads x 256 value dims of the row.  They quantise the row's query to
+// E4M3 with one power-of-two scale per head (as dsa_quantize_q does) straight into LDS,
+// where it is the B operand of
 //   S[token][head] = L8[32 tokens x 576] * Q8^T          (9 x v_mfma 32x32x64 per 32 tokens)
 // The two waves of a head tile each form the logits of one 32-token half of a tile; the A
 // rows are permuted so that lane l holds head l%32's logits for tokens 32*(l/32) + 16*half
@@ -34,10 +38,15 @@ namespace {
 constexpr int kTile = 64;
 constexpr int kRowStride = 592;  // LDS bytes per latent / query row (576 + 16: conflict-free b128 reads)
 constexpr int kThreads = 512;    // 6 compute waves + 2 loader waves
+constexpr int kRing = 3;         // tiles the loader waves keep in flight in registers
+constexpr int kSlotsLds = 4096;  // slots of a split held in LDS (k <= 4096)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 4.0f;      // running-max slack in log2 units
 constexpr float kPScale = 16.0f;  // probabilities are converted to E4M3 as P * 2^4 <= 2^8
+
+// The latent row gathered for padding: a slot of -1 or a position past the split.
+__device__ __attribute__((aligned(64))) uint8_t g_zero_row[kLatDim];
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -45,17 +54,23 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Output of a workgroup: the row's bf16 O and LSE (one split), or its split's partial O
+// (fp32, or fp16 divided by the latent scale, which bounds it by 448) and LSE.
+enum PartMode { kDirect = 0, kPartF32 = 1, kPartF16 = 2 };
+
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
-    const uint8_t* __restrict__ q8, const float* __restrict__ qscale,
-    const uint8_t* __restrict__ lat_pages, int64_t page_stride, float lat_scale,
-    const int32_t* __restrict__ topk_slot, int k, float sm_scale, int num_splits, int n_q,
-    float* __restrict__ o_part, float* __restrict__ lse_part, uint16_t* __restrict__ out_bf16,
-    float* __restrict__ lse_out) {
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ q8_in,
+    const float* __restrict__ qs_in, const uint8_t* __restrict__ lat_pages, int64_t page_stride,
+    float lat_scale, const int32_t* __restrict__ topk_slot, int k, float sm_scale,
+    int num_splits, int n_q, int mode, void* __restrict__ o_part, float* __restrict__ lse_part,
+    uint16_t* __restrict__ out_bf16, float* __restrict__ lse_out) {
   __shared__ __attribute__((aligned(16))) uint8_t lat[2][kTile * kRowStride];
   __shared__ __attribute__((aligned(16))) uint8_t q8s[kMlaHeads * kRowStride];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[3][2][32][64];  // [head tile][hi/lo][head][token]
   __shared__ __attribute__((aligned(16))) float xmax[3][2][32];
   __shared__ __attribute__((aligned(16))) float xfer[6][32];
+  __shared__ __attribute__((aligned(16))) float qsc[kMlaHeads];
+  __shared__ int32_t slot_l[kSlotsLds];
   __shared__ uint64_t valid_mask[2];
 
   const int s = blockIdx.x, row = blockIdx.y;
@@ -68,53 +83,68 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int n = lane & 31, g = lane >> 5;
   const int32_t* slots = topk_slot + (int64_t)row * k + beg;
 
+  // the split's slot list -> LDS (barrier 0)
+  for (int i = threadIdx.x; i < n_tok; i += kThreads) slot_l[i] = slots[i];
+  __syncthreads();
+  auto slot_of = [&](int j) { return j < n_tok ? slot_l[j] : -1; };
+
   if (wave >= 6) {
     // ---------------------------------------------------------------- loader waves
     // wave 6 moves tile rows 0..31, wave 7 rows 32..63; lane l moves 16-byte pieces
     // (l%4) + 4c (c = 0..8) of rows 16*qq + l/4 of its half.
     const int half = wave - 6;
-    auto load_tile = [&](int t, int buf) {
-      const int t0 = t * kTile;
-      v4i data[2][9];
+    typedef v4i TileRegs[2][9];
+    auto issue = [&](int t, TileRegs& d) {
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
-        const int r = 32 * half + 16 * qq + (lane >> 2);
-        const int j = t0 + r;
-        const int slot = j < n_tok ? slots[j] : -1;
-        const uint8_t* src = lat_pages + (int64_t)(slot >> 6) * page_stride +
-                             (int64_t)(slot & (kPage - 1)) * kLatDim;
+        const int j = t * kTile + 32 * half + 16 * qq + (lane >> 2);
+        const int slot = slot_of(j);
+        const uint8_t* src = slot >= 0 ? lat_pages + (int64_t)(slot >> 6) * page_stride +
+                                             (int64_t)(slot & (kPage - 1)) * kLatDim
+                                       : g_zero_row;
 #pragma unroll
-        for (int c = 0; c < 9; ++c) {
-          const int piece = (lane & 3) + 4 * c;
-          data[qq][c] = slot >= 0
-                            ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + piece * 16))
-                            : v4i{0, 0, 0, 0};
-        }
+        for (int c = 0; c < 9; ++c)
+          d[qq][c] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4i*>(src + ((lane & 3) + 4 * c) * 16));
       }
+    };
+    auto store = [&](int t, const TileRegs& d, int buf) {
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const int r = 32 * half + 16 * qq + (lane >> 2);
 #pragma unroll
-        for (int c = 0; c < 9; ++c) {
-          const int piece = (lane & 3) + 4 * c;
-          *reinterpret_cast<v4i*>(&lat[buf][r * kRowStride + piece * 16]) = data[qq][c];
-        }
+        for (int c = 0; c < 9; ++c)
+          *reinterpret_cast<v4i*>(&lat[buf][r * kRowStride + ((lane & 3) + 4 * c) * 16]) = d[qq][c];
       }
       if (half == 0) {
-        const int jl = t0 + lane;
-        const uint64_t m = __ballot(jl < n_tok && slots[jl] >= 0);
+        const uint64_t m = __ballot(slot_of(t * kTile + lane) >= 0);
         if (lane == 0) valid_mask[buf] = m;
       }
     };
-    // every wave executes the same barriers: one before the loop, three per tile and the
-    // two of the compute waves' finalize step
-    if (n_tiles > 0) load_tile(0, 0);
-    __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-      if (t + 1 < n_tiles) load_tile(t + 1, (t + 1) & 1);
-      __syncthreads();
-      __syncthreads();
-      __syncthreads();
+    TileRegs ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i, ring[i]);
+    store(0, ring[0], 0);
+    issue(kRing, ring[0]);
+    __syncthreads();  // barrier 1: tile 0 and the query are in LDS
+    // every wave executes the same barriers: three per tile and the two of the compute
+    // waves' finalize step.  The loader's step for tile t writes tile t+1 (one LDS buffer
+    // ahead) and refills its registers with tile t+1+kRing; steps past the last tile only
+    // move zero rows and run after the compute waves are done with the LDS ring.
+#pragma unroll 1
+    for (int t0 = 0; t0 < n_tiles; t0 += kRing) {
+#pragma unroll
+      for (int u = 0; u < kRing; ++u) {
+        const int t = t0 + u;
+        const int set = (u + 1) % kRing;
+        store(t + 1, ring[set], (t + 1) & 1);
+        issue(t + 1 + kRing, ring[set]);
+        if (t < n_tiles) {
+          __syncthreads();
+          __syncthreads();
+          __syncthreads();
+        }
+      }
     }
     __syncthreads();
     __syncthreads();
@@ -122,18 +152,50 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   }
 
   // ------------------------------------------------------------------ compute waves
-  const int ht = wave >> 1;  // head tile: heads 32*ht .. +31
-  const int hf = wave & 1;   // token half of each tile for the logits, value-dim half for O
-  // FP8 query of the row -> LDS (rows padded to kRowStride), coalesced 16-byte pieces
-  {
-    const uint8_t* src = q8 + (int64_t)row * kMlaHeads * kLatDim;
+  if (q8_in) {
+    // codes and scales prepared by the query quantisation: coalesced copy to LDS
+    const uint8_t* src = q8_in + (int64_t)row * kMlaHeads * kLatDim;
     for (int i = threadIdx.x; i < kMlaHeads * (kLatDim / 16); i += 384) {
       const int h = i / (kLatDim / 16), pc = i % (kLatDim / 16);
       *reinterpret_cast<v4i*>(&q8s[h * kRowStride + pc * 16]) =
           *reinterpret_cast<const v4i*>(src + (int64_t)i * 16);
     }
+    if (threadIdx.x < kMlaHeads) qsc[threadIdx.x] = qs_in[(int64_t)row * kMlaHeads + threadIdx.x];
+  } else {
+    // query prep: 4 threads per head, 144 dims each -> E4M3 codes in LDS and the head's
+    // power-of-two scale (smallest 2^e with absmax <= 448 * 2^e)
+    const int h = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const uint16_t* src = q + ((int64_t)row * kMlaHeads + h) * kLatDim + part * 144;
+    v4i raw[18];
+#pragma unroll
+    for (int i = 0; i < 18; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 8 * i);
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 18; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        am = fmaxf(am, fmaxf(fabsf(bf16_lo((uint32_t)raw[i][j])), fabsf(bf16_hi((uint32_t)raw[i][j]))));
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    const int e = pow2_scale_exp(am);
+    const float inv = ldexpf(1.0f, -e);
+    uint8_t* dst = q8s + h * kRowStride + part * 144;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      v4i c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w0 = (uint32_t)raw[2 * i + j / 2][2 * (j % 2)];
+        const uint32_t w1 = (uint32_t)raw[2 * i + j / 2][2 * (j % 2) + 1];
+        c[j] = (int)cvt4_e4m3(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
+                              bf16_hi(w1) * inv);
+      }
+      *reinterpret_cast<v4i*>(dst + 16 * i) = c;
+    }
+    if (part == 0) qsc[h] = ldexpf(1.0f, e);
   }
-  const float mult = qscale[(int64_t)row * kMlaHeads + 32 * ht + n] * lat_scale * sm_scale * kLog2e;
+  const int ht = wave >> 1;  // head tile: heads 32*ht .. +31
+  const int hf = wave & 1;   // token half of each tile for the logits, value-dim half for O
   const uint8_t* qrow = q8s + (32 * ht + n) * kRowStride + 32 * g;
   v16f acc[8];  // O[32 heads][256 dims] of this wave; acc[dt] covers dims 256*hf + 32*dt .. +31
 #pragma unroll
@@ -141,7 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   float m_run = -INFINITY;  // running max (log2 units) of head n, identical in both waves
   float z_run = 0.f;        // this lane's share of the running sum of head n
   bool started = false;
-  __syncthreads();
+  __syncthreads();  // barrier 1
+  const float mult = qsc[32 * ht + n] * lat_scale * sm_scale * kLog2e;
 
   const int grp = lane >> 4, li = lane & 15;
   // MFMA row n -> tile token 32*((n>>2)&1) + 16*hf + 4*(n>>3) + (n&3)
@@ -283,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   }
   const int head0 = 32 * ht;
   const int dim0 = 256 * hf + n;
-  if (num_splits == 1) {
+  if (mode == kDirect) {
     uint16_t* ob = out_bf16 + (int64_t)row * kMlaHeads * kVDim;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -295,8 +358,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         ob[(int64_t)h * kVDim + dim0 + 32 * dt] = (uint16_t)(u >> 16);
       }
     if (g == 0 && hf == 0) lse_out[(int64_t)row * kMlaHeads + head0 + n] = lse;
-  } else {
-    float* op = o_part + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
+  } else if (mode == kPartF32) {
+    float* op = static_cast<float*>(o_part) + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -305,30 +368,54 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         op[(int64_t)h * kVDim + dim0 + 32 * dt] = acc[dt][i] * fr[i];
       }
     if (g == 0 && hf == 0) lse_part[((int64_t)s * n_q + row) * kMlaHeads + head0 + n] = lse;
+  } else {
+    _Float16* op = static_cast<_Float16*>(o_part) + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
+    const float unscale = 1.0f / lat_scale;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = head0 + 8 * (i / 4) + 4 * g + (i % 4);
+        op[(int64_t)h * kVDim + dim0 + 32 * dt] = (_Float16)(acc[dt][i] * (fr[i] * unscale));
+      }
+    if (g == 0 && hf == 0) lse_part[((int64_t)s * n_q + row) * kMlaHeads + head0 + n] = lse;
   }
 }
 
 }  // namespace
 
-size_t sparse_mla_workspace_bytes(int n_q) {
-  const size_t codes = ((size_t)n_q * kMlaHeads * kLatDim + 255) / 256 * 256;
-  return codes + (size_t)n_q * kMlaHeads * sizeof(float);
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t sparse_mla_workspace_bytes(int n_q, int num_splits) {
+  if (num_splits <= 1) return 256;
+  const size_t parts = (size_t)num_splits * n_q * kMlaHeads;
+  return align256(parts * kVDim * sizeof(uint16_t)) + align256(parts * sizeof(float));
 }
 
-hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* latent_pages,
-                             int64_t latent_page_stride, float latent_scale,
-                             const int32_t* topk_slot, int k, float softmax_scale, int num_splits,
-                             float* o_part, float* lse_part, uint16_t* out_bf16, float* lse,
-                             void* workspace, hipStream_t st) {
-  // query prep once per row: E4M3 codes + power-of-two scales shared by all splits
-  uint8_t* q8 = static_cast<uint8_t*>(workspace);
-  float* qs = reinterpret_cast<float*>(q8 + ((size_t)n_q * kMlaHeads * kLatDim + 255) / 256 * 256);
-  hipError_t e = launch_quantize_q(n_q, kMlaHeads, kLatDim, q, q8, qs, st);
-  if (e != hipSuccess) return e;
+hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, const float* q_scale,
+                             const uint8_t* latent_pages, int64_t latent_page_stride,
+                             float latent_scale, const int32_t* topk_slot, int k,
+                             float softmax_scale, int num_splits, float* o_part, float* lse_part,
+                             uint16_t* out_bf16, float* lse, void* workspace, hipStream_t st) {
+  int mode = kDirect;
+  void* op = o_part;
+  float* lp = lse_part;
+  if (o_part) {
+    mode = kPartF32;
+  } else if (num_splits > 1) {
+    mode = kPartF16;
+    const size_t parts = (size_t)num_splits * n_q * kMlaHeads;
+    op = workspace;
+    lp = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                  align256(parts * kVDim * sizeof(uint16_t)));
+  }
   hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)num_splits, (unsigned)n_q), dim3(kThreads), 0,
-                     st, q8, qs, latent_pages, latent_page_stride, latent_scale, topk_slot, k,
-                     softmax_scale, num_splits, n_q, o_part, lse_part, out_bf16, lse);
-  return hipGetLastError();
+                     st, q, q8, q_scale, latent_pages, latent_page_stride, latent_scale, topk_slot,
+                     k, softmax_scale, num_splits, n_q, mode, op, lp, out_bf16, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || mode != kPartF16) return e;
+  return launch_lse_combine_f16(num_splits, n_q, static_cast<const uint16_t*>(op), lp,
+                                latent_scale, out_bf16, lse, st);
 }
 
 }  // namespace dsa

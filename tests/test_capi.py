@@ -89,23 +89,32 @@ def test_topk_rejects_bad_host_args(L):
 
 def test_sparse_mla_and_combine_reject_bad_host_args(L):
     f = L.dsa_sparse_mla_decode
-    need = L.dsa_sparse_mla_workspace_size(4)
-    assert need >= 4 * 96 * 576
-    base = [4, FAKE, FAKE, 36864, ctypes.c_float(0.01), FAKE, 2048, ctypes.c_float(0.04), 4, FAKE,
-            FAKE, None, None, ctypes.c_void_p(0x10000), need, None]
-    for patch, status in [({0: 0}, 1), ({6: 0}, 2), ({8: 0}, 2), ({8: 65}, 2), ({3: 36863}, 1),
-                          ({4: ctypes.c_float(0.0)}, 1), ({9: None}, 1), ({2: FAKE_ODD}, 1),
-                          ({14: need - 1}, 3), ({13: None}, 3), ({13: ctypes.c_void_p(0x10010)}, 1)]:
+    need = L.dsa_sparse_mla_workspace_size(4, 4)
+    assert need >= 4 * 4 * 96 * 512 * 2
+    assert L.dsa_sparse_mla_workspace_size(0, 4) == 0 and L.dsa_sparse_mla_workspace_size(4, 65) == 0
+    WS = ctypes.c_void_p(0x10000)
+    # n_q, q_bf16, q8, q_scale, latent, stride, lat_scale, slots, k, sm, S, out, lse, o_part,
+    # lse_part, workspace, ws_bytes, stream: merged output through the workspace
+    base = [4, FAKE, None, None, FAKE, 36864, ctypes.c_float(0.01), FAKE, 2048,
+            ctypes.c_float(0.04), 4, FAKE, FAKE, None, None, WS, need, None]
+    for patch, status in [({0: 0}, 1), ({8: 0}, 2), ({10: 0}, 2), ({10: 65}, 2), ({5: 36863}, 1),
+                          ({6: ctypes.c_float(0.0)}, 1), ({7: None}, 1), ({4: FAKE_ODD}, 1),
+                          ({16: need - 1}, 3), ({15: None}, 3), ({15: ctypes.c_void_p(0x10010)}, 1),
+                          ({1: None}, 1), ({2: FAKE}, 1), ({1: FAKE_ODD}, 1), ({11: None}, 1),
+                          ({13: FAKE}, 1)]:
         args = list(base)
         for i, v in patch.items():
             args[i] = v
         assert f(*args) == status, (patch, _err())
     args = list(base)
-    args[6], args[8] = 3, 4                      # more splits than selected tokens
+    args[8], args[10] = 3, 4                     # more splits than selected tokens
     assert f(*args) == 1
-    args = list(base)
-    args[8] = 1                                  # one split needs out/lse
-    assert f(*args) == 1
+    args = list(base)                            # fp32 partials: no workspace needed
+    args[11] = args[12] = None
+    args[13] = args[14] = FAKE
+    args[15], args[16] = None, 0
+    args[0] = 0                                  # (stopped by n_q, after the layout checks)
+    assert f(*args) == 1 and "n_q" in _err()
     g = L.dsa_lse_combine
     assert g(0, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert g(65, 4, FAKE, FAKE, FAKE, FAKE, None) == 2

@@ -58,25 +58,43 @@ def run_topk(batch, scores, k, with_slots=True):
 
 
 def run_mla(batch, slots, num_splits):
+    """fp32 split partials merged by dsa_lse_combine (one split: the direct output)."""
     n_q = batch.wl.n_q
     if num_splits == 1:
         out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
         lse = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
         dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale, slots,
-                                  batch.softmax_scale, 1, out=out, lse=lse,
-                                  workspace=dsa.workspace(dsa.dsa_sparse_mla_workspace_size(n_q)))
+                                  batch.softmax_scale, 1, out=out, lse=lse)
         torch.cuda.synchronize()
         return out, lse, None, None
     op = torch.full((num_splits, n_q, 96, 512), float("nan"), device=DEV)
     lp = torch.full((num_splits, n_q, 96), float("nan"), device=DEV)
     dsa.dsa_sparse_mla_decode(batch.q_mla, batch.latent_pool, batch.latent_scale, slots,
-                              batch.softmax_scale, num_splits, o_part=op, lse_part=lp,
-                              workspace=dsa.workspace(dsa.dsa_sparse_mla_workspace_size(n_q)))
+                              batch.softmax_scale, num_splits, o_part=op, lse_part=lp)
     out = torch.empty((n_q, 96, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
     dsa.dsa_lse_combine(op, lp, out, lse)
     torch.cuda.synchronize()
     return out, lse, op, lp
+
+
+def run_mla_merged(batch, slots, num_splits, prepared=False):
+    """(out, lse) from one call: fp16 partials merged inside it when num_splits > 1;
+    prepared: the query quantised beforehand by dsa_quantize_q."""
+    n_q = batch.wl.n_q
+    out = torch.full((n_q, 96, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((n_q, 96), float("nan"), dtype=torch.float32, device=DEV)
+    kw = {}
+    if prepared:
+        q8 = torch.empty((n_q, 96, 576), dtype=torch.uint8, device=DEV)
+        qs = torch.empty((n_q, 96), dtype=torch.float32, device=DEV)
+        dsa.dsa_quantize_q(batch.q_mla, q8, qs)
+        kw = dict(q8=q8, q_scale=qs)
+    dsa.dsa_sparse_mla_decode(None if prepared else batch.q_mla, batch.latent_pool,
+                              batch.latent_scale, slots, batch.softmax_scale, num_splits,
+                              out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    return out, lse
 
 
 # ------------------------------------------------------------------------ a0: quantisation
@@ -236,9 +254,7 @@ def _oracle_attention(batch, row, slots_row, num_splits):
     return parts
 
 
-@pytest.mark.parametrize("num_splits", [1, 3, 16])
-def test_sparse_mla_small(num_splits):
-    say("mla", num_splits)
+def _mla_small_case(num_splits):
     wl = synth.custom([3000, 700, 64], [2, 1, 1], topk=256, seed=41)
     batch = synth.make_batch(wl, DEV)
     # selections: random distinct visible tokens, the short request padded with -1
@@ -249,6 +265,13 @@ def test_sparse_mla_small(num_splits):
         n = min(256, pos + 1)
         t = np.sort(rng.choice(pos + 1, size=n, replace=False))
         slots[row, :n] = O.physical_slot(bt[b], t)
+    return wl, batch, slots
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16])
+def test_sparse_mla_small(num_splits):
+    say("mla", num_splits)
+    wl, batch, slots = _mla_small_case(num_splits)
     slots_d = torch.from_numpy(slots).to(DEV)
     out, lse, op, lp = run_mla(batch, slots_d, num_splits)
     out = out.float().cpu().numpy()
@@ -261,6 +284,24 @@ def test_sparse_mla_small(num_splits):
             for s_, (po, pl) in enumerate(parts):
                 check_attention(op[s_, row].cpu().numpy(), lp[s_, row].cpu().numpy(), po, pl,
                                 f"row {row} split {s_}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16])
+@pytest.mark.parametrize("prepared", [False, True], ids=["bf16-query", "prepared-query"])
+def test_sparse_mla_merged_in_call(num_splits, prepared):
+    # fp16 split partials merged inside the call, against the oracle; and the prepared
+    # query gives bitwise the output of the query quantised in the kernel
+    say("mla merged", num_splits, prepared)
+    wl, batch, slots = _mla_small_case(num_splits)
+    slots_d = torch.from_numpy(slots).to(DEV)
+    out, lse = run_mla_merged(batch, slots_d, num_splits, prepared)
+    o_np, l_np = out.float().cpu().numpy(), lse.cpu().numpy()
+    for row in range(wl.n_q):
+        o_ref, l_ref = O.lse_combine(_oracle_attention(batch, row, slots[row], num_splits))
+        check_attention(o_np[row], l_np[row], o_ref, l_ref, f"row {row} S={num_splits} merged")
+    if prepared:
+        out2, lse2 = run_mla_merged(batch, slots_d, num_splits, False)
+        assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
 def test_sparse_mla_topk_equal_to_context_is_dense_mla():
