@@ -69,9 +69,9 @@ def _source_hash(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def _traffic_from_profile(kernel_src):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the
-    current kernel source; None otherwise."""
+def _traffic_from_profile():
+    """HBM bytes per launch of the indexer from the committed counter summary, if it was
+    taken on the current kernel sources; None otherwise."""
     p = os.path.join(ROOT, "profiles", "index_score_long_counters.json")
     if not os.path.exists(p):
         return None
@@ -79,7 +79,8 @@ def _traffic_from_profile(kernel_src):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("source_sha256_16") != _source_hash(kernel_src):
+    hashes = d.get("source_sha256_16")
+    if not isinstance(hashes, dict) or any(_source_hash(f) != v for f, v in hashes.items()):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -263,7 +264,7 @@ def main():
     value = ab["total"] / (mean_us * 1e-6) / 1e9
     idx_bytes = index_score_bytes(wl.seq_lens)
     idx_gbps = idx_bytes / (stage_mean[0] * 1e-6) / 1e9
-    traffic = _traffic_from_profile("index_score.hip")
+    traffic = _traffic_from_profile()
     ceiling = stream_read_ceiling(torch)
     if args.copy_calibration:
         src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")

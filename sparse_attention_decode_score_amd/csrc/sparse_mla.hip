@@ -73,7 +73,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ int32_t slot_l[kSlotsLds];
   __shared__ uint64_t valid_mask[2];
 
-  const int s = blockIdx.x, row = blockIdx.y;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id; when the grid divides
+  // evenly, all splits of a row go to one XCD, so the row's query (read by every split)
+  // comes from that XCD's L2 after the first read.
+  int s = blockIdx.x, row = blockIdx.y;
+  {
+    const int total = num_splits * n_q;
+    if ((total & 7) == 0) {
+      const int lin = blockIdx.x + num_splits * blockIdx.y;
+      const int i = (lin & 7) * (total >> 3) + (lin >> 3);
+      row = i / num_splits;
+      s = i - row * num_splits;
+    }
+  }
   const int beg = (int)((int64_t)s * k / num_splits);
   const int end = (int)((int64_t)(s + 1) * k / num_splits);
   const int n_tok = end - beg;
