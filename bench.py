@@ -85,9 +85,10 @@ def _traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(batch, rows, budget_s=20.0):
-    """Times the oracle (as it stands) on a bounded sample of rows of the same workload and
-    returns throughput in the benchmark's unit (algorithmic GB/s)."""
+def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
+    """Times the oracle (as it stands) on a bounded sample of the same workload: the rows are
+    taken in turn (cycling) until budget_s seconds of oracle time have been spent, and the
+    throughput is returned in the benchmark's unit (algorithmic GB/s)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import oracle as O
@@ -95,16 +96,20 @@ def cpu_baseline(batch, rows, budget_s=20.0):
     wl = batch.wl
     rowpos = wl.row_positions()
     done, t_total, byts = 0, 0.0, 0
-    for row in rows:
+    rows = list(rows)
+    host = {}  # each sampled row's inputs, copied to the host once (outside the timing)
+    for i in range(len(rows) * max_passes):
+        row = rows[i % len(rows)]
         b, pos = rowpos[row]
         L = wl.seq_lens[b]
-        pages = batch.block_table[b, : (L + 63) // 64].long()
-        key_pages = batch.key_pool[pages].cpu().numpy()
-        bt_local = np.arange(len(pages))
-        qi = batch.q_idx[row].cpu().double().numpy()
-        w = batch.head_w[row].cpu().numpy()
-        qm = batch.q_mla[row].cpu().double().numpy()
-        lat_pages = batch.latent_pool[pages].cpu().numpy()
+        if row not in host:
+            pages = batch.block_table[b, : (L + 63) // 64].long()
+            host[row] = (batch.key_pool[pages].cpu().numpy(), np.arange(len(pages)),
+                         batch.q_idx[row].cpu().double().numpy(),
+                         batch.head_w[row].cpu().numpy(),
+                         batch.q_mla[row].cpu().double().numpy(),
+                         batch.latent_pool[pages].cpu().numpy())
+        key_pages, bt_local, qi, w, qm, lat_pages = host[row]
         t0 = time.perf_counter()
         kc, ks = O.read_index_keys(key_pages, bt_local, L)
         scores = O.index_scores(qi, w, kc[: pos + 1], ks[: pos + 1])
@@ -125,9 +130,9 @@ def cpu_baseline(batch, rows, budget_s=20.0):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} query rows of the {wl.name} workload (rows {list(rows)[:done]}), "
-                      f"whole path per row, {t_total:.1f} s of CPU time; GB/s = those rows' "
-                      f"share of the algorithmic bytes / time"}
+            "sample": f"{done} query-row passes over the {len(rows)} rows of the {wl.name} "
+                      f"workload taken in turn, whole path per row, {t_total:.1f} s of CPU "
+                      f"time; GB/s = those rows' share of the algorithmic bytes / time"}
 
 
 def _probe_lib():
