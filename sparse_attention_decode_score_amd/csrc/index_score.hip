@@ -129,9 +129,14 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int seg_groups = (p_end - p0 + kGroupPages - 1) / kGroupPages;
   const int ng = max(0, (seg_groups - wave + kWaves - 1) / kWaves);
 
-  // 1. query loads first (older than the key loads, so waiting for them does not wait
-  //    for the keys): 32 heads x 8 parts of 16 dims per row; rows past the group repeat
-  //    its last row
+  // 1. one vector load fetches the wave's block-table entries (lane s: its s-th page,
+  //    clamped to a visible page); it is the only load the key stream depends on, so it
+  //    goes first.  2. the query and head weights (32 heads x 8 parts of 16 dims per row;
+  //    rows past the group repeat its last row).  3. the first NF pages of the ring, as
+  //    soon as the block-table entries are back (waiting for them does not wait for the
+  //    query, issued after them).  The scheduling barriers keep this order: the query's
+  //    arithmetic must not be hoisted above the key loads.
+  const int bt_lane = bt[min(page_of(lane % (kGroupPages * G)), p_end - 1)];
   const int qh = tid >> 3, qpart = tid & 7;
   v4i qraw[R][2];
   float hw[R];
@@ -143,9 +148,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     qraw[r][1] = *reinterpret_cast<const v4i*>(src + 8);
     hw[r] = head_w[(int64_t)row * kIdxHeads + qh];
   }
-  // 2. one vector load fetches the wave's block-table entries (lane s: its s-th page,
-  //    clamped to a visible page), then the first NF pages of the ring
-  const int bt_lane = bt[min(page_of(lane % (kGroupPages * G)), p_end - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   auto page_ptr = [&](int s) {
     return key_pages + (int64_t)__builtin_amdgcn_readlane(bt_lane, s) * page_stride;
   };
@@ -154,6 +157,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   KeyPage kp[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) load_key_page(kp[j], page_ptr(j), lane);
+  __builtin_amdgcn_sched_barrier(0);
   // 3. fused query prep while the keys stream in: E4M3 codes, one power-of-two scale per
   //    (row, head), the scale folded into the head weight
 #pragma unroll
@@ -275,10 +279,20 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   // 5. write what was staged: scores (and candidates) of the workgroup, coalesced
   if constexpr (STAGE) {
     __syncthreads();
+    // non-temporal stores: the scores are read again only by the rare resend of a group,
+    // and plain stores interleaved with the key stream cost the stream about 8% of its rate
     const int seg_tok = min(p_end * kPage, L) - p0 * kPage;
     for (int r = 0; r < nr; ++r) {
       float* dst = scores + (int64_t)(r0 + r) * score_stride + p0 * kPage;
-      for (int i = tid; i < seg_tok; i += 256) dst[i] = sbuf[r][i];
+      const bool vec = (((uintptr_t)dst) & 15) == 0;
+      for (int i = 4 * tid; i < seg_tok; i += 1024) {
+        if (vec && i + 3 < seg_tok) {
+          __builtin_nontemporal_store(*reinterpret_cast<const v4f*>(&sbuf[r][i]),
+                                      reinterpret_cast<v4f*>(dst + i));
+        } else {
+          for (int j = i; j < min(i + 4, seg_tok); ++j) __builtin_nontemporal_store(sbuf[r][j], dst + j);
+        }
+      }
     }
     if constexpr (CAND) {
       const int g_lo = p0 / kGroupPages;
