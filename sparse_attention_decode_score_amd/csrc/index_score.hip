@@ -57,6 +57,13 @@ __device__ __forceinline__ void load_key_page(KeyPage& kp, const uint8_t* base, 
   kp.s = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + kIdxPageKeyBytes + 4 * lane));
 }
 
+// ReLU as a signed-integer max on the float's bits: positive values keep their bits,
+// negative values and -0.0 become +0.0.  One v_max_i32; a float max would first have to
+// quiet possible signalling NaNs of the MFMA result (two instructions per value).
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Pages each wave keeps in flight: four for one or two rows, two for larger row groups
 // (register budget).  Groups per wave at most: the staged scores of a workgroup are
 // 16 KB of LDS for up to four rows; eight rows store directly.
@@ -216,8 +223,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
         const v4f w = *reinterpret_cast<const v4f*>(&wps[r][8 * a + 4 * g]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          acc0 = fmaf(w[c], fmaxf(d0[4 * a + c], 0.f), acc0);
-          acc1 = fmaf(w[c], fmaxf(d1[4 * a + c], 0.f), acc1);
+          acc0 = fmaf(w[c], relu(d0[4 * a + c]), acc0);
+          acc1 = fmaf(w[c], relu(d1[4 * a + c]), acc1);
         }
       }
       // lanes 0..31: (half-0 partial, partner's half-0 partial); lanes 32..63: half 1
