@@ -183,6 +183,9 @@ def main():
     ap.add_argument("--query-side-stream", action="store_true",
                     help="quantise the MLA query on a side stream during stages 1-2 instead of "
                          "inside the attention kernel")
+    ap.add_argument("--select-in-attention", action="store_true",
+                    help="run stage 2's final pass inside the attention kernel (one launch for "
+                         "stages 2-4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -203,7 +206,8 @@ def main():
     torch.cuda.set_device(0)
     batch = synth.make_batch(wl, "cuda")
     step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
-                          query_on_side_stream=args.query_side_stream)
+                          query_on_side_stream=args.query_side_stream,
+                          select_in_attention=args.select_in_attention)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
     flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -229,12 +233,18 @@ def main():
                    batch.block_table, max(wl.q_per_seq), stream)
         if evs:
             evs[1].record(stream)
-        step.select(batch.cu_q, batch.seq_lens, batch.block_table, stream)
+        if not step.select_in_attention:
+            step.select(batch.cu_q, batch.seq_lens, batch.block_table, stream)
         if evs:
             evs[2].record(stream)
         if step.query_on_side_stream:
             stream.wait_event(step._ev_query)
-        step.attend(batch.q_mla, batch.latent_pool, batch.latent_scale, batch.softmax_scale, stream)
+        if step.select_in_attention:
+            step.select_attend(batch.cu_q, batch.seq_lens, batch.block_table, batch.q_mla,
+                               batch.latent_pool, batch.latent_scale, batch.softmax_scale, stream)
+        else:
+            step.attend(batch.q_mla, batch.latent_pool, batch.latent_scale, batch.softmax_scale,
+                        stream)
         if evs:
             evs[3].record(stream)
 
@@ -302,12 +312,16 @@ def main():
                    "context": wl.max_seq_len if len(set(wl.seq_lens)) == 1 else "ragged",
                    "topk": wl.topk, "num_splits": S, "page_size": PAGE,
                    "indexer_emits_topk_candidates": not args.unfused,
+                   "topk_final_in_attention": args.select_in_attention,
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),
         "us_per_layer_median": round(med, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
-        "stage_us": {"index_score": round(stage_mean[0], 2), "topk": round(stage_mean[1], 2),
-                     "sparse_mla_and_merge": round(stage_mean[2], 2)},
+        "stage_us": ({"index_score": round(stage_mean[0], 2),
+                      "topk_final_in_sparse_mla_and_merge": round(stage_mean[2], 2)}
+                     if args.select_in_attention else
+                     {"index_score": round(stage_mean[0], 2), "topk": round(stage_mean[1], 2),
+                      "sparse_mla_and_merge": round(stage_mean[2], 2)}),
         "algorithmic_bytes": ab,
         "dsa_vs_dense_mla_bytes": round(ab["total"] / dense_mla_bytes(wl.seq_lens, wl.q_per_seq), 4),
         "roofline": {"kernel": "dsa_index_score", "bound": "hbm", "achieved": round(idx_gbps, 1),

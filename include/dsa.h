@@ -13,6 +13,8 @@
  *                         scorer + exact top-k pair of "Fused low-latency decode for DSA layers").
  *   dsa_sparse_mla_decode stage 3  MLA over selected tokens ("Sparse attention cuts long-context
  *                                                             decode bandwidth")
+ *   dsa_topk_sparse_mla   stages 2-4 in one launch: each attention workgroup first runs its
+ *                         row's final top-k pass over the stage-1 candidates
  *   dsa_lse_combine       stage 4  LSE merge of splits      ("Decode context parallelism with the
  *                                                             sparse indexer")
  *   dsa_quantize_q        the query quantisation the stages 1 and 3 apply internally
@@ -100,7 +102,7 @@ typedef enum {
  *            keys it may not see (ignored by dsa_topk); other columns are not touched.
  *   cand_k, cand_workspace, cand_workspace_bytes: if cand_workspace is not NULL the
  *            scoring waves also write, for a top-k of cand_k (1..4096), every 256-token
- *            group's best candidates (3x the winners a full group holds on average, in
+ *            group's best candidates (4x the winners a full group holds on average, in
  *            token order) and the group's boundary element into it; it must hold
  *            dsa_topk_workspace_size(n_q, max_seq_len, cand_k) bytes, 256-byte aligned.
  *            Pass it to dsa_topk with from_candidates = 1.  NULL: scores only.
@@ -115,7 +117,7 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
 /*
  * Stage 2 — exact top-k over each row's visible scores (tokens 0..position).
  * Order: score descending, then token index ascending (-0.0 == +0.0; NaN ranks lowest).
- * Two passes: every 256-token group keeps its best m candidates (3x the winners a full
+ * Two passes: every 256-token group keeps its best m candidates (4x the winners a full
  * group holds on average), then one workgroup per row selects from the candidates; the
  * groups that could have held more of the winners than they sent (the detection rule of
  * the K3.1 page's exact one-round merge) are re-read in full from the scores and the row is
@@ -172,6 +174,35 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
                                  int32_t num_splits, void* out_bf16, float* lse, float* o_part,
                                  float* lse_part, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * Stages 2 + 3 (+ 4) in one launch: the final top-k pass and the sparse MLA.  Every
+ * (split, row) workgroup of the attention first selects its row's top k from the
+ * candidates dsa_index_score wrote (cand_workspace, written with cand_k = k for this batch
+ * and these scores), exactly as dsa_topk(..., from_candidates = 1) does, then attends over
+ * its split's slice of the selection.  The pairing of a scorer with an exact top-k ahead of
+ * the attention in one low-latency decode path is that of "Fused low-latency decode for DSA
+ * layers"; putting the row's final pass inside the attention's workgroups (each split of a
+ * row repeats it) removes one launch and the wait on a single workgroup per row.
+ *   Batch, scores, k, block_table (required here): as for dsa_topk.
+ *   cand_workspace: dsa_topk_workspace_size(n_q, max_seq_len, k) bytes, 256-byte aligned,
+ *   read only.
+ *   topk_idx, topk_slot: optional outputs (each may be NULL), as dsa_topk writes them.
+ *   Query, latent cache, softmax_scale, num_splits (S <= k), out_bf16 [n_q][96][512] bf16,
+ *   lse [n_q][96] fp32, workspace (S > 1: dsa_sparse_mla_workspace_size(n_q, S) bytes,
+ *   256-byte aligned): as for dsa_sparse_mla_decode without o_part.  The results are
+ *   bitwise those of dsa_topk(from_candidates = 1) followed by dsa_sparse_mla_decode.
+ */
+dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                               const int32_t* cu_q, const int32_t* seq_lens, const float* scores,
+                               int64_t score_stride, int32_t k, const int32_t* block_table,
+                               int32_t bt_stride, const void* cand_workspace,
+                               size_t cand_workspace_bytes, int32_t* topk_idx,
+                               int32_t* topk_slot, const void* q_bf16, const void* q8,
+                               const float* q_scale, const void* latent_pages,
+                               int64_t latent_page_stride, float latent_scale,
+                               float softmax_scale, int32_t num_splits, void* out_bf16,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Stage 4 — log-sum-exp merge of split partials:

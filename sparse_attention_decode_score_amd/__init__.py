@@ -56,12 +56,15 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_workspace_size.restype = _SZ
         L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _P, _P, _I64, _F32, _P, _I32, _F32, _I32,
                                             _P, _P, _P, _P, _P, _SZ, _P]
+        L.dsa_topk_sparse_mla.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P,
+                                          _SZ, _P, _P, _P, _P, _P, _P, _I64, _F32, _F32, _I32,
+                                          _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
-        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_lse_combine",
-                  "dsa_quantize_q"):
+        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
+                  "dsa_lse_combine", "dsa_quantize_q"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -214,6 +217,50 @@ def dsa_sparse_mla_decode(q_mla: Optional[torch.Tensor], latent_pages: torch.Ten
                                        _stream(stream)))
 
 
+def dsa_topk_sparse_mla(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,
+                        block_table: torch.Tensor, cand_workspace: torch.Tensor,
+                        q_mla: Optional[torch.Tensor], latent_pages: torch.Tensor,
+                        latent_scale: float, softmax_scale: float, num_splits: int, *,
+                        max_seq_len: int, out: torch.Tensor, lse: torch.Tensor,
+                        topk_idx: Optional[torch.Tensor] = None,
+                        topk_slot: Optional[torch.Tensor] = None,
+                        q8: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None,
+                        latent_page_stride: Optional[int] = None, stream=None) -> None:
+    """Final top-k pass and sparse MLA in one launch: every attention workgroup selects its
+    row's top k from the candidates dsa_index_score left in cand_workspace (cand_k = k), then
+    attends over its split of them.  topk_idx / topk_slot, when given, receive the selection."""
+    num_seqs = seq_lens.shape[0]
+    n_q = scores.shape[0]
+    _expect(scores, "scores", torch.float32)
+    _expect(cand_workspace, "cand_workspace", torch.uint8)
+    if topk_idx is not None:
+        _expect(topk_idx, "topk_idx", torch.int32, (n_q, k))
+    if topk_slot is not None:
+        _expect(topk_slot, "topk_slot", torch.int32, (n_q, k))
+    if q8 is not None:
+        _expect(q8, "q8", torch.uint8, (n_q, MLA_HEADS, LATENT_DIM))
+        _expect(q_scale, "q_scale", torch.float32, (n_q, MLA_HEADS))
+    else:
+        _expect(q_mla, "q_mla", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+    _expect(out, "out", torch.bfloat16, (n_q, MLA_HEADS, V_DIM))
+    _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
+    if num_splits > 1 and workspace is None:
+        workspace = globals()["workspace"](dsa_sparse_mla_workspace_size(n_q, num_splits),
+                                           scores.device)
+    if workspace is not None:
+        _expect(workspace, "workspace", torch.uint8)
+    stride = (latent_page_stride if latent_page_stride is not None
+              else latent_pages.stride(0) * latent_pages.element_size())
+    _check(lib().dsa_topk_sparse_mla(
+        num_seqs, n_q, int(max_seq_len), _ptr(cu_q), _ptr(seq_lens), _ptr(scores),
+        scores.shape[1], int(k), _ptr(block_table), block_table.shape[1], _ptr(cand_workspace),
+        cand_workspace.numel(), _ptr(topk_idx), _ptr(topk_slot), _ptr(q_mla), _ptr(q8),
+        _ptr(q_scale), _ptr(latent_pages), int(stride), float(latent_scale),
+        float(softmax_scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
+
+
 def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Tensor,
                     lse: torch.Tensor, stream=None) -> None:
     """LSE merge of split partials [S, n_q, 96, 512] / [S, n_q, 96] into bf16 out and lse."""
@@ -235,9 +282,13 @@ class DecodeStep:
     """
 
     def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
-                 fused: bool = True, query_on_side_stream: bool = False):
+                 fused: bool = True, query_on_side_stream: bool = False,
+                 select_in_attention: bool = False):
+        if select_in_attention and not fused:
+            raise ValueError("select_in_attention needs the indexer's candidates (fused=True)")
         self.n_q, self.max_seq_len, self.k, self.num_splits = n_q, max_seq_len, k, num_splits
         self.fused = fused
+        self.select_in_attention = select_in_attention
         self.query_on_side_stream = query_on_side_stream
         dev = torch.device(device)
         self.scores = torch.empty((n_q, max_seq_len), dtype=torch.float32, device=dev)
@@ -285,6 +336,19 @@ class DecodeStep:
                                   workspace=self.mla_workspace, stream=stream)
         return self.out, self.lse
 
+    def select_attend(self, cu_q, seq_lens, block_table, q_mla, latent_pages, latent_scale,
+                      softmax_scale, stream=None):
+        """Stages 2-4 in one launch (the final top-k pass inside the attention kernel)."""
+        prepared = self.query_on_side_stream
+        dsa_topk_sparse_mla(cu_q, seq_lens, self.scores, self.k, block_table, self.workspace,
+                            None if prepared else q_mla, latent_pages, latent_scale,
+                            softmax_scale, self.num_splits, max_seq_len=self.max_seq_len,
+                            out=self.out, lse=self.lse,
+                            q8=self.q8 if prepared else None,
+                            q_scale=self.q_scale if prepared else None,
+                            workspace=self.mla_workspace, stream=stream)
+        return self.out, self.lse
+
     def run(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, q_mla, latent_pages,
             latent_scale, softmax_scale, max_q_per_seq, stream=None):
         main = torch.cuda.current_stream() if stream is None else stream
@@ -294,6 +358,11 @@ class DecodeStep:
             self.prepare_query(q_mla, stream=self.side)
             self._ev_query.record(self.side)
         self.index(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq, main)
+        if self.select_in_attention:
+            if self.query_on_side_stream:
+                main.wait_event(self._ev_query)
+            return self.select_attend(cu_q, seq_lens, block_table, q_mla, latent_pages,
+                                      latent_scale, softmax_scale, main)
         self.select(cu_q, seq_lens, block_table, main)
         if self.query_on_side_stream:
             main.wait_event(self._ev_query)

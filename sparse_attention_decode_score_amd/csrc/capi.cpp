@@ -52,6 +52,45 @@ dsa_status check_batch(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const
   return DSA_OK;
 }
 
+// Shared checks of the query, the latent cache and the scalars of stage 3.
+dsa_status check_mla_inputs(int32_t n_q, const void* q_bf16, const void* q8,
+                                   const float* q_scale, const void* latent_pages,
+                                   int64_t latent_page_stride, float latent_scale, int32_t k,
+                                   float softmax_scale, int32_t num_splits) {
+  DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
+  if (num_splits < 1 || num_splits > DSA_MAX_SPLITS)
+    return fail(DSA_ERR_UNSUPPORTED, "num_splits must be in 1..64 (got %d)", num_splits);
+  DSA_REQUIRE(num_splits <= k, "num_splits (%d) must be <= k (%d)", num_splits, k);
+  const bool prepared = q8 != nullptr && q_scale != nullptr;
+  DSA_REQUIRE((q8 == nullptr) == (q_scale == nullptr), "q8 and q_scale must both be given or both be NULL");
+  DSA_REQUIRE(prepared || q_bf16, "the query is missing: give q_bf16 or q8 and q_scale");
+  DSA_REQUIRE(latent_pages, "latent_pages must be non-null");
+  DSA_REQUIRE(prepared ? aligned(q8, 16) : aligned(q_bf16, 16), "the query must be 16-byte aligned");
+  DSA_REQUIRE(aligned(latent_pages, 16), "latent_pages must be 16-byte aligned");
+  DSA_REQUIRE(latent_page_stride >= DSA_LATENT_PAGE_BYTES && latent_page_stride % 16 == 0,
+              "latent_page_stride must be >= 36864 and a multiple of 16 (got %lld)",
+              (long long)latent_page_stride);
+  DSA_REQUIRE(latent_scale > 0.f, "latent_scale must be > 0");
+  DSA_REQUIRE(softmax_scale > 0.f, "softmax_scale must be > 0");
+  return DSA_OK;
+}
+
+dsa_status check_merged_outputs(int32_t n_q, int32_t num_splits, const void* out_bf16,
+                                       const float* lse, const void* workspace,
+                                       size_t workspace_bytes) {
+  DSA_REQUIRE(out_bf16 && lse, "out_bf16 and lse are needed when o_part is NULL");
+  DSA_REQUIRE(aligned(out_bf16, 16), "out_bf16 must be 16-byte aligned");
+  if (num_splits > 1) {
+    const size_t need = dsa::sparse_mla_workspace_bytes(n_q, num_splits);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, need);
+    DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
+  }
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,36 +200,18 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
                                  int32_t num_splits, void* out_bf16, float* lse, float* o_part,
                                  float* lse_part, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  DSA_REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
-  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
-  if (num_splits < 1 || num_splits > DSA_MAX_SPLITS)
-    return fail(DSA_ERR_UNSUPPORTED, "num_splits must be in 1..64 (got %d)", num_splits);
-  DSA_REQUIRE(num_splits <= k, "num_splits (%d) must be <= k (%d)", num_splits, k);
-  const bool prepared = q8 != nullptr && q_scale != nullptr;
-  DSA_REQUIRE((q8 == nullptr) == (q_scale == nullptr), "q8 and q_scale must both be given or both be NULL");
-  DSA_REQUIRE(prepared || q_bf16, "the query is missing: give q_bf16 or q8 and q_scale");
-  DSA_REQUIRE(latent_pages && topk_slot, "latent_pages and topk_slot must be non-null");
-  DSA_REQUIRE(prepared ? aligned(q8, 16) : aligned(q_bf16, 16), "the query must be 16-byte aligned");
-  DSA_REQUIRE(aligned(latent_pages, 16), "latent_pages must be 16-byte aligned");
-  DSA_REQUIRE(latent_page_stride >= DSA_LATENT_PAGE_BYTES && latent_page_stride % 16 == 0,
-              "latent_page_stride must be >= 36864 and a multiple of 16 (got %lld)",
-              (long long)latent_page_stride);
-  DSA_REQUIRE(latent_scale > 0.f, "latent_scale must be > 0");
-  DSA_REQUIRE(softmax_scale > 0.f, "softmax_scale must be > 0");
+  dsa_status st = check_mla_inputs(n_q, q_bf16, q8, q_scale, latent_pages, latent_page_stride,
+                                   latent_scale, k, softmax_scale, num_splits);
+  if (st != DSA_OK) return st;
+  const bool prepared = q8 != nullptr;
+  DSA_REQUIRE(topk_slot, "topk_slot must be non-null");
   DSA_REQUIRE((o_part == nullptr) == (lse_part == nullptr),
               "o_part and lse_part must both be given or both be NULL");
   if (o_part) {
     DSA_REQUIRE(aligned(o_part, 16), "o_part must be 16-byte aligned");
   } else {
-    DSA_REQUIRE(out_bf16 && lse, "out_bf16 and lse are needed when o_part is NULL");
-    DSA_REQUIRE(aligned(out_bf16, 16), "out_bf16 must be 16-byte aligned");
-    if (num_splits > 1) {
-      const size_t need = dsa::sparse_mla_workspace_bytes(n_q, num_splits);
-      if (workspace == nullptr || workspace_bytes < need)
-        return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
-                    workspace ? workspace_bytes : (size_t)0, need);
-      DSA_REQUIRE(aligned(workspace, 256), "workspace must be 256-byte aligned");
-    }
+    st = check_merged_outputs(n_q, num_splits, out_bf16, lse, workspace, workspace_bytes);
+    if (st != DSA_OK) return st;
   }
   return launched(dsa::launch_sparse_mla(n_q, static_cast<const uint16_t*>(q_bf16),
                                          prepared ? static_cast<const uint8_t*>(q8) : nullptr,
@@ -201,6 +222,47 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
                                          static_cast<uint16_t*>(out_bf16), lse, workspace,
                                          static_cast<hipStream_t>(stream)),
                   "dsa_sparse_mla_decode");
+}
+
+dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                               const int32_t* cu_q, const int32_t* seq_lens, const float* scores,
+                               int64_t score_stride, int32_t k, const int32_t* block_table,
+                               int32_t bt_stride, const void* cand_workspace,
+                               size_t cand_workspace_bytes, int32_t* topk_idx,
+                               int32_t* topk_slot, const void* q_bf16, const void* q8,
+                               const float* q_scale, const void* latent_pages,
+                               int64_t latent_page_stride, float latent_scale,
+                               float softmax_scale, int32_t num_splits, void* out_bf16,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
+  if (st != DSA_OK) return st;
+  st = check_mla_inputs(n_q, q_bf16, q8, q_scale, latent_pages, latent_page_stride, latent_scale,
+                        k, softmax_scale, num_splits);
+  if (st != DSA_OK) return st;
+  DSA_REQUIRE(scores && block_table, "scores and block_table must be non-null");
+  DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
+              (long long)score_stride, max_seq_len);
+  DSA_REQUIRE(bt_stride >= (max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE,
+              "bt_stride (%d) must cover max_seq_len (%d) in pages of 64", bt_stride, max_seq_len);
+  const size_t need = dsa::topk_workspace_bytes(n_q, max_seq_len, k);
+  if (cand_workspace == nullptr || cand_workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "candidate workspace of %zu bytes is smaller than the %zu needed",
+                cand_workspace ? cand_workspace_bytes : (size_t)0, need);
+  DSA_REQUIRE(aligned(cand_workspace, 256), "cand_workspace must be 256-byte aligned");
+  st = check_merged_outputs(n_q, num_splits, out_bf16, lse, workspace, workspace_bytes);
+  if (st != DSA_OK) return st;
+  const bool prepared = q8 != nullptr;
+  const dsa::TopkBuffers t =
+      dsa::topk_buffers(const_cast<void*>(cand_workspace), n_q, max_seq_len, k);
+  return launched(dsa::launch_topk_sparse_mla(
+                      num_seqs, n_q, cu_q, seq_lens, scores, score_stride, t, block_table,
+                      bt_stride, topk_idx, topk_slot, static_cast<const uint16_t*>(q_bf16),
+                      prepared ? static_cast<const uint8_t*>(q8) : nullptr,
+                      prepared ? q_scale : nullptr, static_cast<const uint8_t*>(latent_pages),
+                      latent_page_stride, latent_scale, k, softmax_scale, num_splits,
+                      static_cast<uint16_t*>(out_bf16), lse, workspace,
+                      static_cast<hipStream_t>(stream)),
+                  "dsa_topk_sparse_mla");
 }
 
 dsa_status dsa_lse_combine(int32_t num_splits, int32_t n_q, const float* o_part,

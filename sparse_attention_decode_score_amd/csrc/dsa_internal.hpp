@@ -56,6 +56,18 @@ hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, cons
                              float softmax_scale, int num_splits, float* o_part, float* lse_part,
                              uint16_t* out_bf16, float* lse, void* workspace, hipStream_t st);
 
+// Stage 2's final pass fused into the sparse MLA: every (split, row) workgroup selects its
+// row's top k from the candidates in t, then attends (out/lse, fp16-merged when S > 1).
+hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
+                                  const int32_t* seq_lens, const float* scores,
+                                  int64_t score_stride, const TopkBuffers& t,
+                                  const int32_t* block_table, int bt_stride, int32_t* topk_idx,
+                                  int32_t* topk_slot, const uint16_t* q, const uint8_t* q8,
+                                  const float* q_scale, const uint8_t* latent_pages,
+                                  int64_t latent_page_stride, float latent_scale, int k,
+                                  float softmax_scale, int num_splits, uint16_t* out_bf16,
+                                  float* lse, void* workspace, hipStream_t st);
+
 hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
                               uint16_t* out_bf16, float* lse, hipStream_t st);
 hipError_t launch_lse_combine_f16(int num_splits, int n_q, const uint16_t* o_part,

@@ -17,7 +17,7 @@ constexpr int kGroupTok = 256;      // tokens per first-pass group (one wave, 4 
 constexpr int kFinalThreads = DSA_FINAL_THREADS;  // threads of the final pass
 constexpr int kFinalWaves = kFinalThreads / 64;
 constexpr int kFinalPerThread = 32;  // at most, in registers
-constexpr int kBucketMax = 512;      // keys of the last search bucket, finished by one wave
+constexpr int kBucketMax = 512;      // keys of the last search bucket, finished from LDS
 constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds on chip
 
 // Per-group record of the first selection pass.
@@ -127,11 +127,54 @@ __device__ __forceinline__ int wave_sum(int v) {
          (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
-// Sum over the workgroup of a per-wave value (wave-uniform v).  red: 2 x 4 ints of LDS used
-// alternately (parity flips), so one barrier per call suffices.
-__device__ __forceinline__ int block_sum_waves(int v, int* red, int& parity) {
-  int* buf = red + kFinalWaves * parity;
+// Maximum / minimum of an unsigned value over the wave (same butterflies), wave-uniform.
+#define DSA_DPP_U32(v, ctrl) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), 0xF, 0xF, false))
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, DSA_DPP_U32(v, 0xB1));
+  v = max(v, DSA_DPP_U32(v, 0x4E));
+  v = max(v, DSA_DPP_U32(v, 0x141));
+  v = max(v, DSA_DPP_U32(v, 0x140));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, DSA_DPP_U32(v, 0xB1));
+  v = min(v, DSA_DPP_U32(v, 0x4E));
+  v = min(v, DSA_DPP_U32(v, 0x141));
+  v = min(v, DSA_DPP_U32(v, 0x140));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+#undef DSA_DPP_U32
+
+// Inclusive prefix sum over the lanes of the wave: shifted DPP adds inside each row of 16
+// lanes (a lane whose source is outside its row adds 0), then the totals of the rows below.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// ----------------------------------------------------------------------------------------
+// Workgroup (kFinalThreads threads) exchanges through `red`: 4 * kFinalWaves ints of LDS,
+// 16-byte aligned, used as two buffers of 2 * kFinalWaves ints in turn (parity flips), so one
+// barrier per exchange suffices: a wave writes a buffer again only after the barrier of the
+// exchange in between, which every wave reaches after reading it.
+__device__ __forceinline__ int* red_buf(int* red, int& parity) {
+  int* buf = red + 2 * kFinalWaves * parity;
   parity ^= 1;
+  return buf;
+}
+
+// Sum over the workgroup of a per-wave value (wave-uniform v).
+__device__ __forceinline__ int block_sum_waves(int v, int* red, int& parity) {
+  int* buf = red_buf(red, parity);
   if (lane_id() == 0) buf[threadIdx.x >> 6] = v;
   __syncthreads();
   int t = 0;
@@ -143,25 +186,35 @@ __device__ __forceinline__ int block_sum_waves(int v, int* red, int& parity) {
   return t;
 }
 
-// Sum over the workgroup of a per-thread value.  Same LDS rule.
+// Sum over the workgroup of a per-thread value.
 __device__ __forceinline__ int block_sum(int v, int* red, int& parity) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return block_sum_waves(v, red, parity);
+  return block_sum_waves(wave_sum(v), red, parity);
 }
 
-// Exclusive prefix sum over thread order; *total gets the workgroup sum.  Same LDS rule.
-__device__ __forceinline__ int block_excl_scan(int v, int* total, int* red, int& parity) {
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+// Workgroup maximum and minimum of per-thread values (both in one exchange).
+__device__ __forceinline__ void block_max_min(uint32_t& mx, uint32_t& mn, int* red, int& parity) {
+  const uint32_t a = wave_max_u32(mx), b = wave_min_u32(mn);
+  int* buf = red_buf(red, parity);
+  if (lane_id() == 0) {
+    buf[threadIdx.x >> 6] = (int)a;
+    buf[kFinalWaves + (threadIdx.x >> 6)] = (int)b;
   }
-  int* buf = red + kFinalWaves * parity;
-  parity ^= 1;
-  if (lane == 63) buf[w] = x;
+  __syncthreads();
+  mx = 0u;
+  mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kFinalWaves; ++i) {
+    mx = max(mx, (uint32_t)buf[i]);
+    mn = min(mn, (uint32_t)buf[kFinalWaves + i]);
+  }
+}
+
+// Exclusive prefix sum over thread order; *total gets the workgroup sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* red, int& parity) {
+  const int w = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  int* buf = red_buf(red, parity);
+  if (lane_id() == 63) buf[w] = x;
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
@@ -174,23 +227,35 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* red, int&
   return before + x - v;
 }
 
+// Bits of the key a step of the bucket search resolves: every wave but the first counts the
+// bucket against one of the 2^bits - 1 thresholds of the step.
+constexpr int kStepBits = kFinalWaves >= 16 ? 4 : kFinalWaves >= 8 ? 3 : kFinalWaves >= 4 ? 2 : 1;
+
 // Exact top-k (1 <= k <= number of real keys) of up to kFinalThreads * E keys held in
 // registers: thread t holds elements t*E .. t*E+E-1 (keys kv, values vv; elements past the
 // end hold the sentinel key).  Writes the values of the chosen elements, in element order,
-// to out[0..k) (LDS) and returns the k-th element's key (*K_out) and value (*I_out).
+// to out[0..k) (LDS) and returns the k-th element's key and value.
 //
-// K (the k-th largest key) is found one bit at a time as the largest T with #{keys >= T} >=
-// k, by the whole workgroup (one barrier per bit) while the keys still in play are many.
-// The counts already give the size of the remaining bucket [K, K_hi) (#{>= K} - #{>= K_hi});
-// once it holds at most kBucketMax keys they are compacted to LDS and one wave resolves the
-// remaining bits with no barriers (#{>= T} = #{>= K_hi} + #{bucket keys >= T}).  Every T
+// K, the k-th largest key, is the largest T with #{keys >= T} >= k.  All real keys share the
+// bits of their maximum and minimum above the highest bit where those differ, so the search
+// starts below it with the bracket [K, K_hi) around every key.  While many keys are in play
+// the whole workgroup settles one bit per exchange; the counts give the number of keys left
+// in [K, K_hi) (#{>= K} - #{>= K_hi}), and once at most kBucketMax remain they are compacted
+// to LDS and every wave loads them: a step then tries 2^kStepBits - 1 thresholds at once
+// (one per wave, #{>= T} = #{>= K_hi} + #{bucket keys >= T}) and settles kStepBits bits per
+// exchange, ending early when one key is left in the bracket (it is the k-th).  Every T
 // tried is >= 1, so sentinels never count.
-// red: >= 2 * kFinalWaves ints of LDS (16-byte aligned); note: 1 int; bucket: kBucketMax.
+// red: 4 * kFinalWaves ints of LDS (16-byte aligned); note: 1 int; bucket: kBucketMax.
+struct KthKey {
+  uint32_t key;
+  int idx;
+};
+
 template <int E>
-__device__ void block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int k, int* out,
-                                int* red, int* note, uint32_t* bucket, uint32_t* K_out,
-                                int* I_out) {
+__device__ KthKey block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int k, int* out,
+                                  int* red, int* note, uint32_t* bucket) {
   const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int parity = 0;
   // this wave's #{keys > T} (strict) or #{keys >= T}, wave-uniform (vector counts in four
   // accumulators, then one DPP reduction)
@@ -205,10 +270,28 @@ __device__ void block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int
     }
     return wave_sum((c0 + c1) + (c2 + c3));
   };
-  uint32_t K = 0, K_hi = 0;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    mx = max(mx, kv[j]);
+    mn = min(mn, kv[j] == kSentinel ? 0xFFFFFFFFu : kv[j]);
+  }
+  block_max_min(mx, mn, red, parity);
+  uint32_t K = mx, K_hi = 0u;
   bool has_hi = false;
   int c_K = kFinalThreads * E, c_hi = 0;  // #{>= K} (an upper bound until K moves), #{>= K_hi}
-  int bit = 31;
+  int bit = -1;                           // mx == mn: every real key is the k-th
+  if (mx != mn) {
+    bit = 31 - __builtin_clz(mx ^ mn);
+    if (bit < 31) {
+      const uint32_t span = 2u << bit;
+      K = mx & ~(span - 1u);
+      K_hi = K + span;
+      has_hi = K_hi != 0u;  // (every key is below K_hi: c_hi = 0)
+    } else {
+      K = 0u;
+    }
+  }
 #pragma unroll 1
   for (; bit >= 0; --bit) {
     const uint32_t T = K | (1u << bit);
@@ -226,6 +309,7 @@ __device__ void block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int
       break;
     }
   }
+  int r;  // equal keys taken (>= 1)
   if (bit >= 0) {
     const uint32_t lo = K > 1u ? K : 1u;
     auto in_bucket = [&](uint32_t x) { return x >= lo && (!has_hi || x < K_hi); };
@@ -238,39 +322,83 @@ __device__ void block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int
     for (int j = 0; j < E; ++j)
       if (in_bucket(kv[j])) bucket[at++] = kv[j];
     __syncthreads();
-    if (tid < 64) {
-      constexpr int BE = kBucketMax / 64;
-      uint32_t bk[BE];
+    constexpr int BE = kBucketMax / 64;
+    uint32_t bk[BE];
 #pragma unroll
-      for (int j = 0; j < BE; ++j) {
-        const int e = lane * BE + j;
-        bk[j] = e < n_bucket ? bucket[e] : kSentinel;
-      }
-#pragma unroll 1
-      for (; bit >= 0; --bit) {
-        const uint32_t T = K | (1u << bit);
-        int c = c_hi;
-#pragma unroll
-        for (int j = 0; j < BE; ++j) c += __popcll(__ballot(bk[j] >= T));
-        if (c >= k) K = T;
-      }
-      if (tid == 0) *note = (int)K;
+    for (int j = 0; j < BE; ++j) {
+      const int e = 64 * j + lane;
+      bk[j] = e < n_bucket ? bucket[e] : kSentinel;
     }
-    __syncthreads();
-    K = (uint32_t)*note;
+    const int c_hi0 = c_hi;
+    auto bcount = [&](uint32_t T, bool strict) {
+      int c = c_hi0;
+#pragma unroll
+      for (int j = 0; j < BE; ++j) c += __popcll(__ballot(strict ? bk[j] > T : bk[j] >= T));
+      return c;
+    };
+#pragma unroll 1
+    while (bit >= 0) {  // uniform
+      if (c_K - c_hi == 1) {
+        // one key in [K, K_hi) (c_K, even as a bound, is then exact): it is the k-th
+        const uint32_t lo2 = K > 1u ? K : 1u;
+        uint32_t x = K;
+#pragma unroll
+        for (int j = 0; j < BE; ++j) {
+          const uint64_t m = __ballot(bk[j] >= lo2 && (!has_hi || bk[j] < K_hi));
+          if (m) x = (uint32_t)__builtin_amdgcn_readlane((int)bk[j], (int)__builtin_ctzll(m));
+        }
+        K = x;
+        break;
+      }
+      const int d = bit + 1 < kStepBits ? bit + 1 : kStepBits;
+      const int sh = bit + 1 - d;
+      const int n_t = (1 << d) - 1;
+      int* buf = red_buf(red, parity);
+      if (w >= 1 && w <= n_t) {
+        const int c = bcount(K | ((uint32_t)w << sh), false);
+        if (lane == 0) buf[w] = c;
+      }
+      __syncthreads();
+      int cs[kFinalWaves];
+#pragma unroll
+      for (int j = 1; j < kFinalWaves; ++j) cs[j] = j <= n_t ? buf[j] : -1;  // -1 < k
+      int digit = 0, c_dig = c_K, c_next = c_hi;
+#pragma unroll
+      for (int j = 1; j < kFinalWaves; ++j) {
+        if (cs[j] >= k) {  // counts fall as j grows
+          digit = j;
+          c_dig = cs[j];
+        }
+      }
+#pragma unroll
+      for (int j = 1; j < kFinalWaves; ++j)
+        if (j == digit + 1 && j <= n_t) c_next = cs[j];
+      if (digit + 1 <= n_t) {
+        K_hi = K | ((uint32_t)(digit + 1) << sh);
+        has_hi = true;
+        c_hi = c_next;
+      }
+      K |= (uint32_t)digit << sh;
+      c_K = c_dig;
+      bit -= d;
+    }
+    r = k - bcount(K, true);
+  } else {
+    r = k - block_sum_waves(count(K, true), red, parity);
   }
-  const int r = k - block_sum_waves(count(K, true), red, parity);  // equal keys taken (>= 1)
-  if (tid == 0) *note = -1;
+  // one scan of (#{> K}, #{== K}) per thread (each field stays below 2^16): equal keys are
+  // taken in element order until r of them are, so the output position is the keys above K
+  // before this thread plus min(equal keys before it, r)
   int n_eq = 0, n_gt = 0;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     n_eq += kv[j] == K ? 1 : 0;
     n_gt += kv[j] > K ? 1 : 0;
   }
-  int eq_tot, take_tot;
-  const int eq_before = block_excl_scan(n_eq, &eq_tot, red, parity);
-  const int eq_take = min(max(r - eq_before, 0), n_eq);
-  int pos = block_excl_scan(n_gt + eq_take, &take_tot, red, parity);
+  int tot;
+  const int before = block_excl_scan(n_gt | (n_eq << 16), &tot, red, parity);
+  const int eq_before = before >> 16;
+  int pos = (before & 0xFFFF) + min(eq_before, r);
   int e_rank = eq_before;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
@@ -283,9 +411,9 @@ __device__ void block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int
     if (take) out[pos++] = vv[j];
   }
   __syncthreads();
-  *K_out = K;
-  *I_out = *note;
+  const int I = *note;
   __syncthreads();
+  return KthKey{K, I};
 }
 
 // Smallest per-thread count E in {8, 16, 32} with kFinalThreads * E >= n.
@@ -297,8 +425,8 @@ __host__ __device__ __forceinline__ int final_per_thread(int n) {
 // kFinalTile elements go through registers, more are re-read tile by tile (slow; only the
 // exact fallbacks of the final pass come here).
 template <int E, class Get, class Val>
-__device__ void block_topk_e(const Get& get, const Val& val, int n, int k, int* out, int* red,
-                             int* note, uint32_t* bucket, uint32_t* K_out, int* I_out) {
+__device__ KthKey block_topk_e(Get get, Val val, int n, int k, int* out, int* red, int* note,
+                               uint32_t* bucket) {
   const int tid = threadIdx.x;
   uint32_t kv[E];
   int vv[E];
@@ -308,18 +436,19 @@ __device__ void block_topk_e(const Get& get, const Val& val, int n, int k, int* 
     kv[j] = e < n ? get(e) : kSentinel;
     vv[j] = e < n ? val(e) : 0;
   }
-  block_topk_regs<E>(kv, vv, k, out, red, note, bucket, K_out, I_out);
+  return block_topk_regs<E>(kv, vv, k, out, red, note, bucket);
 }
 
+// (get / val are taken by value: they hold a pointer or two, and the slow path is a call.)
 template <class Get, class Val>
-__device__ void block_topk(const Get& get, const Val& val, int n, int k, int* out, int* red,
-                           int* note, uint32_t* bucket, uint32_t* K_out, int* I_out) {
+__device__ KthKey block_topk(Get get, Val val, int n, int k, int* out, int* red, int* note,
+                             uint32_t* bucket) {
   const int tid = threadIdx.x;
   if (n <= kFinalTile) {
     switch (final_per_thread(n)) {
-      case 8: block_topk_e<8>(get, val, n, k, out, red, note, bucket, K_out, I_out); return;
-      case 16: block_topk_e<16>(get, val, n, k, out, red, note, bucket, K_out, I_out); return;
-      default: block_topk_e<32>(get, val, n, k, out, red, note, bucket, K_out, I_out); return;
+      case 8: return block_topk_e<8>(get, val, n, k, out, red, note, bucket);
+      case 16: return block_topk_e<16>(get, val, n, k, out, red, note, bucket);
+      default: return block_topk_e<32>(get, val, n, k, out, red, note, bucket);
     }
   }
   constexpr int E = 16;  // tile of the re-read path
@@ -378,9 +507,9 @@ __device__ void block_topk(const Get& get, const Val& val, int n, int k, int* ou
     if (out_base >= k) break;  // uniform
   }
   __syncthreads();
-  *K_out = K;
-  *I_out = *note;
+  const int I = *note;
   __syncthreads();
+  return KthKey{K, I};
 }
 
 }  // namespace dsa

@@ -1,0 +1,223 @@
+// Pass 2 of the exact top-k (see topk.hip) as a function of one workgroup of kFinalThreads
+// threads and one query row, so that the standalone final kernel and the fused
+// select-and-attend kernel run the same code.
+#pragma once
+
+#include <type_traits>
+
+#include "dsa_device.hpp"
+#include "dsa_select.hpp"
+
+namespace dsa {
+
+constexpr int kMaxTopk = 4096;
+
+// Request and absolute position of query row `row`: one wave-wide ballot over cu_q per 64
+// requests (rows are grouped by request and are its last tokens).
+__device__ __forceinline__ void row_of(const int32_t* cu_q, const int32_t* seq_lens, int num_seqs,
+                                       int row, int& b, int& pos) {
+  const int lane = lane_id();
+  int count = 0;
+  for (int base = 0; base < num_seqs; base += 64) {  // uniform loop
+    const int i = base + lane;
+    const bool le = i < num_seqs && cu_q[i] <= row;
+    count += __popcll(__ballot(le));
+  }
+  b = count - 1;
+  const int c0 = cu_q[b], c1 = cu_q[b + 1];
+  pos = seq_lens[b] - (c1 - c0) + (row - c0);
+}
+
+// Copies, in element order, every element of get(0 .. n-1) whose key is >= K into
+// lkey / lidx (key, element index) while they fit in kFinalTile slots.  Returns the number of
+// such elements (more than kFinalTile: the copy is incomplete).
+template <class Get>
+__device__ int gather_at_least(const Get& get, int n, uint32_t K, uint32_t* lkey, int32_t* lidx,
+                               int* red, int& parity) {
+  const int tid = threadIdx.x;
+  constexpr int E = 16;
+  constexpr int kTile = kFinalThreads * E;
+  int kept = 0;
+#pragma unroll 1
+  for (int base = 0; base < n; base += kTile) {
+    uint32_t tk[E];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = base + tid * E + j;
+      tk[j] = e < n ? get(e) : kSentinel;
+      c += tk[j] >= K ? 1 : 0;
+    }
+    int tot;
+    int pos = kept + block_excl_scan(c, &tot, red, parity);
+    if (kept + tot <= kFinalTile) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if (tk[j] >= K) {
+          lkey[pos] = tk[j];
+          lidx[pos] = base + tid * E + j;
+          ++pos;
+        }
+      }
+    }
+    kept += tot;
+    if (kept > kFinalTile) break;  // uniform
+  }
+  __syncthreads();
+  return kept;
+}
+
+// LDS the final pass needs besides its output: the on-chip candidate tile (keys, token
+// indices), the reduction scratch and the last search bucket.
+struct FinalScratch {
+  uint32_t* lkey;   // kFinalTile
+  int32_t* lidx;    // kFinalTile
+  int* red;         // 4 * kFinalWaves, 16-byte aligned
+  int* note;        // 1
+  uint32_t* bucket; // kBucketMax
+};
+
+// The exact top k (token order) of row `row` (request position pos, n_vis = pos + 1 visible
+// tokens) from its group candidates, resending flagged groups from the scores.  Writes the
+// selected token indices to out[0 .. n_out) (LDS, kMaxTopk entries) and returns n_out =
+// min(k, n_vis).  Ends with a barrier, so out[] is visible to the whole workgroup.
+__device__ inline int final_select_row(int row, int n_vis, const float* __restrict__ scores,
+                                int64_t score_stride, int k, int num_groups, int64_t row_cap,
+                                const uint32_t* __restrict__ cand_key,
+                                const int32_t* __restrict__ cand_idx,
+                                const ChunkInfo* __restrict__ info, int* out,
+                                const FinalScratch& sc) {
+  const int tid = threadIdx.x;
+  uint32_t* lkey = sc.lkey;
+  int32_t* lidx = sc.lidx;
+  int* red = sc.red;
+  int* note_p = sc.note;
+  uint32_t* bucket = sc.bucket;
+  const float* src = scores + (int64_t)row * score_stride;
+  auto score_get = [src](int i) { return score_key(src[i]); };
+  auto ident = [](int i) { return i; };
+  int n_out;
+  if (n_vis <= k) {
+    for (int i = tid; i < n_vis; i += kFinalThreads) out[i] = i;
+    n_out = n_vis;
+  } else {
+    const int n_groups = (n_vis + kGroupTok - 1) / kGroupTok;
+    const int m = group_cand_count(n_vis, k);
+    const int n_cand = n_groups * m;
+    const uint32_t* ck = cand_key + (int64_t)row * row_cap;
+    const int32_t* ci = cand_idx + (int64_t)row * row_cap;
+    const ChunkInfo* inf = info + (int64_t)row * num_groups;
+    // this thread's first group record, loaded now so that the flag check after the
+    // selection does not wait for it
+    const ChunkInfo info0 = inf[min(tid, n_groups - 1)];
+    KthKey kth;
+    if (n_cand <= kFinalTile) {
+      // this thread's E consecutive candidates straight into registers (n_cand and the
+      // row's slots are multiples of 4 and 16-byte aligned)
+      auto run = [&](auto e_tag) {
+        constexpr int E = decltype(e_tag)::value;
+        uint32_t kv[E];
+        int vv[E];
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const int e = tid * E + 4 * q;
+          v4i a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
+          if (e < n_cand) {
+            a = *reinterpret_cast<const v4i*>(ck + e);
+            c = *reinterpret_cast<const v4i*>(ci + e);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kv[4 * q + j] = (uint32_t)a[j];
+            vv[4 * q + j] = c[j];
+          }
+        }
+        kth = block_topk_regs<E>(kv, vv, k, out, red, note_p, bucket);
+      };
+      switch (final_per_thread(n_cand)) {
+        case 8: run(std::integral_constant<int, 8>()); break;
+        case 16: run(std::integral_constant<int, 16>()); break;
+        default: run(std::integral_constant<int, 32>()); break;
+      }
+    } else {
+      kth = block_topk([ck](int i) { return ck[i]; }, [ci](int i) { return ci[i]; }, n_cand, k,
+                       out, red, note_p, bucket);
+    }
+    const uint32_t K = kth.key;
+    const int I = kth.idx;
+    // groups whose m-th element beats the k-th selected may hide winners
+    auto flag_of = [&](const ChunkInfo& ic) {
+      return ic.saturated && (ic.key > K || (ic.key == K && ic.idx < I));
+    };
+    auto flagged = [&](int g) { return flag_of(inf[g]); };
+    int any = tid < n_groups && flag_of(info0) ? 1 : 0;
+#pragma unroll 4
+    for (int g = tid + kFinalThreads; g < n_groups; g += kFinalThreads) any |= flagged(g) ? 1 : 0;
+    int parity = 0;
+    if (block_sum(any, red, parity) > 0) {
+      // Rebuild the candidate list in token order, flagged groups in full and the others as
+      // sent: group starts go to LDS (`out` is free until the next selection), then every
+      // thread fills its own elements, locating each one's group by binary search.
+      int total = 0;
+      if (n_groups <= kMaxTopk) {
+        constexpr int GPT = kMaxTopk / kFinalThreads;  // groups per thread
+        int len[GPT], sum = 0;
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+          const int g = GPT * tid + q;
+          len[q] = g >= n_groups ? 0
+                                 : (flagged(g) ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
+          sum += len[q];
+        }
+        int at = block_excl_scan(sum, &total, red, parity);
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+          const int g = GPT * tid + q;
+          if (g < n_groups) out[g] = at;  // every group has >= 1 element: starts increase
+          at += len[q];
+        }
+      } else {
+        total = kFinalTile + 1;
+      }
+      __syncthreads();
+      if (total <= kFinalTile) {
+#pragma unroll 8
+        for (int e = tid; e < total; e += kFinalThreads) {
+          int lo = 0, hi = n_groups - 1;  // the last group starting at or before e
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (out[mid] <= e) lo = mid;
+            else hi = mid - 1;
+          }
+          const int i = e - out[lo];
+          if (flagged(lo)) {
+            const int t = lo * kGroupTok + i;
+            lkey[e] = score_key(src[t]);
+            lidx[e] = t;
+          } else {
+            lkey[e] = ck[(int64_t)lo * m + i];
+            lidx[e] = ci[(int64_t)lo * m + i];
+          }
+        }
+        __syncthreads();
+        block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, total, k,
+                   out, red, note_p, bucket);
+      } else {
+        // Too many to hold: every winner has a key >= K (the candidates' k-th is a lower
+        // bound of the true k-th), so keep those, in token order, if they fit on chip.
+        const int kept = gather_at_least(score_get, n_vis, K, lkey, lidx, red, parity);
+        if (kept <= kFinalTile) {
+          block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
+                     k, out, red, note_p, bucket);
+        } else {
+          block_topk(score_get, ident, n_vis, k, out, red, note_p, bucket);
+        }
+      }
+    }
+    n_out = k;
+  }
+  __syncthreads();
+  return n_out;
+}
+
+}  // namespace dsa

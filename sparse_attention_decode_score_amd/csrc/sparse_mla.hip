@@ -30,6 +30,8 @@
 // which keeps about 8 significant bits through the value product.
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
+#include "dsa_select.hpp"
+#include "dsa_topk_final.hpp"
 
 namespace dsa {
 
@@ -58,20 +60,63 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (fp32, or fp16 divided by the latent scale, which bounds it by 448) and LSE.
 enum PartMode { kDirect = 0, kPartF32 = 1, kPartF16 = 2 };
 
+struct MlaSmem {
+  uint8_t lat[2][kTile * kRowStride];
+  uint8_t q8s[kMlaHeads * kRowStride];
+  uint8_t pbuf[3][2][32][64];  // [head tile][hi/lo][head][token]
+  float xmax[3][2][32];
+  float xfer[6][32];
+  float qsc[kMlaHeads];
+  int32_t slot_l[kSlotsLds];
+  uint64_t valid_mask[2];
+};
+// The final top-k pass of the fused kernel runs before any of the above is used: its
+// scratch overlays the latent ring, the query and the probability buffers, and its output
+// (the row's selected token indices) is written straight into slot_l.
+struct SelectSmem {
+  uint32_t lkey[kFinalTile];
+  int32_t lidx[kFinalTile];
+  alignas(16) int red[4 * kFinalWaves];
+  int note;
+  uint32_t bucket[kBucketMax];
+};
+static_assert(sizeof(SelectSmem) <= offsetof(MlaSmem, slot_l), "selection scratch overlaps slot_l");
+static_assert(kFinalThreads == kThreads, "the fused kernel runs the final pass on its own threads");
+
+// Inputs of the fused final top-k pass (stage 2) of the select-and-attend kernel.
+struct SelectArgs {
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  int num_seqs;
+  const float* scores;
+  int64_t score_stride;
+  int num_groups;
+  int64_t row_cap;
+  const uint32_t* cand_key;
+  const int32_t* cand_idx;
+  const ChunkInfo* info;
+  const int32_t* block_table;
+  int bt_stride;
+  int32_t* topk_idx;   // optional outputs, written by split 0 of each row
+  int32_t* topk_slot;
+};
+
+template <bool SELECT>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ q8_in,
+    SelectArgs sel, const uint16_t* __restrict__ q, const uint8_t* __restrict__ q8_in,
     const float* __restrict__ qs_in, const uint8_t* __restrict__ lat_pages, int64_t page_stride,
     float lat_scale, const int32_t* __restrict__ topk_slot, int k, float sm_scale,
     int num_splits, int n_q, int mode, void* __restrict__ o_part, float* __restrict__ lse_part,
     uint16_t* __restrict__ out_bf16, float* __restrict__ lse_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lat[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint8_t q8s[kMlaHeads * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[3][2][32][64];  // [head tile][hi/lo][head][token]
-  __shared__ __attribute__((aligned(16))) float xmax[3][2][32];
-  __shared__ __attribute__((aligned(16))) float xfer[6][32];
-  __shared__ __attribute__((aligned(16))) float qsc[kMlaHeads];
-  __shared__ int32_t slot_l[kSlotsLds];
-  __shared__ uint64_t valid_mask[2];
+  __shared__ __attribute__((aligned(16))) MlaSmem sm;
+  auto& lat = sm.lat;
+  auto& q8s = sm.q8s;
+  auto& pbuf = sm.pbuf;
+  auto& xmax = sm.xmax;
+  auto& xfer = sm.xfer;
+  auto& qsc = sm.qsc;
+  auto& slot_l = sm.slot_l;
+  auto& valid_mask = sm.valid_mask;
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; when the grid divides
   // evenly, all splits of a row go to one XCD, so the row's query (read by every split)
@@ -93,11 +138,46 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
-  const int32_t* slots = topk_slot + (int64_t)row * k + beg;
 
-  // the split's slot list -> LDS (barrier 0)
-  for (int i = threadIdx.x; i < n_tok; i += kThreads) slot_l[i] = slots[i];
-  __syncthreads();
+  if constexpr (SELECT) {
+    // stage 2 for this row (every split of the row runs it: it is latency-bound), then the
+    // split's slice of the selected tokens -> physical slots in slot_l
+    SelectSmem& ss = *reinterpret_cast<SelectSmem*>(&sm);
+    int b, pos;
+    row_of(sel.cu_q, sel.seq_lens, sel.num_seqs, row, b, pos);
+    const FinalScratch sc{ss.lkey, ss.lidx, ss.red, &ss.note, ss.bucket};
+    const int n_out = final_select_row(row, pos + 1, sel.scores, sel.score_stride, k,
+                                       sel.num_groups, sel.row_cap, sel.cand_key, sel.cand_idx,
+                                       sel.info, slot_l, sc);
+    const int32_t* bt = sel.block_table + (int64_t)b * sel.bt_stride;
+    auto to_slot = [&](int t) { return t < 0 ? -1 : bt[t >> 6] * kPage + (t & (kPage - 1)); };
+    if (s == 0 && (sel.topk_idx || sel.topk_slot)) {
+      for (int i = threadIdx.x; i < k; i += kThreads) {
+        const int t = i < n_out ? slot_l[i] : -1;
+        if (sel.topk_idx) sel.topk_idx[(int64_t)row * k + i] = t;
+        if (sel.topk_slot) sel.topk_slot[(int64_t)row * k + i] = to_slot(t);
+      }
+    }
+    constexpr int kPer = kSlotsLds / kThreads;
+    int mine[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = threadIdx.x + u * kThreads;
+      mine[u] = (j < n_tok && beg + j < n_out) ? to_slot(slot_l[beg + j]) : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = threadIdx.x + u * kThreads;
+      if (j < n_tok) slot_l[j] = mine[u];
+    }
+    __syncthreads();  // barrier 0: the selection scratch is dead, slot_l holds the split's slots
+  } else {
+    // the split's slot list -> LDS (barrier 0)
+    const int32_t* slots = topk_slot + (int64_t)row * k + beg;
+    for (int i = threadIdx.x; i < n_tok; i += kThreads) slot_l[i] = slots[i];
+    __syncthreads();
+  }
   auto slot_of = [&](int j) { return j < n_tok ? slot_l[j] : -1; };
 
   if (wave >= 6) {
@@ -404,11 +484,13 @@ size_t sparse_mla_workspace_bytes(int n_q, int num_splits) {
   return align256(parts * kVDim * sizeof(uint16_t)) + align256(parts * sizeof(float));
 }
 
-hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, const float* q_scale,
-                             const uint8_t* latent_pages, int64_t latent_page_stride,
-                             float latent_scale, const int32_t* topk_slot, int k,
-                             float softmax_scale, int num_splits, float* o_part, float* lse_part,
-                             uint16_t* out_bf16, float* lse, void* workspace, hipStream_t st) {
+static hipError_t launch_mla_common(const SelectArgs* sel, int n_q, const uint16_t* q,
+                                    const uint8_t* q8, const float* q_scale,
+                                    const uint8_t* latent_pages, int64_t latent_page_stride,
+                                    float latent_scale, const int32_t* topk_slot, int k,
+                                    float softmax_scale, int num_splits, float* o_part,
+                                    float* lse_part, uint16_t* out_bf16, float* lse,
+                                    void* workspace, hipStream_t st) {
   int mode = kDirect;
   void* op = o_part;
   float* lp = lse_part;
@@ -421,13 +503,47 @@ hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, cons
     lp = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                   align256(parts * kVDim * sizeof(uint16_t)));
   }
-  hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)num_splits, (unsigned)n_q), dim3(kThreads), 0,
-                     st, q, q8, q_scale, latent_pages, latent_page_stride, latent_scale, topk_slot,
-                     k, softmax_scale, num_splits, n_q, mode, op, lp, out_bf16, lse);
+  const dim3 grid((unsigned)num_splits, (unsigned)n_q), block(kThreads);
+  if (sel) {
+    hipLaunchKernelGGL(sparse_mla_kernel<true>, grid, block, 0, st, *sel, q, q8, q_scale,
+                       latent_pages, latent_page_stride, latent_scale, topk_slot, k,
+                       softmax_scale, num_splits, n_q, mode, op, lp, out_bf16, lse);
+  } else {
+    hipLaunchKernelGGL(sparse_mla_kernel<false>, grid, block, 0, st, SelectArgs{}, q, q8,
+                       q_scale, latent_pages, latent_page_stride, latent_scale, topk_slot, k,
+                       softmax_scale, num_splits, n_q, mode, op, lp, out_bf16, lse);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode != kPartF16) return e;
   return launch_lse_combine_f16(num_splits, n_q, static_cast<const uint16_t*>(op), lp,
                                 latent_scale, out_bf16, lse, st);
+}
+
+hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, const float* q_scale,
+                             const uint8_t* latent_pages, int64_t latent_page_stride,
+                             float latent_scale, const int32_t* topk_slot, int k,
+                             float softmax_scale, int num_splits, float* o_part, float* lse_part,
+                             uint16_t* out_bf16, float* lse, void* workspace, hipStream_t st) {
+  return launch_mla_common(nullptr, n_q, q, q8, q_scale, latent_pages, latent_page_stride,
+                           latent_scale, topk_slot, k, softmax_scale, num_splits, o_part,
+                           lse_part, out_bf16, lse, workspace, st);
+}
+
+hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
+                                  const int32_t* seq_lens, const float* scores,
+                                  int64_t score_stride, const TopkBuffers& t,
+                                  const int32_t* block_table, int bt_stride, int32_t* topk_idx,
+                                  int32_t* topk_slot, const uint16_t* q, const uint8_t* q8,
+                                  const float* q_scale, const uint8_t* latent_pages,
+                                  int64_t latent_page_stride, float latent_scale, int k,
+                                  float softmax_scale, int num_splits, uint16_t* out_bf16,
+                                  float* lse, void* workspace, hipStream_t st) {
+  const SelectArgs sel{cu_q, seq_lens, num_seqs, scores, score_stride, t.plan.num_groups,
+                       (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info, block_table,
+                       bt_stride, topk_idx, topk_slot};
+  return launch_mla_common(&sel, n_q, q, q8, q_scale, latent_pages, latent_page_stride,
+                           latent_scale, nullptr, k, softmax_scale, num_splits, nullptr, nullptr,
+                           out_bf16, lse, workspace, st);
 }
 
 }  // namespace dsa

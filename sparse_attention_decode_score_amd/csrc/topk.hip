@@ -24,28 +24,11 @@
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
 #include "dsa_select.hpp"
+#include "dsa_topk_final.hpp"
 
 namespace dsa {
 
 namespace {
-
-constexpr int kMaxTopk = 4096;
-
-// Request and absolute position of query row `row`: one wave-wide ballot over cu_q per 64
-// requests (rows are grouped by request and are its last tokens).
-__device__ __forceinline__ void row_of(const int32_t* cu_q, const int32_t* seq_lens, int num_seqs,
-                                       int row, int& b, int& pos) {
-  const int lane = lane_id();
-  int count = 0;
-  for (int base = 0; base < num_seqs; base += 64) {  // uniform loop
-    const int i = base + lane;
-    const bool le = i < num_seqs && cu_q[i] <= row;
-    count += __popcll(__ballot(le));
-  }
-  b = count - 1;
-  const int c0 = cu_q[b], c1 = cu_q[b + 1];
-  pos = seq_lens[b] - (c1 - c0) + (row - c0);
-}
 
 // ---------------------------------------------------------------- pass 1 from stored scores
 // grid (ceil(groups / 4), n_q), 4 waves: wave w takes group 4 * blockIdx.x + w of the row.
@@ -73,45 +56,6 @@ __global__ __launch_bounds__(256) void topk_group_kernel(
                info + (int64_t)row * num_groups + g);
 }
 
-// Copies, in element order, every element of get(0 .. n-1) whose key is >= K into
-// lkey / lidx (key, element index) while they fit in kFinalTile slots.  Returns the number of
-// such elements (more than kFinalTile: the copy is incomplete).
-template <class Get>
-__device__ int gather_at_least(const Get& get, int n, uint32_t K, uint32_t* lkey, int32_t* lidx,
-                               int* red, int& parity) {
-  const int tid = threadIdx.x;
-  constexpr int E = 16;
-  constexpr int kTile = kFinalThreads * E;
-  int kept = 0;
-#pragma unroll 1
-  for (int base = 0; base < n; base += kTile) {
-    uint32_t tk[E];
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int e = base + tid * E + j;
-      tk[j] = e < n ? get(e) : kSentinel;
-      c += tk[j] >= K ? 1 : 0;
-    }
-    int tot;
-    int pos = kept + block_excl_scan(c, &tot, red, parity);
-    if (kept + tot <= kFinalTile) {
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        if (tk[j] >= K) {
-          lkey[pos] = tk[j];
-          lidx[pos] = base + tid * E + j;
-          ++pos;
-        }
-      }
-    }
-    kept += tot;
-    if (kept > kFinalTile) break;  // uniform
-  }
-  __syncthreads();
-  return kept;
-}
-
 // ---------------------------------------------------------------- pass 2
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int num_seqs,
@@ -122,7 +66,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t lkey[kFinalTile];
   __shared__ __attribute__((aligned(16))) int32_t lidx[kFinalTile];
   __shared__ int out[kMaxTopk];
-  __shared__ __attribute__((aligned(16))) int red[2 * kFinalWaves];
+  __shared__ __attribute__((aligned(16))) int red[4 * kFinalWaves];
   __shared__ int note;
   __shared__ uint32_t bucket[kBucketMax];
   const int row = blockIdx.x, tid = threadIdx.x;
@@ -132,127 +76,9 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   int32_t* oi = topk_idx + (int64_t)row * k;
   int32_t* os = topk_slot ? topk_slot + (int64_t)row * k : nullptr;
   const int32_t* bt = block_table ? block_table + (int64_t)b * bt_stride : nullptr;
-  const float* src = scores + (int64_t)row * score_stride;
-  auto score_get = [&](int i) { return score_key(src[i]); };
-  auto ident = [](int i) { return i; };
-
-  int n_out;
-  if (n_vis <= k) {
-    for (int i = tid; i < n_vis; i += kFinalThreads) out[i] = i;
-    n_out = n_vis;
-  } else {
-    const int n_groups = (n_vis + kGroupTok - 1) / kGroupTok;
-    const int m = group_cand_count(n_vis, k);
-    const int n_cand = n_groups * m;
-    const uint32_t* ck = cand_key + (int64_t)row * row_cap;
-    const int32_t* ci = cand_idx + (int64_t)row * row_cap;
-    const ChunkInfo* inf = info + (int64_t)row * num_groups;
-    uint32_t K;
-    int I;
-    if (n_cand <= kFinalTile) {
-      // this thread's E consecutive candidates straight into registers (n_cand and the
-      // row's slots are multiples of 4 and 16-byte aligned)
-      auto run = [&](auto e_tag) {
-        constexpr int E = decltype(e_tag)::value;
-        uint32_t kv[E];
-        int vv[E];
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-          const int e = tid * E + 4 * q;
-          v4i a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-          if (e < n_cand) {
-            a = *reinterpret_cast<const v4i*>(ck + e);
-            c = *reinterpret_cast<const v4i*>(ci + e);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            kv[4 * q + j] = (uint32_t)a[j];
-            vv[4 * q + j] = c[j];
-          }
-        }
-        block_topk_regs<E>(kv, vv, k, out, red, &note, bucket, &K, &I);
-      };
-      switch (final_per_thread(n_cand)) {
-        case 8: run(std::integral_constant<int, 8>()); break;
-        case 16: run(std::integral_constant<int, 16>()); break;
-        default: run(std::integral_constant<int, 32>()); break;
-      }
-    } else {
-      block_topk([&](int i) { return ck[i]; }, [&](int i) { return ci[i]; }, n_cand, k, out, red,
-                 &note, bucket, &K, &I);
-    }
-    // groups whose m-th element beats the k-th selected may hide winners
-    auto flagged = [&](int g) {
-      const ChunkInfo ic = inf[g];
-      return ic.saturated && (ic.key > K || (ic.key == K && ic.idx < I));
-    };
-    int any = 0;
-#pragma unroll 4
-    for (int g = tid; g < n_groups; g += kFinalThreads) any |= flagged(g) ? 1 : 0;
-    int parity = 0;
-    if (block_sum(any, red, parity) > 0) {
-      // Rebuild the candidate list in token order, flagged groups in full and the others as
-      // sent: group starts go to LDS (`out` is free until the next selection), then every
-      // thread fills its own elements, locating each one's group by binary search.
-      int total = 0;
-      if (n_groups <= kMaxTopk) {
-        constexpr int GPT = kMaxTopk / kFinalThreads;  // groups per thread
-        int len[GPT], sum = 0;
-#pragma unroll
-        for (int q = 0; q < GPT; ++q) {
-          const int g = GPT * tid + q;
-          len[q] = g >= n_groups ? 0
-                                 : (flagged(g) ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
-          sum += len[q];
-        }
-        int at = block_excl_scan(sum, &total, red, parity);
-#pragma unroll
-        for (int q = 0; q < GPT; ++q) {
-          const int g = GPT * tid + q;
-          if (g < n_groups) out[g] = at;  // every group has >= 1 element: starts increase
-          at += len[q];
-        }
-      } else {
-        total = kFinalTile + 1;
-      }
-      __syncthreads();
-      if (total <= kFinalTile) {
-#pragma unroll 8
-        for (int e = tid; e < total; e += kFinalThreads) {
-          int lo = 0, hi = n_groups - 1;  // the last group starting at or before e
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (out[mid] <= e) lo = mid;
-            else hi = mid - 1;
-          }
-          const int i = e - out[lo];
-          if (flagged(lo)) {
-            const int t = lo * kGroupTok + i;
-            lkey[e] = score_key(src[t]);
-            lidx[e] = t;
-          } else {
-            lkey[e] = ck[(int64_t)lo * m + i];
-            lidx[e] = ci[(int64_t)lo * m + i];
-          }
-        }
-        __syncthreads();
-        block_topk([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, total, k,
-                   out, red, &note, bucket, &K, &I);
-      } else {
-        // Too many to hold: every winner has a key >= K (the candidates' k-th is a lower
-        // bound of the true k-th), so keep those, in token order, if they fit on chip.
-        const int kept = gather_at_least(score_get, n_vis, K, lkey, lidx, red, parity);
-        if (kept <= kFinalTile) {
-          block_topk([&](int i) { return lkey[i]; }, [&](int i) { return lidx[i]; }, kept, k,
-                     out, red, &note, bucket, &K, &I);
-        } else {
-          block_topk(score_get, ident, n_vis, k, out, red, &note, bucket, &K, &I);
-        }
-      }
-    }
-    n_out = k;
-  }
-  __syncthreads();
+  FinalScratch sc{lkey, lidx, red, &note, bucket};
+  const int n_out = final_select_row(row, n_vis, scores, score_stride, k, num_groups, row_cap,
+                                     cand_key, cand_idx, info, out, sc);
 #pragma unroll 8
   for (int i = tid; i < k; i += kFinalThreads) {
     const int t = i < n_out ? out[i] : -1;

@@ -248,7 +248,9 @@ def random_scores(n_rows: int, n_cols: int, seed: int, kind: str = "normal") -> 
     """fp32 score matrices for exercising top-k on its own (host tensor).
 
     kinds: normal, ties (few distinct values), equal (all the same), signed_zero
-    (only +0.0 and -0.0), increasing, neg_inf_tail (normal with the second half -inf).
+    (only +0.0 and -0.0), increasing, neg_inf_tail (normal with the second half -inf),
+    extremes (normal with 1% each of +-inf, +-FLT_MAX and denormals), huge (all within a
+    factor of two below FLT_MAX).
     """
     g = torch.Generator().manual_seed(seed)
     if kind == "normal":
@@ -266,4 +268,15 @@ def random_scores(n_rows: int, n_cols: int, seed: int, kind: str = "normal") -> 
         x = torch.randn((n_rows, n_cols), generator=g)
         x[:, n_cols // 2:] = float("-inf")
         return x
+    if kind == "extremes":
+        x = torch.randn((n_rows, n_cols), generator=g)
+        pick = torch.randint(0, 100, (n_rows, n_cols), generator=g)
+        fmax = torch.finfo(torch.float32).max
+        for code, v in ((0, float("inf")), (1, fmax), (2, -fmax), (3, float("-inf")),
+                        (4, 1e-40), (5, -1e-40)):
+            x[pick == code] = v
+        return x
+    if kind == "huge":
+        u = torch.rand((n_rows, n_cols), generator=g)
+        return torch.finfo(torch.float32).max * (0.5 + 0.5 * u)
     raise KeyError(kind)

@@ -29,7 +29,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"dsa_index_score", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_sparse_mla_workspace_size", "dsa_lse_combine", "dsa_quantize_q", "dsa_last_error",
+            "dsa_sparse_mla_workspace_size", "dsa_topk_sparse_mla", "dsa_lse_combine", "dsa_quantize_q", "dsa_last_error",
             "dsa_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -120,6 +120,36 @@ def test_sparse_mla_and_combine_reject_bad_host_args(L):
     assert g(65, 4, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert g(4, 0, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert g(4, 4, None, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_topk_sparse_mla_rejects_bad_host_args(L):
+    f = L.dsa_topk_sparse_mla
+    cand = L.dsa_topk_workspace_size(4, 1000, 512)
+    need = L.dsa_sparse_mla_workspace_size(4, 4)
+    CW, WS = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+    # num_seqs, n_q, max_seq_len, cu_q, seq_lens, scores, score_stride, k, block_table,
+    # bt_stride, cand_ws, cand_bytes, topk_idx, topk_slot, q_bf16, q8, q_scale, latent,
+    # latent_stride, latent_scale, softmax_scale, S, out, lse, workspace, ws_bytes, stream
+    base = [2, 4, 1000, FAKE, FAKE, FAKE, 1000, 512, FAKE, 16, CW, cand, None, None, FAKE,
+            None, None, FAKE, 36864, ctypes.c_float(0.01), ctypes.c_float(0.04), 4, FAKE, FAKE,
+            WS, need, None]
+    cases = [({0: 0}, 1, "num_seqs"), ({7: 0}, 2, "k"), ({7: 4097}, 2, "k"),
+             ({21: 65}, 2, "num_splits"), ({8: None}, 1, "block_table"),
+             ({5: None}, 1, "scores"), ({6: 999}, 1, "score_stride"), ({9: 15}, 1, "bt_stride"),
+             ({10: None}, 3, "candidate"), ({11: cand - 1}, 3, "candidate"),
+             ({10: ctypes.c_void_p(0x10010)}, 1, "cand_workspace"),
+             ({14: None}, 1, "query"), ({15: FAKE}, 1, "q8"), ({17: None}, 1, "latent_pages"),
+             ({18: 36863}, 1, "latent_page_stride"), ({22: None}, 1, "out_bf16"),
+             ({24: None}, 3, "workspace"), ({25: need - 1}, 3, "workspace")]
+    for patch, status, word in cases:
+        args = list(base)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == status, (patch, _err())
+        assert word in _err(), (patch, _err())
+    args = list(base)
+    args[7], args[21] = 3, 4                     # more splits than selected tokens
+    assert f(*args) == 1 and "num_splits" in _err()
 
 
 def test_quantize_rejects_bad_dim(L):

@@ -177,6 +177,9 @@ TOPK_CASES = [
     ([70000], [1], 100, "neg_inf_tail"),
     ([5000, 3000], [1, 1], 1, "normal"),
     ([3000], [1], 4096, "normal"),          # k >= visible: everything, then -1
+    ([60000, 131072], [2, 1], 2048, "extremes"),
+    ([60000], [1], 64, "extremes"),
+    ([100000], [2], 2048, "huge"),
 ]
 
 
@@ -497,3 +500,97 @@ def test_fused_topk_resends_groups_that_hold_the_winners():
         assert topk_is_valid_for(got, i2[row].cpu().numpy(), 2048)
         in_groups = ((i2[row] >= 5120) & (i2[row] < 6144)).sum().item()
         assert in_groups > 200, in_groups
+
+
+# ------------------------------------------------------------- stage 2's final pass in stage 3
+def _select_attend(batch, k, num_splits, prepared=False, outputs=True):
+    """Indexer with candidates, then dsa_topk_sparse_mla: (idx, slot, out, lse)."""
+    wl = batch.wl
+    scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    ws = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k))
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, scores, max_seq_len=wl.max_seq_len,
+                        max_q_per_seq=max(wl.q_per_seq), cand_k=k, cand_workspace=ws)
+    idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((wl.n_q, 96, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((wl.n_q, 96), float("nan"), dtype=torch.float32, device=DEV)
+    kw = {}
+    if prepared:
+        q8 = torch.empty((wl.n_q, 96, 576), dtype=torch.uint8, device=DEV)
+        qs = torch.empty((wl.n_q, 96), dtype=torch.float32, device=DEV)
+        dsa.dsa_quantize_q(batch.q_mla, q8, qs)
+        kw = dict(q8=q8, q_scale=qs)
+    dsa.dsa_topk_sparse_mla(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, ws,
+                            None if prepared else batch.q_mla, batch.latent_pool,
+                            batch.latent_scale, batch.softmax_scale, num_splits,
+                            max_seq_len=wl.max_seq_len, out=out, lse=lse,
+                            topk_idx=idx if outputs else None,
+                            topk_slot=slot if outputs else None, **kw)
+    torch.cuda.synchronize()
+    return idx, slot, out, lse
+
+
+def _two_calls(batch, k, num_splits):
+    _, idx, slot = _fused(batch, k)
+    out, lse = run_mla_merged(batch, slot, num_splits)
+    return idx, slot, out, lse
+
+
+@pytest.mark.parametrize("num_splits", [1, 4])
+@pytest.mark.parametrize("wl", FUSED, ids=lambda w: w.name)
+def test_select_in_attention_is_bitwise_the_two_call_path(wl, num_splits):
+    say("select+attend", wl.name, num_splits)
+    batch = synth.make_batch(wl, DEV)
+    i1, t1, o1, l1 = _two_calls(batch, wl.topk, num_splits)
+    i2, t2, o2, l2 = _select_attend(batch, wl.topk, num_splits)
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_select_in_attention_without_selection_outputs_and_with_prepared_query():
+    wl = FUSED[1]
+    say("select+attend variants", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    _, _, o1, l1 = _select_attend(batch, wl.topk, 3)
+    i2, t2, o2, l2 = _select_attend(batch, wl.topk, 3, prepared=True, outputs=False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert bool((i2 == -7).all()) and bool((t2 == -7).all())   # not written
+
+
+def test_select_in_attention_matches_the_oracle():
+    # the selection is a valid exact top-k of the row's scores (checked against the oracle's
+    # scores), its slots follow the block table, and the attention over them matches the
+    # oracle's MLA + LSE merge
+    wl = SMALL[0]
+    say("select+attend oracle", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    idx, slot, out, lse = _select_attend(batch, wl.topk, 2)
+    scores = run_scores(batch)
+    h = host(batch)
+    o_np, l_np = out.float().cpu().numpy(), lse.cpu().numpy()
+    idx_np, slots = idx.cpu().numpy(), slot.cpu().numpy()
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref, mag = oracle_scores(batch, row, keys=request_keys(batch, b, h["key_pool"], h["bt"]))
+        got = scores[row, : pos + 1].cpu().numpy()
+        check_scores(got, ref, mag, f"row {row}")
+        assert topk_is_valid_for(got, idx_np[row], wl.topk), row
+        sel = idx_np[row][idx_np[row] >= 0]
+        assert np.array_equal(slots[row][: sel.size], O.physical_slot(h["bt"][b], sel)), row
+        assert (slots[row][sel.size:] == -1).all(), row
+        o_ref, l_ref = O.lse_combine(_oracle_attention(batch, row, slots[row], 2))
+        check_attention(o_np[row], l_np[row], o_ref, l_ref, f"row {row} select+attend")
+
+
+def test_select_in_attention_resends_groups_that_hold_the_winners():
+    wl = synth.custom([40000], [2], topk=2048, seed=64, name="fused-skew")
+    batch = synth.make_batch(wl, DEV)
+    bt = batch.block_table.cpu().numpy()
+    for page in range(80, 96):
+        batch.key_pool[int(bt[0, page]), 8192:].view(torch.float32).mul_(1000.0)
+    torch.cuda.synchronize()
+    i1, t1, o1, l1 = _two_calls(batch, 2048, 2)
+    i2, t2, o2, l2 = _select_attend(batch, 2048, 2)
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert ((i2[0] >= 5120) & (i2[0] < 6144)).sum().item() > 200
