@@ -183,9 +183,9 @@ def main():
     ap.add_argument("--query-side-stream", action="store_true",
                     help="quantise the MLA query on a side stream during stages 1-2 instead of "
                          "inside the attention kernel")
-    ap.add_argument("--select-in-attention", action="store_true",
-                    help="run stage 2's final pass inside the attention kernel (one launch for "
-                         "stages 2-4)")
+    ap.add_argument("--separate-topk", action="store_true",
+                    help="run stage 2's final pass as its own kernel instead of inside the "
+                         "attention kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -207,7 +207,8 @@ def main():
     batch = synth.make_batch(wl, "cuda")
     step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
                           query_on_side_stream=args.query_side_stream,
-                          select_in_attention=args.select_in_attention)
+                          select_in_attention=not (args.separate_topk or args.unfused),
+                          write_selection=False)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
     flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -254,22 +255,34 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
-    per_step = []
-    stage = [[], [], []]
+    def timed_steps(with_stages):
+        per = []
+        for _ in range(args.steps):
+            if not args.no_flush:
+                flush()                     # outside the events
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            if with_stages:
+                one_step(evs)
+            else:
+                evs[0].record(stream)
+                one_step()
+                evs[3].record(stream)
+            per.append(evs)
+        torch.cuda.synchronize()
+        return per
+
+    # the timed steps carry only a start and an end event (each event between kernels adds a
+    # few microseconds); the same steps are then run again with events between the stages
+    # for the per-stage times and the indexer's launch duration
+    torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        if not args.no_flush:
-            flush()                     # outside the events
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        one_step(evs)
-        per_step.append(evs)
-    torch.cuda.synchronize()
+    per_step = timed_steps(False)
     t_wall = time.perf_counter() - t_wall0
-    for evs in per_step:
+    step_us = [evs[0].elapsed_time(evs[3]) * 1e3 for evs in per_step]
+    stage = [[], [], []]
+    for evs in timed_steps(True):
         for i in range(3):
             stage[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
-    step_us = [sum(s[i] for s in stage) for i in range(args.steps)]
     step_us_sorted = sorted(step_us)
     med = step_us_sorted[len(step_us_sorted) // 2]
     mean_us = sum(step_us) / len(step_us)
@@ -312,14 +325,14 @@ def main():
                    "context": wl.max_seq_len if len(set(wl.seq_lens)) == 1 else "ragged",
                    "topk": wl.topk, "num_splits": S, "page_size": PAGE,
                    "indexer_emits_topk_candidates": not args.unfused,
-                   "topk_final_in_attention": args.select_in_attention,
+                   "topk_final_in_attention": step.select_in_attention,
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),
         "us_per_layer_median": round(med, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "stage_us": ({"index_score": round(stage_mean[0], 2),
                       "topk_final_in_sparse_mla_and_merge": round(stage_mean[2], 2)}
-                     if args.select_in_attention else
+                     if step.select_in_attention else
                      {"index_score": round(stage_mean[0], 2), "topk": round(stage_mean[1], 2),
                       "sparse_mla_and_merge": round(stage_mean[2], 2)}),
         "algorithmic_bytes": ab,

@@ -277,15 +277,22 @@ class DecodeStep:
     """Device buffers for one pass of the whole path over a fixed batch shape.
 
     Allocates (through torch) the scores, top-k outputs, workspaces and the prepared MLA
-    query once; run() issues the library calls on the current stream, with the MLA query
-    quantised on a side stream while stages 1 and 2 run.
+    query once; run() issues the library calls on the current stream.  By default the
+    indexer also emits the top-k candidates (fused) and the final top-k pass runs inside the
+    attention kernel (select_in_attention: two launches, plus the split merge); otherwise
+    stage 2 is its own call.  With query_on_side_stream the MLA query is quantised on a side
+    stream while stages 1 and 2 run.
     """
 
     def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
                  fused: bool = True, query_on_side_stream: bool = False,
-                 select_in_attention: bool = False):
+                 select_in_attention: Optional[bool] = None, write_selection: bool = True):
+        if select_in_attention is None:
+            select_in_attention = fused
         if select_in_attention and not fused:
             raise ValueError("select_in_attention needs the indexer's candidates (fused=True)")
+        # with select_in_attention, topk_idx / topk_slot are written only if write_selection
+        self.write_selection = write_selection
         self.n_q, self.max_seq_len, self.k, self.num_splits = n_q, max_seq_len, k, num_splits
         self.fused = fused
         self.select_in_attention = select_in_attention
@@ -344,6 +351,8 @@ class DecodeStep:
                             None if prepared else q_mla, latent_pages, latent_scale,
                             softmax_scale, self.num_splits, max_seq_len=self.max_seq_len,
                             out=self.out, lse=self.lse,
+                            topk_idx=self.topk_idx if self.write_selection else None,
+                            topk_slot=self.topk_slot if self.write_selection else None,
                             q8=self.q8 if prepared else None,
                             q_scale=self.q_scale if prepared else None,
                             workspace=self.mla_workspace, stream=stream)

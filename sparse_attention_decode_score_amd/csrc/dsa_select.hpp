@@ -54,68 +54,6 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// One wave's top-m of a group: lane l holds element 64*j + l in keys[j] (element i is token
-// t0 + i; elements i >= n are not visible).  Writes the min(n, m) chosen keys and token
-// indices in token order to ck / ci, sentinels (key 0, index INT_MAX) after them, and the
-// group's record.  Wave-uniform control flow only; no LDS.
-__device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, int m, int t0,
-                                             uint32_t* ck, int32_t* ci, ChunkInfo* inf) {
-  const int lane = lane_id();
-  uint32_t kv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) kv[j] = (64 * j + lane < n) ? keys[j] : kSentinel;
-  if (n <= m) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 64 * j + lane;
-      if (i < m) {
-        ck[i] = kv[j];
-        ci[i] = i < n ? t0 + i : 0x7FFFFFFF;
-      }
-    }
-    if (lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
-    return;
-  }
-  // K = the m-th largest key: the largest T with #{keys >= T} >= m, one bit at a time
-  // (every T tried is >= 1, so the sentinel of an invisible element never counts)
-  uint32_t K = 0;
-#pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t T = K | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c += __popcll(__ballot(kv[j] >= T));
-    if (c >= m) K = T;
-  }
-  int gt = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) gt += __popcll(__ballot(kv[j] > K));
-  const int r = m - gt;  // equal keys taken, the first r in token order
-  int base = 0, eq_seen = 0, last = -1;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool eq = kv[j] == K;
-    const uint64_t eqm = __ballot(eq);
-    const int rank = eq_seen + lanes_below(eqm);
-    const bool take = kv[j] > K || (eq && rank < r);
-    if (eq && rank == r - 1) last = 64 * j + lane;
-    const uint64_t tm = __ballot(take);
-    if (take) {
-      const int pos = base + lanes_below(tm);
-      ck[pos] = kv[j];
-      ci[pos] = t0 + 64 * j + lane;
-    }
-    base += __popcll(tm);
-    eq_seen += __popcll(eqm);
-  }
-  const uint64_t who = __ballot(last >= 0);
-  const int last_i = __shfl(last, (int)__builtin_ctzll(who), 64);
-  if (lane == 0) *inf = ChunkInfo{m, 1, K, t0 + last_i};
-}
-
-// ----------------------------------------------------------------------------------------
-// Workgroup (kFinalThreads threads) primitives.
-
 // Sum of v over the wave, returned wave-uniform: DPP butterflies inside each row of 16 lanes
 // (quad swaps, half-row and row mirrors), then the four row sums.
 __device__ __forceinline__ int wave_sum(int v) {
@@ -161,11 +99,113 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
 }
 
+// One wave's top-m of a group: lane l holds element 64*j + l in keys[j] (element i is token
+// t0 + i; elements i >= n are not visible).  Writes the min(n, m) chosen keys and token
+// indices in token order to ck / ci, sentinels (key 0, index INT_MAX) after them, and the
+// group's record.  Wave-uniform control flow only; no LDS.
+__device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, int m, int t0,
+                                             uint32_t* ck, int32_t* ci, ChunkInfo* inf) {
+  const int lane = lane_id();
+  uint32_t kv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kv[j] = (64 * j + lane < n) ? keys[j] : kSentinel;
+  if (n <= m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 64 * j + lane;
+      if (i < m) {
+        ck[i] = kv[j];
+        ci[i] = i < n ? t0 + i : 0x7FFFFFFF;
+      }
+    }
+    if (lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
+    return;
+  }
+  // K = the m-th largest key: the largest T with #{keys >= T} >= m, one bit at a time.  The
+  // visible keys (>= 1) share the bits of their maximum and minimum above the highest bit
+  // where those differ, so the search starts below it with the bracket [K, K_hi) around
+  // every key; it ends early when one key is left in the bracket (that key is the m-th).
+  // Every T tried is >= 1, so the sentinel of an invisible element never counts.
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mx = max(mx, kv[j]);
+    mn = min(mn, kv[j] == kSentinel ? 0xFFFFFFFFu : kv[j]);
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  uint32_t K = mx, K_hi = 0u;
+  bool has_hi = false;
+  int c_K = n, c_hi = 0;  // #{>= K} (an upper bound until K moves), #{>= K_hi}
+  int bit = -1;           // mx == mn: every visible key is the m-th
+  if (mx != mn) {
+    bit = 31 - __builtin_clz(mx ^ mn);
+    if (bit < 31) {
+      const uint32_t span = 2u << bit;
+      K = mx & ~(span - 1u);
+      K_hi = K + span;
+      has_hi = K_hi != 0u;
+    } else {
+      K = 0u;
+    }
+  }
+#pragma unroll 1
+  for (; bit >= 0; --bit) {
+    if (c_K - c_hi == 1) {
+      const uint32_t lo = K > 1u ? K : 1u;
+      uint32_t x = K;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t b = __ballot(kv[j] >= lo && (!has_hi || kv[j] < K_hi));
+        if (b) x = (uint32_t)__builtin_amdgcn_readlane((int)kv[j], (int)__builtin_ctzll(b));
+      }
+      K = x;
+      break;
+    }
+    const uint32_t T = K | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c += __popcll(__ballot(kv[j] >= T));
+    if (c >= m) {
+      K = T;
+      c_K = c;
+    } else {
+      K_hi = T;
+      has_hi = true;
+      c_hi = c;
+    }
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gt += __popcll(__ballot(kv[j] > K));
+  const int r = m - gt;  // equal keys taken, the first r in token order
+  int base = 0, eq_seen = 0, last = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool eq = kv[j] == K;
+    const uint64_t eqm = __ballot(eq);
+    const int rank = eq_seen + lanes_below(eqm);
+    const bool take = kv[j] > K || (eq && rank < r);
+    if (eq && rank == r - 1) last = 64 * j + lane;
+    const uint64_t tm = __ballot(take);
+    if (take) {
+      const int pos = base + lanes_below(tm);
+      ck[pos] = kv[j];
+      ci[pos] = t0 + 64 * j + lane;
+    }
+    base += __popcll(tm);
+    eq_seen += __popcll(eqm);
+  }
+  const uint64_t who = __ballot(last >= 0);
+  const int last_i = __shfl(last, (int)__builtin_ctzll(who), 64);
+  if (lane == 0) *inf = ChunkInfo{m, 1, K, t0 + last_i};
+}
+
 // ----------------------------------------------------------------------------------------
-// Workgroup (kFinalThreads threads) exchanges through `red`: 4 * kFinalWaves ints of LDS,
-// 16-byte aligned, used as two buffers of 2 * kFinalWaves ints in turn (parity flips), so one
-// barrier per exchange suffices: a wave writes a buffer again only after the barrier of the
-// exchange in between, which every wave reaches after reading it.
+// Workgroup (kFinalThreads threads) primitives.  Exchanges go through `red`: 4 * kFinalWaves
+// ints of LDS, 16-byte aligned, used as two buffers of 2 * kFinalWaves ints in turn (parity
+// flips), so one barrier per exchange suffices: a wave writes a buffer again only after the
+// barrier of the exchange in between, which every wave reaches after reading it.
 __device__ __forceinline__ int* red_buf(int* red, int& parity) {
   int* buf = red + 2 * kFinalWaves * parity;
   parity ^= 1;
