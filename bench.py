@@ -183,6 +183,9 @@ def main():
     ap.add_argument("--query-side-stream", action="store_true",
                     help="quantise the MLA query on a side stream during stages 1-2 instead of "
                          "inside the attention kernel")
+    ap.add_argument("--store-scores", action="store_true",
+                    help="have the indexer store its scores (by default with candidates it "
+                         "stores none and the final pass recomputes what it re-reads)")
     ap.add_argument("--separate-topk", action="store_true",
                     help="run stage 2's final pass as its own kernel instead of inside the "
                          "attention kernel")
@@ -208,6 +211,7 @@ def main():
     step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
                           query_on_side_stream=args.query_side_stream,
                           select_in_attention=not (args.separate_topk or args.unfused),
+                          store_scores=args.store_scores or args.unfused,
                           write_selection=False)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
@@ -325,6 +329,7 @@ def main():
                    "context": wl.max_seq_len if len(set(wl.seq_lens)) == 1 else "ragged",
                    "topk": wl.topk, "num_splits": S, "page_size": PAGE,
                    "indexer_emits_topk_candidates": not args.unfused,
+                   "scores_stored": step.store_scores,
                    "topk_final_in_attention": step.select_in_attention,
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),

@@ -100,6 +100,11 @@ typedef enum {
  *   scores   fp32 [n_q][score_stride], score_stride >= max_seq_len.  Row i's columns
  *            0 .. seq_lens[b]-1 are written; columns past its position hold scores of
  *            keys it may not see (ignored by dsa_topk); other columns are not touched.
+ *            NULL with cand_workspace given: candidates only, no score is stored (the
+ *            scorer + per-chunk candidates with no materialised scores of the page's exact
+ *            one-round merge, "Exact top-k merge with ~10x less traffic"); dsa_topk and
+ *            dsa_topk_sparse_mla then recompute the few groups they must re-read from the
+ *            same q_bf16 / head_w / key cache (pass them there).
  *   cand_k, cand_workspace, cand_workspace_bytes: if cand_workspace is not NULL the
  *            scoring waves also write, for a top-k of cand_k (1..4096), every 256-token
  *            group's best candidates (4x the winners a full group holds on average, in
@@ -117,6 +122,7 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
 /*
  * Stage 2 — exact top-k over each row's visible scores (tokens 0..position).
  * Order: score descending, then token index ascending (-0.0 == +0.0; NaN ranks lowest).
+ * scores is only read, unless the scores were not stored (see q_idx_bf16 below).
  * Two passes: every 256-token group keeps its best m candidates (4x the winners a full
  * group holds on average), then one workgroup per row selects from the candidates; the
  * groups that could have held more of the winners than they sent (the detection rule of
@@ -132,13 +138,20 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
  *   workspace: device memory of at least dsa_topk_workspace_size(n_q, max_seq_len, k)
  *   bytes, 256-byte aligned; with from_candidates = 0 its contents need no
  *   initialisation.  It is scratch after the call.
+ *   q_idx_bf16, head_w, key_pages, key_page_stride: all NULL / 0 when the scores were
+ *   stored.  When dsa_index_score stored none (scores = NULL there), pass its query, head
+ *   weights and index-key cache here (from_candidates = 1 and block_table required): the
+ *   groups that must be re-read are recomputed with the indexer's own arithmetic (bitwise
+ *   its scores) into `scores`, which is then scratch of [n_q][score_stride] fp32 whose
+ *   contents need no initialisation.
  */
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k);
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
-                    const int32_t* seq_lens, const float* scores, int64_t score_stride, int32_t k,
+                    const int32_t* seq_lens, float* scores, int64_t score_stride, int32_t k,
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
                     int32_t* topk_slot, void* workspace, size_t workspace_bytes,
-                    int32_t from_candidates, void* stream);
+                    int32_t from_candidates, const void* q_idx_bf16, const float* head_w,
+                    const void* key_pages, int64_t key_page_stride, void* stream);
 
 /*
  * Stage 3 — exact MLA (NoPE) over the selected slots, one query row at a time.
@@ -186,7 +199,8 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
  * row repeats it) removes one launch and the wait on a single workgroup per row.
  *   Batch, scores, k, block_table (required here): as for dsa_topk.
  *   cand_workspace: dsa_topk_workspace_size(n_q, max_seq_len, k) bytes, 256-byte aligned,
- *   read only.
+ *   read only.  q_idx_bf16, head_w, key_pages, key_page_stride: as for dsa_topk (scores
+ *   not stored: `scores` is scratch).
  *   topk_idx, topk_slot: optional outputs (each may be NULL), as dsa_topk writes them.
  *   Query, latent cache, softmax_scale, num_splits (S <= k), out_bf16 [n_q][96][512] bf16,
  *   lse [n_q][96] fp32, workspace (S > 1: dsa_sparse_mla_workspace_size(n_q, S) bytes,
@@ -194,10 +208,12 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
  *   bitwise those of dsa_topk(from_candidates = 1) followed by dsa_sparse_mla_decode.
  */
 dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
-                               const int32_t* cu_q, const int32_t* seq_lens, const float* scores,
+                               const int32_t* cu_q, const int32_t* seq_lens, float* scores,
                                int64_t score_stride, int32_t k, const int32_t* block_table,
                                int32_t bt_stride, const void* cand_workspace,
-                               size_t cand_workspace_bytes, int32_t* topk_idx,
+                               size_t cand_workspace_bytes, const void* q_idx_bf16,
+                               const float* head_w, const void* key_pages,
+                               int64_t key_page_stride, int32_t* topk_idx,
                                int32_t* topk_slot, const void* q_bf16, const void* q8,
                                const float* q_scale, const void* latent_pages,
                                int64_t latent_page_stride, float latent_scale,

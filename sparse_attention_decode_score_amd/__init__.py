@@ -51,14 +51,14 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
-                               _I32, _P]
+                               _I32, _P, _P, _P, _I64, _P]
         L.dsa_sparse_mla_workspace_size.argtypes = [_I32, _I32]
         L.dsa_sparse_mla_workspace_size.restype = _SZ
         L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _P, _P, _I64, _F32, _P, _I32, _F32, _I32,
                                             _P, _P, _P, _P, _P, _SZ, _P]
         L.dsa_topk_sparse_mla.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P,
-                                          _SZ, _P, _P, _P, _P, _P, _P, _I64, _F32, _F32, _I32,
-                                          _P, _P, _P, _SZ, _P]
+                                          _SZ, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I64,
+                                          _F32, _F32, _I32, _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_last_error.restype = ctypes.c_char_p
@@ -113,12 +113,13 @@ def dsa_quantize_q(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, s
 
 def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Tensor,
                     head_w: torch.Tensor, key_pages: torch.Tensor, block_table: torch.Tensor,
-                    scores: torch.Tensor, *, max_seq_len: int, max_q_per_seq: int,
+                    scores: Optional[torch.Tensor], *, max_seq_len: int, max_q_per_seq: int,
                     key_page_stride: Optional[int] = None, cand_k: int = 0,
                     cand_workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Indexer scores into scores [n_q, score_stride] (fp32); with cand_workspace, also the
     per-chunk top-k candidates for a top-k of cand_k (consumed by dsa_topk with
-    from_candidates=True)."""
+    from_candidates=True).  scores=None with cand_workspace: candidates only (no scores
+    stored; pass rescore=(q_idx, head_w, key_pages) to the final top-k pass)."""
     num_seqs = seq_lens.shape[0]
     n_q = q_idx.shape[0]
     _expect(cu_q, "cu_q", torch.int32, (num_seqs + 1,))
@@ -126,19 +127,33 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
     _expect(q_idx, "q_idx", torch.bfloat16, (n_q, IDX_HEADS, IDX_DIM))
     _expect(head_w, "head_w", torch.float32, (n_q, IDX_HEADS))
     _expect(block_table, "block_table", torch.int32)
-    _expect(scores, "scores", torch.float32)
-    if scores.dim() != 2 or scores.shape[0] != n_q:
-        raise ValueError("scores must be [n_q, score_stride]")
+    if scores is not None:
+        _expect(scores, "scores", torch.float32)
+        if scores.dim() != 2 or scores.shape[0] != n_q:
+            raise ValueError("scores must be [n_q, score_stride]")
     stride = key_page_stride if key_page_stride is not None else key_pages.stride(0) * key_pages.element_size()
     if cand_workspace is not None:
         _expect(cand_workspace, "cand_workspace", torch.uint8)
     _check(lib().dsa_index_score(num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q),
                                  _ptr(seq_lens), _ptr(q_idx), _ptr(head_w), _ptr(key_pages),
                                  int(stride), _ptr(block_table), block_table.shape[1],
-                                 _ptr(scores), scores.shape[1], int(cand_k),
+                                 _ptr(scores), scores.shape[1] if scores is not None else 0,
+                                 int(cand_k),
                                  _ptr(cand_workspace),
                                  cand_workspace.numel() if cand_workspace is not None else 0,
                                  _stream(stream)))
+
+
+def _rescore_args(rescore):
+    """(q_idx, head_w, key_pages[, key_page_stride]) -> C arguments, or NULLs."""
+    if rescore is None:
+        return (None, None, None, 0)
+    q_idx, head_w, key_pages = rescore[:3]
+    _expect(q_idx, "q_idx", torch.bfloat16)
+    _expect(head_w, "head_w", torch.float32)
+    stride = (rescore[3] if len(rescore) > 3
+              else key_pages.stride(0) * key_pages.element_size())
+    return (_ptr(q_idx), _ptr(head_w), _ptr(key_pages), int(stride))
 
 
 def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
@@ -148,8 +163,9 @@ def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
 def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,
              block_table: Optional[torch.Tensor], topk_idx: torch.Tensor,
              topk_slot: Optional[torch.Tensor], workspace: torch.Tensor, *, max_seq_len: int,
-             from_candidates: bool = False, stream=None) -> None:
-    """Exact top-k token indices (and physical slots) of every row's visible scores."""
+             from_candidates: bool = False, rescore=None, stream=None) -> None:
+    """Exact top-k token indices (and physical slots) of every row's visible scores.
+    rescore=(q_idx, head_w, key_pages): the indexer stored no scores; scores is scratch."""
     num_seqs = seq_lens.shape[0]
     n_q = scores.shape[0]
     _expect(scores, "scores", torch.float32)
@@ -161,7 +177,7 @@ def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k
                           scores.shape[1], int(k), _ptr(block_table),
                           block_table.shape[1] if block_table is not None else 0,
                           _ptr(topk_idx), _ptr(topk_slot), _ptr(workspace), workspace.numel(),
-                          int(bool(from_candidates)), _stream(stream)))
+                          int(bool(from_candidates)), *_rescore_args(rescore), _stream(stream)))
 
 
 def dsa_sparse_mla_workspace_size(n_q: int, num_splits: int) -> int:
@@ -226,10 +242,12 @@ def dsa_topk_sparse_mla(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torc
                         topk_slot: Optional[torch.Tensor] = None,
                         q8: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None,
-                        latent_page_stride: Optional[int] = None, stream=None) -> None:
+                        latent_page_stride: Optional[int] = None, rescore=None,
+                        stream=None) -> None:
     """Final top-k pass and sparse MLA in one launch: every attention workgroup selects its
     row's top k from the candidates dsa_index_score left in cand_workspace (cand_k = k), then
-    attends over its split of them.  topk_idx / topk_slot, when given, receive the selection."""
+    attends over its split of them.  topk_idx / topk_slot, when given, receive the selection.
+    rescore=(q_idx, head_w, key_pages): the indexer stored no scores; scores is scratch."""
     num_seqs = seq_lens.shape[0]
     n_q = scores.shape[0]
     _expect(scores, "scores", torch.float32)
@@ -255,7 +273,8 @@ def dsa_topk_sparse_mla(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torc
     _check(lib().dsa_topk_sparse_mla(
         num_seqs, n_q, int(max_seq_len), _ptr(cu_q), _ptr(seq_lens), _ptr(scores),
         scores.shape[1], int(k), _ptr(block_table), block_table.shape[1], _ptr(cand_workspace),
-        cand_workspace.numel(), _ptr(topk_idx), _ptr(topk_slot), _ptr(q_mla), _ptr(q8),
+        cand_workspace.numel(), *_rescore_args(rescore), _ptr(topk_idx), _ptr(topk_slot),
+        _ptr(q_mla), _ptr(q8),
         _ptr(q_scale), _ptr(latent_pages), int(stride), float(latent_scale),
         float(softmax_scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
@@ -278,17 +297,27 @@ class DecodeStep:
 
     Allocates (through torch) the scores, top-k outputs, workspaces and the prepared MLA
     query once; run() issues the library calls on the current stream.  By default the
-    indexer also emits the top-k candidates (fused) and the final top-k pass runs inside the
-    attention kernel (select_in_attention: two launches, plus the split merge); otherwise
-    stage 2 is its own call.  With query_on_side_stream the MLA query is quantised on a side
+    indexer also emits the top-k candidates (fused) and stores no scores (store_scores=False:
+    the final pass recomputes the few groups it must re-read), and the final top-k pass runs
+    inside the attention kernel (select_in_attention: two launches, plus the split merge);
+    otherwise stage 2 is its own call.  With query_on_side_stream the MLA query is quantised on a side
     stream while stages 1 and 2 run.
     """
 
     def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
                  fused: bool = True, query_on_side_stream: bool = False,
-                 select_in_attention: Optional[bool] = None, write_selection: bool = True):
+                 select_in_attention: Optional[bool] = None, write_selection: bool = True,
+                 store_scores: Optional[bool] = None):
         if select_in_attention is None:
             select_in_attention = fused
+        if store_scores is None:
+            store_scores = not fused
+        if not store_scores and not fused:
+            raise ValueError("store_scores=False needs the indexer's candidates (fused=True)")
+        # without stored scores, the final top-k pass recomputes the groups it re-reads from
+        # the indexer's inputs (kept from index()) into self.scores, used as scratch
+        self.store_scores = store_scores
+        self._rescore = None
         if select_in_attention and not fused:
             raise ValueError("select_in_attention needs the indexer's candidates (fused=True)")
         # with select_in_attention, topk_idx / topk_slot are written only if write_selection
@@ -314,7 +343,9 @@ class DecodeStep:
     def index(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq,
               stream=None):
         """Stage 1 (with the fused first top-k pass when self.fused)."""
-        dsa_index_score(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, self.scores,
+        self._rescore = None if self.store_scores else (q_idx, head_w, key_pages)
+        dsa_index_score(cu_q, seq_lens, q_idx, head_w, key_pages, block_table,
+                        self.scores if self.store_scores else None,
                         max_seq_len=self.max_seq_len, max_q_per_seq=max_q_per_seq,
                         cand_k=self.k, cand_workspace=self.workspace if self.fused else None,
                         stream=stream)
@@ -323,7 +354,7 @@ class DecodeStep:
         """Stage 2."""
         dsa_topk(cu_q, seq_lens, self.scores, self.k, block_table, self.topk_idx, self.topk_slot,
                  self.workspace, max_seq_len=self.max_seq_len, from_candidates=self.fused,
-                 stream=stream)
+                 rescore=self._rescore, stream=stream)
 
     def prepare_query(self, q_mla, stream=None):
         """E4M3 codes and scales of the MLA query (stage 3's own quantisation)."""
@@ -353,6 +384,7 @@ class DecodeStep:
                             out=self.out, lse=self.lse,
                             topk_idx=self.topk_idx if self.write_selection else None,
                             topk_slot=self.topk_slot if self.write_selection else None,
+                            rescore=self._rescore,
                             q8=self.q8 if prepared else None,
                             q_scale=self.q_scale if prepared else None,
                             workspace=self.mla_workspace, stream=stream)

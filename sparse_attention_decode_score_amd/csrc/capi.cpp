@@ -76,6 +76,23 @@ dsa_status check_mla_inputs(int32_t n_q, const void* q_bf16, const void* q8,
   return DSA_OK;
 }
 
+// The indexer inputs the final top-k pass recomputes scores from (all NULL: scores stored).
+dsa_status check_rescore(const void* q_idx_bf16, const float* head_w, const void* key_pages,
+                         int64_t key_page_stride, const int32_t* block_table,
+                         int32_t from_candidates) {
+  if (!q_idx_bf16 && !head_w && !key_pages) return DSA_OK;
+  DSA_REQUIRE(q_idx_bf16 && head_w && key_pages,
+              "q_idx_bf16, head_w and key_pages must all be given (scores not stored) or all be NULL");
+  DSA_REQUIRE(from_candidates, "recomputing scores needs the indexer's candidates (from_candidates)");
+  DSA_REQUIRE(block_table, "recomputing scores needs block_table");
+  DSA_REQUIRE(aligned(q_idx_bf16, 16) && aligned(head_w, 16) && aligned(key_pages, 16),
+              "q_idx_bf16, head_w and key_pages must be 16-byte aligned");
+  DSA_REQUIRE(key_page_stride >= DSA_IDX_PAGE_BYTES && key_page_stride % 16 == 0,
+              "key_page_stride must be >= 8448 and a multiple of 16 (got %lld)",
+              (long long)key_page_stride);
+  return DSA_OK;
+}
+
 dsa_status check_merged_outputs(int32_t n_q, int32_t num_splits, const void* out_bf16,
                                        const float* lse, const void* workspace,
                                        size_t workspace_bytes) {
@@ -121,8 +138,10 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
   if (st != DSA_OK) return st;
   DSA_REQUIRE(max_q_per_seq >= 1 && max_q_per_seq <= n_q,
               "max_q_per_seq must be in 1..n_q (got %d)", max_q_per_seq);
-  DSA_REQUIRE(q_bf16 && head_w && key_pages && block_table && scores,
-              "q_bf16, head_w, key_pages, block_table and scores must be non-null");
+  DSA_REQUIRE(q_bf16 && head_w && key_pages && block_table,
+              "q_bf16, head_w, key_pages and block_table must be non-null");
+  DSA_REQUIRE(scores || cand_workspace,
+              "scores may be NULL only when cand_workspace is given (candidates only)");
   DSA_REQUIRE(aligned(q_bf16, 16), "q_bf16 must be 16-byte aligned");
   DSA_REQUIRE(aligned(head_w, 16), "head_w must be 16-byte aligned");
   DSA_REQUIRE(aligned(key_pages, 16), "key_pages must be 16-byte aligned");
@@ -131,8 +150,9 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
               (long long)key_page_stride);
   DSA_REQUIRE(bt_stride >= (max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE,
               "bt_stride (%d) must cover max_seq_len (%d) in pages of 64", bt_stride, max_seq_len);
-  DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
-              (long long)score_stride, max_seq_len);
+  if (scores)
+    DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
+                (long long)score_stride, max_seq_len);
   if (cand_workspace) {
     if (cand_k < 1 || cand_k > DSA_MAX_TOPK)
       return fail(DSA_ERR_UNSUPPORTED, "cand_k must be in 1..4096 (got %d)", cand_k);
@@ -156,11 +176,14 @@ size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k) {
 }
 
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
-                    const int32_t* seq_lens, const float* scores, int64_t score_stride, int32_t k,
+                    const int32_t* seq_lens, float* scores, int64_t score_stride, int32_t k,
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
                     int32_t* topk_slot, void* workspace, size_t workspace_bytes,
-                    int32_t from_candidates, void* stream) {
+                    int32_t from_candidates, const void* q_idx_bf16, const float* head_w,
+                    const void* key_pages, int64_t key_page_stride, void* stream) {
   dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
+  if (st != DSA_OK) return st;
+  st = check_rescore(q_idx_bf16, head_w, key_pages, key_page_stride, block_table, from_candidates);
   if (st != DSA_OK) return st;
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
   DSA_REQUIRE(scores && topk_idx, "scores and topk_idx must be non-null");
@@ -179,8 +202,10 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (from_candidates) {
     const dsa::TopkBuffers t = dsa::topk_buffers(workspace, n_q, max_seq_len, k);
+    const dsa::IndexRescore rs{static_cast<const uint16_t*>(q_idx_bf16), head_w,
+                               static_cast<const uint8_t*>(key_pages), key_page_stride};
     return launched(dsa::launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k,
-                                           t, block_table, bt_stride, topk_idx, topk_slot, hs),
+                                           t, rs, block_table, bt_stride, topk_idx, topk_slot, hs),
                     "dsa_topk");
   }
   return launched(dsa::launch_topk(num_seqs, n_q, max_seq_len, cu_q, seq_lens, scores, score_stride,
@@ -225,10 +250,12 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
 }
 
 dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
-                               const int32_t* cu_q, const int32_t* seq_lens, const float* scores,
+                               const int32_t* cu_q, const int32_t* seq_lens, float* scores,
                                int64_t score_stride, int32_t k, const int32_t* block_table,
                                int32_t bt_stride, const void* cand_workspace,
-                               size_t cand_workspace_bytes, int32_t* topk_idx,
+                               size_t cand_workspace_bytes, const void* q_idx_bf16,
+                               const float* head_w, const void* key_pages,
+                               int64_t key_page_stride, int32_t* topk_idx,
                                int32_t* topk_slot, const void* q_bf16, const void* q8,
                                const float* q_scale, const void* latent_pages,
                                int64_t latent_page_stride, float latent_scale,
@@ -240,6 +267,8 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                         k, softmax_scale, num_splits);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(scores && block_table, "scores and block_table must be non-null");
+  st = check_rescore(q_idx_bf16, head_w, key_pages, key_page_stride, block_table, 1);
+  if (st != DSA_OK) return st;
   DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
               (long long)score_stride, max_seq_len);
   DSA_REQUIRE(bt_stride >= (max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE,
@@ -254,8 +283,11 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
   const bool prepared = q8 != nullptr;
   const dsa::TopkBuffers t =
       dsa::topk_buffers(const_cast<void*>(cand_workspace), n_q, max_seq_len, k);
+  const dsa::IndexRescore rs{static_cast<const uint16_t*>(q_idx_bf16), head_w,
+                             static_cast<const uint8_t*>(key_pages), key_page_stride};
   return launched(dsa::launch_topk_sparse_mla(
-                      num_seqs, n_q, cu_q, seq_lens, scores, score_stride, t, block_table,
+                      num_seqs, n_q, cu_q, seq_lens, scores, score_stride, t,
+                      rs, block_table,
                       bt_stride, topk_idx, topk_slot, static_cast<const uint16_t*>(q_bf16),
                       prepared ? static_cast<const uint8_t*>(q8) : nullptr,
                       prepared ? q_scale : nullptr, static_cast<const uint8_t*>(latent_pages),

@@ -13,6 +13,16 @@ struct TopkPlan {
 };
 
 struct ChunkInfo;
+
+// Inputs the final top-k pass recomputes scores from when the indexer did not store them
+// (q == nullptr: the scores are stored).
+struct IndexRescore {
+  const uint16_t* q;       // indexer query bf16 [n_q][32][128]
+  const float* head_w;     // [n_q][32]
+  const uint8_t* key_pages;
+  int64_t page_stride;
+};
+
 struct TopkBuffers {
   TopkPlan plan;
   uint32_t* cand_key;
@@ -24,10 +34,12 @@ TopkPlan topk_plan(int max_seq_len, int k);
 size_t topk_workspace_bytes(int n_q, int max_seq_len, int k);
 TopkBuffers topk_buffers(void* workspace, int n_q, int max_seq_len, int k);
 // Final pass only: the workspace already holds every group's candidates.
+// With rs.q set, scores is scratch: the pass recomputes there the groups it must re-read.
 hipError_t launch_topk_final(int num_seqs, int n_q, const int32_t* cu_q, const int32_t* seq_lens,
                              const float* scores, int64_t score_stride, int k,
-                             const TopkBuffers& t, const int32_t* block_table, int bt_stride,
-                             int32_t* topk_idx, int32_t* topk_slot, hipStream_t st);
+                             const TopkBuffers& t, const IndexRescore& rs,
+                             const int32_t* block_table, int bt_stride, int32_t* topk_idx,
+                             int32_t* topk_slot, hipStream_t st);
 
 hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, uint8_t* codes,
                              float* scales, hipStream_t st);
@@ -59,10 +71,11 @@ hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, cons
 // Stage 2's final pass fused into the sparse MLA: every (split, row) workgroup selects its
 // row's top k from the candidates in t, then attends (out/lse, fp16-merged when S > 1).
 hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
-                                  const int32_t* seq_lens, const float* scores,
+                                  const int32_t* seq_lens, float* scores,
                                   int64_t score_stride, const TopkBuffers& t,
-                                  const int32_t* block_table, int bt_stride, int32_t* topk_idx,
-                                  int32_t* topk_slot, const uint16_t* q, const uint8_t* q8,
+                                  const IndexRescore& rs, const int32_t* block_table,
+                                  int bt_stride, int32_t* topk_idx, int32_t* topk_slot,
+                                  const uint16_t* q, const uint8_t* q8,
                                   const float* q_scale, const uint8_t* latent_pages,
                                   int64_t latent_page_stride, float latent_scale, int k,
                                   float softmax_scale, int num_splits, uint16_t* out_bf16,

@@ -6,6 +6,8 @@
 #include <type_traits>
 
 #include "dsa_device.hpp"
+#include "dsa_index_core.hpp"
+#include "dsa_internal.hpp"
 #include "dsa_select.hpp"
 
 namespace dsa {
@@ -67,6 +69,41 @@ __device__ int gather_at_least(const Get& get, int n, uint32_t K, uint32_t* lkey
   return kept;
 }
 
+// Recomputes into row_scores (the row's score buffer, [0, n_vis)) the scores of every
+// group g of row `row` with need(g), with the indexer's own arithmetic, so the values are
+// bitwise those the indexer would have stored.  q8 / w: LDS for the row's quantised query
+// (32 * kQRowStride bytes, 16-byte aligned) and folded head weights (32 floats, 16-byte
+// aligned).  Starts and ends with a barrier; every thread of the workgroup calls it.
+template <class Need>
+__device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n_groups,
+                               const int32_t* bt_row, float* row_scores, Need need, uint8_t* q8,
+                               float* w) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __syncthreads();
+  if (tid < kIdxHeads * 8) {  // whole waves: 8 lanes per head
+    const int qh = tid >> 3, qpart = tid & 7;
+    const uint16_t* src = rs.q + ((int64_t)row * kIdxHeads + qh) * kIdxDim + qpart * 16;
+    const v4i raw[2] = {*reinterpret_cast<const v4i*>(src), *reinterpret_cast<const v4i*>(src + 8)};
+    quantize_index_query_part(raw, rs.head_w[(int64_t)row * kIdxHeads + qh], qpart,
+                              q8 + qh * kQRowStride + qpart * 16, w + qh);
+  }
+  __syncthreads();
+  constexpr int kPagesPerGroup = kGroupTok / kPage;
+  const int n_pages = (n_vis + kPage - 1) / kPage;
+  for (int g = wave; g < n_groups; g += kFinalWaves) {
+    if (!need(g)) continue;  // the same for every lane of the wave
+    for (int p = g * kPagesPerGroup; p < min(n_pages, (g + 1) * kPagesPerGroup); ++p) {
+      KeyPage kp;
+      load_key_page(kp, rs.key_pages + (int64_t)bt_row[p] * rs.page_stride, lane);
+      const float sc = score_key_page(q8, w, kp, lane);
+      const int t = p * kPage + lane;
+      if (t < n_vis) row_scores[t] = sc;
+    }
+  }
+  __syncthreads();
+}
+
 // LDS the final pass needs besides its output: the on-chip candidate tile (keys, token
 // indices), the reduction scratch and the last search bucket.
 struct FinalScratch {
@@ -81,19 +118,26 @@ struct FinalScratch {
 // tokens) from its group candidates, resending flagged groups from the scores.  Writes the
 // selected token indices to out[0 .. n_out) (LDS, kMaxTopk entries) and returns n_out =
 // min(k, n_vis).  Ends with a barrier, so out[] is visible to the whole workgroup.
-__device__ inline int final_select_row(int row, int n_vis, const float* __restrict__ scores,
-                                int64_t score_stride, int k, int num_groups, int64_t row_cap,
-                                const uint32_t* __restrict__ cand_key,
-                                const int32_t* __restrict__ cand_idx,
-                                const ChunkInfo* __restrict__ info, int* out,
-                                const FinalScratch& sc) {
+// rs.q set: the indexer stored no scores; the groups that must be re-read are first
+// recomputed into the row's score buffer (bt_row: the request's block-table row).
+__device__ inline int final_select_row(int row, int n_vis, float* scores, int64_t score_stride,
+                                       int k, int num_groups, int64_t row_cap,
+                                       const uint32_t* __restrict__ cand_key,
+                                       const int32_t* __restrict__ cand_idx,
+                                       const ChunkInfo* __restrict__ info,
+                                       const IndexRescore& rs, const int32_t* bt_row, int* out,
+                                       const FinalScratch& sc) {
   const int tid = threadIdx.x;
   uint32_t* lkey = sc.lkey;
   int32_t* lidx = sc.lidx;
   int* red = sc.red;
   int* note_p = sc.note;
   uint32_t* bucket = sc.bucket;
-  const float* src = scores + (int64_t)row * score_stride;
+  float* const row_scores = scores + (int64_t)row * score_stride;
+  const float* src = row_scores;
+  // LDS of a recomputation (the candidate tile is free until the resend rebuilds it)
+  uint8_t* const rq8 = reinterpret_cast<uint8_t*>(sc.lkey);
+  float* const rw = reinterpret_cast<float*>(sc.lkey) + kIdxHeads * kQRowStride / 4;
   auto score_get = [src](int i) { return score_key(src[i]); };
   auto ident = [](int i) { return i; };
   int n_out;
@@ -180,6 +224,13 @@ __device__ inline int final_select_row(int row, int n_vis, const float* __restri
         total = kFinalTile + 1;
       }
       __syncthreads();
+      if (rs.q) {
+        // no stored scores: recompute the groups the resend reads (all of them when the
+        // resend does not fit on chip)
+        const bool all = total > kFinalTile;
+        rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
+                       [&](int g) { return all || flagged(g); }, rq8, rw);
+      }
       if (total <= kFinalTile) {
 #pragma unroll 8
         for (int e = tid; e < total; e += kFinalThreads) {

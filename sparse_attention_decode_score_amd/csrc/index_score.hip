@@ -24,6 +24,7 @@
 
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
+#include "dsa_index_core.hpp"
 #include "dsa_select.hpp"
 
 namespace dsa {
@@ -32,37 +33,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kGroupPages = kGroupTok / kPage;  // 4
-constexpr int kQRowStride = 144;  // LDS row stride of the FP8 query (128 + 16 pad: no bank conflicts)
-
-struct KeyPage {
-  v8i k[2][2];  // [half][k-block]
-  float s;
-};
-
-// Keys are streamed once per step and never reused, so they are read with non-temporal
-// loads: on gfx950 this lets a shuffled page stream run near the HBM rate instead of
-// thrashing the L2 and the last-level cache (measured 6.5 vs 3.5 TB/s for this pattern).
-__device__ __forceinline__ void load_key_page(KeyPage& kp, const uint8_t* base, int lane) {
-  const int n = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const uint8_t* tok = base + (32 * hf + n) * 16;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const v4i a = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tok + (4 * g + 2 * kb) * 1024));
-      const v4i b = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tok + (4 * g + 2 * kb + 1) * 1024));
-      kp.k[hf][kb] = v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    }
-  }
-  kp.s = __builtin_nontemporal_load(reinterpret_cast<const float*>(base + kIdxPageKeyBytes + 4 * lane));
-}
-
-// ReLU as a signed-integer max on the float's bits: positive values keep their bits,
-// negative values and -0.0 become +0.0.  One v_max_i32; a float max would first have to
-// quiet possible signalling NaNs of the MFMA result (two instructions per value).
-__device__ __forceinline__ float relu(float x) {
-  return __int_as_float(max(__float_as_int(x), 0));
-}
 
 // Pages each wave keeps in flight: four for one or two rows, two for larger row groups
 // (register budget).  Groups per wave at most: the staged scores of a workgroup are
@@ -168,31 +138,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   // 3. fused query prep while the keys stream in: E4M3 codes, one power-of-two scale per
   //    (row, head), the scale folded into the head weight
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float x[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = bf16_lo((uint32_t)qraw[r][0][j]);
-      x[2 * j + 1] = bf16_hi((uint32_t)qraw[r][0][j]);
-      x[8 + 2 * j] = bf16_lo((uint32_t)qraw[r][1][j]);
-      x[8 + 2 * j + 1] = bf16_hi((uint32_t)qraw[r][1][j]);
-    }
-    float am = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) am = fmaxf(am, fabsf(x[j]));
-    am = fmaxf(am, __shfl_xor(am, 1, 64));
-    am = fmaxf(am, __shfl_xor(am, 2, 64));
-    am = fmaxf(am, __shfl_xor(am, 4, 64));
-    const int e = pow2_scale_exp(am);
-    const float inv = ldexpf(1.0f, -e);
-    v4i c;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      c[j] = (int)cvt4_e4m3(x[4 * j] * inv, x[4 * j + 1] * inv, x[4 * j + 2] * inv,
-                            x[4 * j + 3] * inv);
-    *reinterpret_cast<v4i*>(&q8s[r][qh][qpart * 16]) = c;
-    if (qpart == 0) wps[r][qh] = hw[r] * ldexpf(1.0f, e);
-  }
+  for (int r = 0; r < R; ++r)
+    quantize_index_query_part(qraw[r], hw[r], qpart, &q8s[r][qh][qpart * 16], &wps[r][qh]);
   __syncthreads();
 
   // 4. the wave's groups: score each ring slot, refill it at once, and after four pages
@@ -204,37 +151,11 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const int t = p * kPage + lane;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint8_t* qa = &q8s[r][n][64 * g];
-      const v4i a0 = *reinterpret_cast<const v4i*>(qa);
-      const v4i a1 = *reinterpret_cast<const v4i*>(qa + 16);
-      const v4i a2 = *reinterpret_cast<const v4i*>(qa + 32);
-      const v4i a3 = *reinterpret_cast<const v4i*>(qa + 48);
-      const v8i A0 = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      const v8i A1 = v8i{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-      const v16f z = {};
-      v16f d0 = mfma_32x32x64_fp8(A0, cur.k[0][0], z);
-      d0 = mfma_32x32x64_fp8(A1, cur.k[0][1], d0);
-      v16f d1 = mfma_32x32x64_fp8(A0, cur.k[1][0], z);
-      d1 = mfma_32x32x64_fp8(A1, cur.k[1][1], d1);
-      // output register i of lane l is head 8*(i/4) + 4*g + i%4 for token l%32
-      float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const v4f w = *reinterpret_cast<const v4f*>(&wps[r][8 * a + 4 * g]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc0 = fmaf(w[c], relu(d0[4 * a + c]), acc0);
-          acc1 = fmaf(w[c], relu(d1[4 * a + c]), acc1);
-        }
-      }
-      // lanes 0..31: (half-0 partial, partner's half-0 partial); lanes 32..63: half 1
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0),
-                                                       __float_as_uint(acc1), false, false);
-      const float score = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * cur.s;
+      const float score = score_key_page(&q8s[r][0][0], &wps[r][0], cur, lane);
       if constexpr (STAGE) {
-        if (valid) sbuf[r][(p - p0) * kPage + lane] = score;
+        if (valid && scores) sbuf[r][(p - p0) * kPage + lane] = score;
       } else {
-        if (valid && r < nr && t < L) scores[(int64_t)(r0 + r) * score_stride + t] = score;
+        if (valid && scores && r < nr && t < L) scores[(int64_t)(r0 + r) * score_stride + t] = score;
       }
       keys[r][jj] = valid ? score_key(score) : kSentinel;
     }
@@ -289,7 +210,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     // non-temporal stores: the scores are read again only by the rare resend of a group,
     // and plain stores interleaved with the key stream cost the stream about 8% of its rate
     const int seg_tok = min(p_end * kPage, L) - p0 * kPage;
-    for (int r = 0; r < nr; ++r) {
+    for (int r = 0; r < (scores ? nr : 0); ++r) {
       float* dst = scores + (int64_t)(r0 + r) * score_stride + p0 * kPage;
       const bool vec = (((uintptr_t)dst) & 15) == 0;
       for (int i = 4 * tid; i < seg_tok; i += 1024) {

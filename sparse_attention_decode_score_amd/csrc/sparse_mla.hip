@@ -88,13 +88,14 @@ struct SelectArgs {
   const int32_t* cu_q;
   const int32_t* seq_lens;
   int num_seqs;
-  const float* scores;
+  float* scores;  // written only by a recomputation (rs.q set)
   int64_t score_stride;
   int num_groups;
   int64_t row_cap;
   const uint32_t* cand_key;
   const int32_t* cand_idx;
   const ChunkInfo* info;
+  IndexRescore rs;
   const int32_t* block_table;
   int bt_stride;
   int32_t* topk_idx;   // optional outputs, written by split 0 of each row
@@ -146,10 +147,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     int b, pos;
     row_of(sel.cu_q, sel.seq_lens, sel.num_seqs, row, b, pos);
     const FinalScratch sc{ss.lkey, ss.lidx, ss.red, &ss.note, ss.bucket};
+    const int32_t* bt = sel.block_table + (int64_t)b * sel.bt_stride;
     const int n_out = final_select_row(row, pos + 1, sel.scores, sel.score_stride, k,
                                        sel.num_groups, sel.row_cap, sel.cand_key, sel.cand_idx,
-                                       sel.info, slot_l, sc);
-    const int32_t* bt = sel.block_table + (int64_t)b * sel.bt_stride;
+                                       sel.info, sel.rs, bt, slot_l, sc);
     auto to_slot = [&](int t) { return t < 0 ? -1 : bt[t >> 6] * kPage + (t & (kPage - 1)); };
     if (s == 0 && (sel.topk_idx || sel.topk_slot)) {
       for (int i = threadIdx.x; i < k; i += kThreads) {
@@ -530,16 +531,17 @@ hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, cons
 }
 
 hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
-                                  const int32_t* seq_lens, const float* scores,
+                                  const int32_t* seq_lens, float* scores,
                                   int64_t score_stride, const TopkBuffers& t,
-                                  const int32_t* block_table, int bt_stride, int32_t* topk_idx,
-                                  int32_t* topk_slot, const uint16_t* q, const uint8_t* q8,
+                                  const IndexRescore& rs, const int32_t* block_table,
+                                  int bt_stride, int32_t* topk_idx, int32_t* topk_slot,
+                                  const uint16_t* q, const uint8_t* q8,
                                   const float* q_scale, const uint8_t* latent_pages,
                                   int64_t latent_page_stride, float latent_scale, int k,
                                   float softmax_scale, int num_splits, uint16_t* out_bf16,
                                   float* lse, void* workspace, hipStream_t st) {
   const SelectArgs sel{cu_q, seq_lens, num_seqs, scores, score_stride, t.plan.num_groups,
-                       (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info, block_table,
+                       (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info, rs, block_table,
                        bt_stride, topk_idx, topk_slot};
   return launch_mla_common(&sel, n_q, q, q8, q_scale, latent_pages, latent_page_stride,
                            latent_scale, nullptr, k, softmax_scale, num_splits, nullptr, nullptr,

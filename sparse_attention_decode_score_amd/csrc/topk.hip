@@ -59,10 +59,10 @@ __global__ __launch_bounds__(256) void topk_group_kernel(
 // ---------------------------------------------------------------- pass 2
 __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int num_seqs,
-    const float* __restrict__ scores, int64_t score_stride, int k, int num_groups,
-    int64_t row_cap, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
-    const ChunkInfo* __restrict__ info, const int32_t* __restrict__ block_table, int bt_stride,
-    int32_t* __restrict__ topk_idx, int32_t* __restrict__ topk_slot) {
+    float* scores, int64_t score_stride, int k, int num_groups, int64_t row_cap,
+    const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
+    const ChunkInfo* __restrict__ info, IndexRescore rs, const int32_t* __restrict__ block_table,
+    int bt_stride, int32_t* __restrict__ topk_idx, int32_t* __restrict__ topk_slot) {
   __shared__ __attribute__((aligned(16))) uint32_t lkey[kFinalTile];
   __shared__ __attribute__((aligned(16))) int32_t lidx[kFinalTile];
   __shared__ int out[kMaxTopk];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   const int32_t* bt = block_table ? block_table + (int64_t)b * bt_stride : nullptr;
   FinalScratch sc{lkey, lidx, red, &note, bucket};
   const int n_out = final_select_row(row, n_vis, scores, score_stride, k, num_groups, row_cap,
-                                     cand_key, cand_idx, info, out, sc);
+                                     cand_key, cand_idx, info, rs, bt, out, sc);
 #pragma unroll 8
   for (int i = tid; i < k; i += kFinalThreads) {
     const int t = i < n_out ? out[i] : -1;
@@ -129,12 +129,14 @@ TopkBuffers topk_buffers(void* workspace, int n_q, int max_seq_len, int k) {
 
 hipError_t launch_topk_final(int num_seqs, int n_q, const int32_t* cu_q, const int32_t* seq_lens,
                              const float* scores, int64_t score_stride, int k,
-                             const TopkBuffers& t, const int32_t* block_table, int bt_stride,
-                             int32_t* topk_idx, int32_t* topk_slot, hipStream_t st) {
+                             const TopkBuffers& t, const IndexRescore& rs,
+                             const int32_t* block_table, int bt_stride, int32_t* topk_idx,
+                             int32_t* topk_slot, hipStream_t st) {
+  // (scores is written only when rs.q is set: it is then the caller's scratch)
   hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)n_q), dim3(kFinalThreads), 0, st, cu_q,
-                     seq_lens, num_seqs, scores, score_stride, k, t.plan.num_groups,
-                     (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info, block_table,
-                     bt_stride, topk_idx, topk_slot);
+                     seq_lens, num_seqs, const_cast<float*>(scores), score_stride, k,
+                     t.plan.num_groups, (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info,
+                     rs, block_table, bt_stride, topk_idx, topk_slot);
   return hipGetLastError();
 }
 
@@ -148,8 +150,9 @@ hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu
                      t.plan.num_groups, (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k, t, block_table,
-                           bt_stride, topk_idx, topk_slot, st);
+  return launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k, t,
+                           IndexRescore{nullptr, nullptr, nullptr, 0}, block_table, bt_stride,
+                           topk_idx, topk_slot, st);
 }
 
 }  // namespace dsa

@@ -59,7 +59,7 @@ def test_index_score_rejects_bad_host_args(L):
              ({9: 8447}, 1, "key_page_stride"), ({9: 8456}, 1, "key_page_stride"),
              ({11: 15}, 1, "bt_stride"), ({13: 999}, 1, "score_stride"),
              ({6: FAKE_ODD}, 1, "aligned"), ({14: 0}, 2, "cand_k"), ({14: 4097}, 2, "cand_k"),
-             ({16: cand_need - 1}, 3, "workspace"),
+             ({16: cand_need - 1}, 3, "workspace"), ({12: None, 15: None}, 1, "scores"),
              ({15: ctypes.c_void_p(0x10010)}, 1, "aligned")]
     for patch, status, word in cases:
         args = list(ok_args)
@@ -75,7 +75,7 @@ def test_topk_rejects_bad_host_args(L):
         need = L.dsa_topk_workspace_size(3, 1000, 2048)
         assert need > 0
         base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE,
-                ctypes.c_void_p(0x10000), need, fused, None]
+                ctypes.c_void_p(0x10000), need, fused, None, None, None, 0, None]
         for patch, status in [({7: 0}, 2), ({7: 4097}, 2), ({8: None}, 1), ({6: 10}, 1),
                               ({13: need - 1}, 3), ({12: None}, 3),
                               ({12: ctypes.c_void_p(0x10010)}, 1)]:
@@ -83,6 +83,18 @@ def test_topk_rejects_bad_host_args(L):
             for i, v in patch.items():
                 args[i] = v
             assert f(*args) == status, (fused, patch, _err())
+    # recomputation inputs: all or none, only with candidates, with a block table
+    base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE,
+            ctypes.c_void_p(0x10000), L.dsa_topk_workspace_size(3, 1000, 2048), 1,
+            FAKE, FAKE, FAKE, 8448, None]
+    for patch, word in [({16: None}, "all"), ({14: 0}, "from_candidates"),
+                        ({8: None, 11: None}, "block_table"), ({18: 8447}, "key_page_stride"),
+                        ({15: FAKE_ODD}, "aligned")]:
+        args = list(base)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == 1, (patch, _err())
+        assert word in _err(), (patch, _err())
     assert L.dsa_topk_workspace_size(0, 10, 10) == 0
     assert L.dsa_topk_workspace_size(4, 10, 5000) == 0
 
@@ -128,19 +140,21 @@ def test_topk_sparse_mla_rejects_bad_host_args(L):
     need = L.dsa_sparse_mla_workspace_size(4, 4)
     CW, WS = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
     # num_seqs, n_q, max_seq_len, cu_q, seq_lens, scores, score_stride, k, block_table,
-    # bt_stride, cand_ws, cand_bytes, topk_idx, topk_slot, q_bf16, q8, q_scale, latent,
-    # latent_stride, latent_scale, softmax_scale, S, out, lse, workspace, ws_bytes, stream
-    base = [2, 4, 1000, FAKE, FAKE, FAKE, 1000, 512, FAKE, 16, CW, cand, None, None, FAKE,
-            None, None, FAKE, 36864, ctypes.c_float(0.01), ctypes.c_float(0.04), 4, FAKE, FAKE,
-            WS, need, None]
+    # bt_stride, cand_ws, cand_bytes, q_idx, head_w, key_pages, key_stride, topk_idx,
+    # topk_slot, q_bf16, q8, q_scale, latent, latent_stride, latent_scale, softmax_scale, S,
+    # out, lse, workspace, ws_bytes, stream
+    base = [2, 4, 1000, FAKE, FAKE, FAKE, 1000, 512, FAKE, 16, CW, cand, None, None, None, 0,
+            None, None, FAKE, None, None, FAKE, 36864, ctypes.c_float(0.01),
+            ctypes.c_float(0.04), 4, FAKE, FAKE, WS, need, None]
     cases = [({0: 0}, 1, "num_seqs"), ({7: 0}, 2, "k"), ({7: 4097}, 2, "k"),
-             ({21: 65}, 2, "num_splits"), ({8: None}, 1, "block_table"),
+             ({25: 65}, 2, "num_splits"), ({8: None}, 1, "block_table"),
              ({5: None}, 1, "scores"), ({6: 999}, 1, "score_stride"), ({9: 15}, 1, "bt_stride"),
              ({10: None}, 3, "candidate"), ({11: cand - 1}, 3, "candidate"),
              ({10: ctypes.c_void_p(0x10010)}, 1, "cand_workspace"),
-             ({14: None}, 1, "query"), ({15: FAKE}, 1, "q8"), ({17: None}, 1, "latent_pages"),
-             ({18: 36863}, 1, "latent_page_stride"), ({22: None}, 1, "out_bf16"),
-             ({24: None}, 3, "workspace"), ({25: need - 1}, 3, "workspace")]
+             ({12: FAKE}, 1, "all"), ({12: FAKE, 13: FAKE, 14: FAKE, 15: 100}, 1, "key_page_stride"),
+             ({18: None}, 1, "query"), ({19: FAKE}, 1, "q8"), ({21: None}, 1, "latent_pages"),
+             ({22: 36863}, 1, "latent_page_stride"), ({26: None}, 1, "out_bf16"),
+             ({28: None}, 3, "workspace"), ({29: need - 1}, 3, "workspace")]
     for patch, status, word in cases:
         args = list(base)
         for i, v in patch.items():
@@ -148,7 +162,7 @@ def test_topk_sparse_mla_rejects_bad_host_args(L):
         assert f(*args) == status, (patch, _err())
         assert word in _err(), (patch, _err())
     args = list(base)
-    args[7], args[21] = 3, 4                     # more splits than selected tokens
+    args[7], args[25] = 3, 4                     # more splits than selected tokens
     assert f(*args) == 1 and "num_splits" in _err()
 
 

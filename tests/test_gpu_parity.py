@@ -350,7 +350,9 @@ def _end_to_end(wl, rows, num_splits=None):
                         batch.block_table, batch.q_mla, batch.latent_pool, batch.latent_scale,
                         batch.softmax_scale, max(wl.q_per_seq))
     torch.cuda.synchronize()
-    scores = step.scores
+    # the default step stores no scores (the final pass recomputes what it re-reads); the
+    # scores come from a stored-score indexer call, whose candidates are bitwise the same
+    scores = step.scores if step.store_scores else run_scores(batch)
     idx = step.topk_idx.cpu().numpy()
     slots = step.topk_slot.cpu().numpy()
     out = out.float().cpu().numpy()
@@ -594,3 +596,108 @@ def test_select_in_attention_resends_groups_that_hold_the_winners():
     assert torch.equal(i1, i2) and torch.equal(t1, t2)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert ((i2[0] >= 5120) & (i2[0] < 6144)).sum().item() > 200
+
+
+# --------------------------------------------- candidates with no stored scores (recomputed)
+def _index(batch, k, store_scores, ws_fill=0):
+    wl = batch.wl
+    scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    ws = torch.full((dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k),), ws_fill,
+                    dtype=torch.uint8, device=DEV)
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, scores if store_scores else None,
+                        max_seq_len=wl.max_seq_len, max_q_per_seq=max(wl.q_per_seq),
+                        cand_k=k, cand_workspace=ws)
+    torch.cuda.synchronize()
+    return scores, ws
+
+
+def _final(batch, k, scores, ws, rescore):
+    wl = batch.wl
+    idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, idx, slot, ws,
+                 max_seq_len=wl.max_seq_len, from_candidates=True,
+                 rescore=(batch.q_idx, batch.head_w, batch.key_pool) if rescore else None)
+    torch.cuda.synchronize()
+    return idx, slot
+
+
+def _boost_pages(batch, b, pages, factor=1000.0):
+    """Multiplies the key scales of logical pages `pages` of request b (scores scale too)."""
+    bt = batch.block_table.cpu().numpy()
+    for page in pages:
+        batch.key_pool[int(bt[b, page]), 8192:].view(torch.float32).mul_(factor)
+    torch.cuda.synchronize()
+
+
+def _check_no_scores_matches(batch, k, expect_rescored):
+    """Stored-scores path vs no-scores path: candidates, selection and the recomputed
+    scores (bitwise), and whether anything was recomputed."""
+    wl = batch.wl
+    s_ref, ws_ref = _index(batch, k, True)
+    s_none, ws_none = _index(batch, k, False)
+    assert bool(torch.isnan(s_none).all())          # the indexer stored nothing
+    assert torch.equal(ws_ref, ws_none)             # same candidates, byte for byte
+    i1, t1 = _final(batch, k, s_ref, ws_ref, False)
+    i2, t2 = _final(batch, k, s_none, ws_none, True)
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+    n_rescored = 0
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        got = s_none[row, : pos + 1]
+        done = ~torch.isnan(got)
+        n_rescored += int(done.sum().item())
+        assert torch.equal(got[done], s_ref[row, : pos + 1][done]), row
+    assert (n_rescored > 0) == expect_rescored, n_rescored
+    return i2, n_rescored
+
+
+@pytest.mark.parametrize("wl", FUSED, ids=lambda w: w.name)
+def test_no_stored_scores_is_bitwise_the_stored_scores_path(wl):
+    say("no scores", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    _check_no_scores_matches(batch, wl.topk, expect_rescored=False)
+
+
+def test_no_stored_scores_recomputes_flagged_groups_exactly():
+    # four groups hold ~500 of the winners but send 56 candidates each: flagged, recomputed
+    wl = synth.custom([40000], [2], topk=2048, seed=64, name="rescore-skew")
+    batch = synth.make_batch(wl, DEV)
+    _boost_pages(batch, 0, range(80, 96))
+    idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
+    assert n <= 2 * 4 * 256                          # only the flagged groups (both rows)
+    assert ((idx[0] >= 5120) & (idx[0] < 6144)).sum().item() > 200
+
+
+def test_no_stored_scores_recomputes_the_whole_row_when_the_resend_is_too_large():
+    # one boosted page in every fourth group: 128 groups each hold ~32 winners and send 16,
+    # so nearly all are flagged and the resend would not fit on chip: the whole row is
+    # recomputed, filtered by the candidates' k-th key and selected again
+    L = 131072
+    wl = synth.custom([L], [1], topk=2048, seed=65, name="rescore-all")
+    batch = synth.make_batch(wl, DEV)
+    _boost_pages(batch, 0, range(0, L // 64, 16))
+    idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
+    assert n == L
+
+
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_select_in_attention_with_no_stored_scores(num_splits):
+    wl = synth.custom([40000, 9000], [2, 1], topk=2048, seed=66, name="rescore-attend")
+    batch = synth.make_batch(wl, DEV)
+    _boost_pages(batch, 0, range(80, 96))
+    i1, t1, o1, l1 = _select_attend(batch, 2048, num_splits)
+    k = 2048
+    s_none, ws = _index(batch, k, False)
+    idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((wl.n_q, 96, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((wl.n_q, 96), float("nan"), dtype=torch.float32, device=DEV)
+    dsa.dsa_topk_sparse_mla(batch.cu_q, batch.seq_lens, s_none, k, batch.block_table, ws,
+                            batch.q_mla, batch.latent_pool, batch.latent_scale,
+                            batch.softmax_scale, num_splits, max_seq_len=wl.max_seq_len,
+                            out=out, lse=lse, topk_idx=idx, topk_slot=slot,
+                            rescore=(batch.q_idx, batch.head_w, batch.key_pool))
+    torch.cuda.synchronize()
+    assert torch.equal(i1, idx) and torch.equal(t1, slot)
+    assert torch.equal(o1, out) and torch.equal(l1, lse)
