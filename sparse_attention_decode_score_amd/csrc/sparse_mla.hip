@@ -214,29 +214,37 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         if (lane == 0) valid_mask[buf] = m;
       }
     };
+    // Every wave executes the same barriers: barrier 1, three per tile (A, B, C) and the two
+    // of the compute waves' finalize step.  Tile i lives in ring[i % kRing].  Under load a
+    // gather request can wait a long time to issue (every workgroup of the chip gathers at
+    // once), and a loader wave late for a barrier holds all six compute waves, so the
+    // loader requests one tile per step and at most two are in flight: tile 0 alone
+    // first, tile 1 after barrier 1; in the step of tile t it writes tile t+1 to the free
+    // LDS buffer between A and B, and requests tile t+kRing between B and C.  Steps past
+    // the last tile only move zero rows, after the compute waves are done with the ring.
+    static_assert(kRing == 3, "the schedule below is written for a ring of three tiles");
     TileRegs ring[kRing];
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) issue(i, ring[i]);
+    issue(0, ring[0]);
     store(0, ring[0], 0);
-    issue(kRing, ring[0]);
     __syncthreads();  // barrier 1: tile 0 and the query are in LDS
-    // every wave executes the same barriers: three per tile and the two of the compute
-    // waves' finalize step.  The loader's step for tile t writes tile t+1 (one LDS buffer
-    // ahead) and refills its registers with tile t+1+kRing; steps past the last tile only
-    // move zero rows and run after the compute waves are done with the LDS ring.
+    issue(1, ring[1]);
+    __syncthreads();  // tile 0: A
+    issue(2, ring[2]);
+    store(1, ring[1], 1);
+    __syncthreads();  // B
+    issue(3, ring[0]);
+    __syncthreads();  // C
 #pragma unroll 1
-    for (int t0 = 0; t0 < n_tiles; t0 += kRing) {
+    for (int t0 = 1; t0 < n_tiles; t0 += kRing) {
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
-        const int t = t0 + u;
-        const int set = (u + 1) % kRing;
-        store(t + 1, ring[set], (t + 1) & 1);
-        issue(t + 1 + kRing, ring[set]);
-        if (t < n_tiles) {
-          __syncthreads();
-          __syncthreads();
-          __syncthreads();
-        }
+        const int t = t0 + u;  // t % kRing == (1 + u) % kRing
+        const bool live = t < n_tiles;
+        if (live) __syncthreads();  // A
+        store(t + 1, ring[(u + 2) % kRing], (t + 1) & 1);
+        if (live) __syncthreads();  // B
+        issue(t + kRing, ring[(u + 1) % kRing]);
+        if (live) __syncthreads();  // C
       }
     }
     __syncthreads();
