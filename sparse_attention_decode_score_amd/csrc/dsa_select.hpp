@@ -399,9 +399,14 @@ __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], i
         if (lane == 0) buf[w] = c;
       }
       __syncthreads();
+      // all counts in vector reads (no read waits on another); unused slots count as -1 < k
       int cs[kFinalWaves];
 #pragma unroll
-      for (int j = 1; j < kFinalWaves; ++j) cs[j] = j <= n_t ? buf[j] : -1;  // -1 < k
+      for (int j = 0; j < kFinalWaves; j += 4) {
+        const v4i c4 = *reinterpret_cast<const v4i*>(buf + j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cs[j + q] = (j + q >= 1 && j + q <= n_t) ? c4[q] : -1;
+      }
       int digit = 0, c_dig = c_K, c_next = c_hi;
 #pragma unroll
       for (int j = 1; j < kFinalWaves; ++j) {

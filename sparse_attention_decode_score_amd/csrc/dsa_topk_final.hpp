@@ -162,18 +162,27 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
         constexpr int E = decltype(e_tag)::value;
         uint32_t kv[E];
         int vv[E];
+        // keys first, then the token indices: the search waits for the keys only, and the
+        // index loads are still in flight until the compaction needs them
+        // (a quad past the end reads element 0 and is masked below)
+        v4i a[E / 4], c[E / 4];
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
           const int e = tid * E + 4 * q;
-          v4i a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-          if (e < n_cand) {
-            a = *reinterpret_cast<const v4i*>(ck + e);
-            c = *reinterpret_cast<const v4i*>(ci + e);
-          }
+          a[q] = *reinterpret_cast<const v4i*>(ck + (e < n_cand ? e : 0));
+        }
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const int e = tid * E + 4 * q;
+          c[q] = *reinterpret_cast<const v4i*>(ci + (e < n_cand ? e : 0));
+        }
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const bool in = tid * E + 4 * q < n_cand;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            kv[4 * q + j] = (uint32_t)a[j];
-            vv[4 * q + j] = c[j];
+            kv[4 * q + j] = in ? (uint32_t)a[q][j] : kSentinel;
+            vv[4 * q + j] = c[q][j];
           }
         }
         kth = block_topk_regs<E>(kv, vv, k, out, red, note_p, bucket);
