@@ -85,6 +85,34 @@ def _traffic_from_profile():
     return d.get("hbm_bytes_per_launch")
 
 
+def cache_append_timing(torch, dsa, batch, wl, steps):
+    """dsa_cache_append of one new token per query row (its own position), timed with events
+    over `steps` calls; run after everything else (it rewrites those tokens)."""
+    import numpy as np
+    bt = batch.block_table.cpu().numpy()
+    slots = []
+    for b, pos in wl.row_positions():
+        slots.append(int(bt[b][pos // PAGE]) * PAGE + pos % PAGE)
+    n = len(slots)
+    slots_d = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(99)
+    key = torch.randn((n, 128), generator=g, device="cuda").to(torch.bfloat16)
+    lat = torch.randn((n, 576), generator=g, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        dsa.dsa_cache_append(slots_d, key, lat, batch.latent_scale, batch.key_pool, batch.latent_pool)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dsa.dsa_cache_append(slots_d, key, lat, batch.latent_scale, batch.key_pool, batch.latent_pool)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    return {"tokens": n, "us_per_call": round(us, 2),
+            "note": "one new token per query row: its index key (132 B) and latent (576 B) "
+                    "quantised into the paged caches; calls back to back, caches warm"}
+
+
 def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
     """Times the oracle (as it stands) on a bounded sample of the same workload: the rows are
     taken in turn (cycling) until budget_s seconds of oracle time have been spent, and the
@@ -311,6 +339,8 @@ def main():
         rows = list(range(0, wl.n_q, max(1, wl.n_q // 8)))
         cpu = cpu_baseline(batch, rows, budget_s=args.cpu_budget)
 
+    append = cache_append_timing(torch, dsa, batch, wl, steps=args.steps)
+
     rec = {
         "metric": "DSA decode µs/layer & HBM GB/s (%peak) at 128K ctx, batch 32",
         "value": round(value, 2),
@@ -349,6 +379,7 @@ def main():
         "stream_read_ceiling_GBps": round(ceiling, 1),
         "wall_s_timed_loop": round(t_wall, 4),
         "cpu_baseline": cpu,
+        "cache_append": append,
     }
     print(json.dumps(rec, ensure_ascii=False))
 

@@ -17,6 +17,7 @@
  *                         row's final top-k pass over the stage-1 candidates
  *   dsa_lse_combine       stage 4  LSE merge of splits      ("Decode context parallelism with the
  *                                                             sparse indexer")
+ *   dsa_cache_append      quantises the step's new tokens into the two paged caches
  *   dsa_quantize_q        the query quantisation the stages 1 and 3 apply internally
  *                         (fused indexer front of "Fused low-latency decode for DSA layers"),
  *                         exposed so callers and tests can see the exact FP8 codes.
@@ -229,6 +230,28 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
  */
 dsa_status dsa_lse_combine(int32_t num_splits, int32_t n_q, const float* o_part,
                            const float* lse_part, void* out_bf16, float* lse, void* stream);
+
+/*
+ * Cache append (the step just before the path in a decode): quantises the step's new tokens
+ * into the two paged caches at their physical slots, in the layouts above.  One FP8 index
+ * key of 132 bytes with its scale per token ("What changed in Kimi K3.1 Pro") and a 576-byte
+ * FP8 latent ("Packed KV cache for three kinds of state"); the page's fused indexer front
+ * writes the new token's index key ("Fused low-latency decode for DSA layers").
+ *   index key: s = absmax / 448 in fp32 (1 if the key is all zero), stored as the token's
+ *              fp32 scale; codes = E4M3 round-to-nearest-even of k / s, saturating at 448.
+ *   latent:    codes = E4M3 round-to-nearest-even of x / latent_scale (the cache's
+ *              per-tensor scale), saturating at 448.
+ * Divisions are IEEE fp32.
+ *   n_tok (host) >= 0; slots int32 [n_tok]: page * 64 + offset, -1 = skip (no two valid
+ *   entries may be equal); key_bf16 bf16 [n_tok][128] and/or latent_bf16 bf16
+ *   [n_tok][576] (either may be NULL: that cache is not touched), 16-byte aligned;
+ *   key_pages / latent_pages and their strides as for stages 1 and 3.  Only the bytes of
+ *   the given slots are written.
+ */
+dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key_bf16,
+                            const void* latent_bf16, float latent_scale, void* key_pages,
+                            int64_t key_page_stride, void* latent_pages,
+                            int64_t latent_page_stride, void* stream);
 
 /*
  * Per-(row, head) E4M3 query quantisation used inside stages 1 and 3.

@@ -166,6 +166,44 @@ def read_latents(latent_pool: np.ndarray, slots: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------
+# Cache append: the new tokens' index keys and latents into the paged caches
+# --------------------------------------------------------------------------------------
+def cache_append(key_pool: np.ndarray, latent_pool: np.ndarray, slots, key_bf16, latent_bf16,
+                 latent_scale: float) -> None:
+    """Quantises and writes tokens into the paged caches by physical slot (in place).
+
+    The K3.1 page stores one FP8 index key per token, 132 bytes with its scale ("What
+    changed in Kimi K3.1 Pro" / Kimi K3.1 Proの変更点), and a 576-byte FP8 latent ("Packed KV
+    cache for three kinds of state" / パック型KVキャッシュ); its fused indexer front writes
+    the new token's index key in the same kernel as the query prep ("Fused low-latency
+    decode for DSA layers").  Readings (the page fixes neither): the key's scale is one
+    fp32 per token, s = absmax / 448 (1 for an all-zero key), and its codes are the E4M3
+    round-to-nearest-even (saturating) of k / s evaluated in fp32; the latent's codes are
+    the E4M3 of x / latent_scale in fp32 with the cache's per-tensor scale.  Slot -1 is
+    skipped.  key_bf16 [n, 128] / latent_bf16 [n, 576] are bf16 bit patterns (uint16);
+    either may be None (that cache is left alone).
+    """
+    slots = np.asarray(slots, dtype=np.int64)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        page, o = int(slot // PAGE), int(slot % PAGE)
+        if key_bf16 is not None:
+            k = bf16_value(np.asarray(key_bf16)[i]).astype(np.float32)
+            a = np.float32(np.max(np.abs(k)))
+            sc = np.float32(a / np.float32(E4M3_MAX)) if a > 0 else np.float32(1.0)
+            codes = e4m3_encode((k / sc).astype(np.float32))
+            for d in range(IDX_DIM):
+                key_pool[page, (d // 16) * 1024 + o * 16 + d % 16] = codes[d]
+            off = IDX_PAGE_KEY_BYTES + 4 * o
+            key_pool[page, off:off + 4] = np.array([sc], dtype=np.float32).view(np.uint8)
+        if latent_bf16 is not None:
+            x = bf16_value(np.asarray(latent_bf16)[i]).astype(np.float32)
+            latent_pool[page, o * LAT_ROW:(o + 1) * LAT_ROW] = e4m3_encode(
+                (x / np.float32(latent_scale)).astype(np.float32))
+
+
+# --------------------------------------------------------------------------------------
 # Stage 1: lightning-indexer score
 # --------------------------------------------------------------------------------------
 def index_scores(q_idx: np.ndarray, head_w: np.ndarray, key_codes: np.ndarray,

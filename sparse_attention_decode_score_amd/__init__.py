@@ -60,11 +60,12 @@ def lib() -> ctypes.CDLL:
                                           _SZ, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I64,
                                           _F32, _F32, _I32, _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
+        L.dsa_cache_append.argtypes = [_I32, _P, _P, _P, _F32, _P, _I64, _P, _I64, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
         for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
-                  "dsa_lse_combine", "dsa_quantize_q"):
+                  "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -290,6 +291,28 @@ def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Ten
     _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
     _check(lib().dsa_lse_combine(S, n_q, _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse),
                                  _stream(stream)))
+
+
+def dsa_cache_append(slots: torch.Tensor, key: Optional[torch.Tensor],
+                     latent: Optional[torch.Tensor], latent_scale: float,
+                     key_pages: Optional[torch.Tensor], latent_pages: Optional[torch.Tensor], *,
+                     key_page_stride: Optional[int] = None,
+                     latent_page_stride: Optional[int] = None, stream=None) -> None:
+    """Quantises new tokens (index keys bf16 [n, 128], latents bf16 [n, 576]) into the paged
+    caches at their physical slots (int32 [n], -1 = skip)."""
+    n = slots.shape[0]
+    _expect(slots, "slots", torch.int32, (n,))
+    if key is not None:
+        _expect(key, "key", torch.bfloat16, (n, IDX_DIM))
+    if latent is not None:
+        _expect(latent, "latent", torch.bfloat16, (n, LATENT_DIM))
+    ks = (key_page_stride if key_page_stride is not None
+          else (key_pages.stride(0) * key_pages.element_size() if key_pages is not None else 0))
+    ls = (latent_page_stride if latent_page_stride is not None
+          else (latent_pages.stride(0) * latent_pages.element_size() if latent_pages is not None else 0))
+    _check(lib().dsa_cache_append(int(n), _ptr(slots), _ptr(key), _ptr(latent),
+                                  float(latent_scale), _ptr(key_pages), int(ks),
+                                  _ptr(latent_pages), int(ls), _stream(stream)))
 
 
 class DecodeStep:

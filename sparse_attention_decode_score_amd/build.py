@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdsa.so")
-SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "lse_combine.hip", "capi.cpp"]
+SOURCES = ["index_score.hip", "topk.hip", "sparse_mla.hip", "lse_combine.hip", "cache_append.hip",
+           "capi.cpp"]
 # measurement kernels used by the benchmark only (streaming-read ceiling, page-read rate)
 PROBE_LIB = os.path.join(LIBDIR, "libdsa_probe.so")
 PROBE_SOURCES = ["bandwidth_probe.hip"]

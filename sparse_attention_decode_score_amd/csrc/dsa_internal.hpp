@@ -81,6 +81,13 @@ hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
                                   float softmax_scale, int num_splits, uint16_t* out_bf16,
                                   float* lse, void* workspace, hipStream_t st);
 
+// New tokens' index keys (bf16 [n][128]) and latents (bf16 [n][576]) quantised into the
+// paged caches at their physical slots (-1: skipped); key or lat may be null.
+hipError_t launch_cache_append(int n_tok, const int32_t* slots, const uint16_t* key,
+                               const uint16_t* lat, float lat_scale, uint8_t* key_pages,
+                               int64_t key_page_stride, uint8_t* lat_pages,
+                               int64_t lat_page_stride, hipStream_t st);
+
 hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
                               uint16_t* out_bf16, float* lse, hipStream_t st);
 hipError_t launch_lse_combine_f16(int num_splits, int n_q, const uint16_t* o_part,

@@ -29,7 +29,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"dsa_index_score", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_sparse_mla_workspace_size", "dsa_topk_sparse_mla", "dsa_lse_combine", "dsa_quantize_q", "dsa_last_error",
+            "dsa_sparse_mla_workspace_size", "dsa_topk_sparse_mla", "dsa_lse_combine", "dsa_cache_append", "dsa_quantize_q", "dsa_last_error",
             "dsa_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -177,3 +177,22 @@ def test_python_binding_refuses_host_tensors(L):
     q = torch.zeros((1, 32, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dsa.dsa_quantize_q(q, torch.zeros((1, 32, 128), dtype=torch.uint8), torch.zeros((1, 32)))
+
+
+def test_cache_append_rejects_bad_host_args(L):
+    f = L.dsa_cache_append
+    base = [4, FAKE, FAKE, FAKE, ctypes.c_float(0.01), FAKE, 8448, FAKE, 36864, None]
+    for patch, word in [({0: -1}, "n_tok"), ({1: None}, "slots"), ({2: None, 3: None}, "give"),
+                        ({5: None}, "key_pages"), ({6: 8447}, "key_page_stride"),
+                        ({7: None}, "latent_pages"), ({8: 100}, "latent_page_stride"),
+                        ({4: ctypes.c_float(0.0)}, "latent_scale"), ({2: FAKE_ODD}, "aligned")]:
+        args = list(base)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == 1, (patch, _err())
+        assert word in _err(), (patch, _err())
+    # a cache that is not given is not checked
+    args = list(base)
+    args[3], args[7], args[8] = None, None, 0
+    args[0] = -1
+    assert f(*args) == 1 and "n_tok" in _err()

@@ -701,3 +701,61 @@ def test_select_in_attention_with_no_stored_scores(num_splits):
     torch.cuda.synchronize()
     assert torch.equal(i1, idx) and torch.equal(t1, slot)
     assert torch.equal(o1, out) and torch.equal(l1, lse)
+
+
+# ------------------------------------------------------------------------ cache append
+def _bf16_bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("n,key_mag,lat_sat,pad", [(1, 1.0, False, 0), (37, 1.0, True, 0),
+                                                   (300, 1e-3, False, 64), (64, 300.0, True, 16)])
+def test_cache_append_bit_exact(n, key_mag, lat_sat, pad):
+    say("append", n, key_mag, lat_sat, pad)
+    pages = 24
+    g = torch.Generator().manual_seed(n)
+    key_pool = torch.full((pages, 8448 + pad), 0x7F, dtype=torch.uint8)
+    key_pool[:, 8192:8448] = torch.full((pages, 64), float("nan")).view(torch.uint8)
+    lat_pool = torch.full((pages, 64 * 576 + pad), 0x7F, dtype=torch.uint8)
+    slots = torch.randperm(pages * 64, generator=g)[:n].to(torch.int32)
+    if n > 2:
+        slots[1] = -1
+    key = (torch.randn((n, 128), generator=g) * key_mag).to(torch.bfloat16)
+    if n > 3:
+        key[3] = 0.0
+    lat = (torch.randn((n, 576), generator=g) * torch.logspace(-3, 2, n).view(n, 1)).to(torch.bfloat16)
+    lat_scale = float(np.float32(lat.float().abs().max() / (1000.0 if lat_sat else 448.0)))
+    kp_ref, lp_ref = key_pool.numpy().copy(), lat_pool.numpy().copy()
+    O.cache_append(kp_ref, lp_ref, slots.numpy(), _bf16_bits(key), _bf16_bits(lat), lat_scale)
+    kp, lp = key_pool.to(DEV), lat_pool.to(DEV)
+    dsa.dsa_cache_append(slots.to(DEV), key.to(DEV), lat.to(DEV), lat_scale, kp, lp)
+    torch.cuda.synchronize()
+    assert np.array_equal(kp.cpu().numpy(), kp_ref)
+    assert np.array_equal(lp.cpu().numpy(), lp_ref)
+
+
+def test_cache_append_keys_only_leaves_latents_and_feeds_the_indexer():
+    # append the last token of each request into a batch's caches, then score: the new
+    # token's score equals the oracle's on the appended (oracle-quantised) key
+    wl = synth.custom([1000, 70], [1, 1], topk=64, seed=71)
+    batch = synth.make_batch(wl, DEV)
+    bt = batch.block_table.cpu().numpy()
+    g = torch.Generator().manual_seed(71)
+    key = torch.randn((2, 128), generator=g).to(torch.bfloat16)
+    slots = torch.tensor([O.physical_slot(bt[b], np.array([L - 1]))[0]
+                          for b, L in enumerate(wl.seq_lens)], dtype=torch.int32)
+    lat_before = batch.latent_pool.clone()
+    kp_ref = batch.key_pool.cpu().numpy().copy()
+    O.cache_append(kp_ref, None, slots.numpy(), _bf16_bits(key), None, 1.0)
+    dsa.dsa_cache_append(slots.to(DEV), key.to(DEV), None, 1.0, batch.key_pool, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(batch.key_pool.cpu().numpy(), kp_ref)
+    assert torch.equal(batch.latent_pool, lat_before)
+    scores = run_scores(batch)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        kc, ks = O.read_index_keys(kp_ref, bt[b], pos + 1)
+        ref = O.index_scores(batch.q_idx[row].cpu().double().numpy(), batch.head_w[row].cpu().numpy(),
+                             kc, ks)
+        mag = O.index_scores(batch.q_idx[row].cpu().double().numpy(),
+                             np.abs(batch.head_w[row].cpu().numpy()), kc, ks)
+        check_scores(scores[row, : pos + 1].cpu().numpy(), ref, mag, f"append row {row}")

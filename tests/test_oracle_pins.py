@@ -333,3 +333,58 @@ def test_decode_row_small_batch(small_batch):
             o_d, l_d = O.dense_mla(qm[i], lc[:pos + 1], b.latent_scale, b.softmax_scale)
             np.testing.assert_allclose(out["o"], o_d, rtol=1e-10, atol=1e-13)
             np.testing.assert_allclose(out["lse"], l_d, rtol=1e-12)
+
+
+# ------------------------------------------------------------------------ cache append
+def _append_inputs(seed, n, scale_mag=1.0):
+    rng = np.random.default_rng(seed)
+    k = (rng.normal(size=(n, 128)) * scale_mag).astype(np.float32)
+    x = rng.normal(size=(n, 576)).astype(np.float32)
+    kb = torch.from_numpy(k).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return kb, xb
+
+
+def test_cache_append_codes_scales_and_layout():
+    pages, n = 6, 40
+    key_pool = np.full((pages, 8448), 0x7F, dtype=np.uint8)
+    key_pool[:, 8192:] = np.full((pages, 64), np.nan, dtype=np.float32).view(np.uint8)
+    lat_pool = np.full((pages, 64 * 576), 0x7F, dtype=np.uint8)
+    rng = np.random.default_rng(3)
+    slots = rng.choice(pages * 64, size=n, replace=False).astype(np.int64)
+    slots[5] = -1                                      # skipped
+    kb, xb = _append_inputs(4, n)
+    kb[7] = 0                                          # all-zero key: scale 1, codes 0
+    kb[9] = torch.tensor([1e-30] * 128).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    lat_scale = np.float32(0.0123)
+    key_before, lat_before = key_pool.copy(), lat_pool.copy()
+    O.cache_append(key_pool, lat_pool, slots, kb, xb, float(lat_scale))
+    kf = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    xf = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    touched_k = np.zeros_like(key_pool, dtype=bool)
+    touched_l = np.zeros_like(lat_pool, dtype=bool)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        page, o = int(slot // 64), int(slot % 64)
+        codes, scales = O.read_index_keys(key_pool, np.array([page]), 64)
+        a = np.float32(np.abs(kf[i]).max())
+        sc = np.float32(a / np.float32(448)) if a > 0 else np.float32(1)
+        assert scales[o] == sc
+        # the codes are torch's own E4M3 conversion of k / s in fp32
+        assert np.array_equal(codes[o], _torch_e4m3(kf[i] / sc)), i
+        lat = O.read_latents(lat_pool, np.array([slot]))[0]
+        assert np.array_equal(lat, _torch_e4m3(xf[i] / lat_scale)), i
+        for d in range(128):
+            touched_k[page, (d // 16) * 1024 + o * 16 + d % 16] = True
+        touched_k[page, 8192 + 4 * o: 8192 + 4 * o + 4] = True
+        touched_l[page, o * 576:(o + 1) * 576] = True
+    # nothing else changed
+    assert np.array_equal(key_pool[~touched_k], key_before[~touched_k])
+    assert np.array_equal(lat_pool[~touched_l], lat_before[~touched_l])
+    # the zero key and the absmax element
+    p7, o7 = int(slots[7] // 64), int(slots[7] % 64)
+    c7, s7 = O.read_index_keys(key_pool, np.array([p7]), 64)
+    assert s7[o7] == 1.0 and (c7[o7] == 0).all()
+    c0, s0 = O.read_index_keys(key_pool, np.array([int(slots[0] // 64)]), 64)
+    assert np.abs(O.e4m3_decode(c0[int(slots[0] % 64)])).max() == 448.0
