@@ -90,6 +90,29 @@ def e4m3_encode(x) -> np.ndarray:
     return (code.astype(np.int64) | sign).astype(np.uint8)
 
 
+# MXFP4 (OCP microscaling): E2M1 elements in blocks of 32 sharing one E8M0 scale.  The K3.1
+# page's opt-in MXFP4 index key is 68 bytes with its scales ("Packed KV cache for three kinds
+# of state" / パック型KVキャッシュ, "Native MXFP4 indexer" / ネイティブMXFP4インデクサー):
+# 128 E2M1 values (64 bytes) and one E8M0 scale per 32 dimensions (4 bytes).
+E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(nibbles) -> np.ndarray:
+    """E2M1 nibble -> value: bit 3 sign, 2-bit exponent (bias 1), 1-bit mantissa; exponent 0
+    is subnormal (m * 0.5), otherwise (1 + m/2) * 2^(e-1).  No NaN or infinity."""
+    c = np.asarray(nibbles, dtype=np.int64) & 0xF
+    e, m = (c >> 1) & 3, c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def e8m0_value(b) -> np.ndarray:
+    """E8M0 scale byte -> 2^(b - 127); 0xFF is NaN."""
+    b = np.asarray(b, dtype=np.int64)
+    with np.errstate(over="ignore"):
+        return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
 def bf16_value(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> fp64: a bf16 is the top 16 bits of an fp32."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
@@ -157,6 +180,30 @@ def read_index_keys(key_pool: np.ndarray, block_table_row: np.ndarray, n: int):
     return codes, scales
 
 
+MX_PAGE_KEY_BYTES = PAGE * IDX_DIM // 2   # 4096 bytes of E2M1 codes, then 64 x 4 scale bytes
+MX_PAGE_BYTES = MX_PAGE_KEY_BYTES + PAGE * 4  # 4352 = 64 x 68
+
+
+def read_index_keys_mxfp4(key_pool: np.ndarray, block_table_row: np.ndarray, n: int):
+    """Key values [n, 128] (fp64) of logical tokens 0..n-1 of one request, MXFP4 cache.
+
+    MXFP4 index-key page (4,352 B): block b (dims 32b .. 32b+31) of token o is 16 bytes at
+    b * 1024 + o * 16, byte j holding dims 32b + 2j (low nibble) and 32b + 2j + 1 (high
+    nibble); the E8M0 scale of block b of token o is the byte at 4096 + 4 * o + b.
+    """
+    pool = np.asarray(key_pool, dtype=np.uint8)
+    vals = np.empty((n, IDX_DIM), dtype=np.float64)
+    for t in range(0, n, PAGE):
+        page = pool[int(block_table_row[t // PAGE])]
+        cnt = min(PAGE, n - t)
+        blocks = page[:MX_PAGE_KEY_BYTES].reshape(4, PAGE, 16)          # [block, token, byte]
+        by = blocks.transpose(1, 0, 2)[:cnt].astype(np.int64)           # [tok, block, byte]
+        nib = np.stack([by & 0xF, by >> 4], axis=-1).reshape(cnt, 4, 32)  # dims in order
+        sc = page[MX_PAGE_KEY_BYTES:MX_PAGE_KEY_BYTES + 4 * PAGE].reshape(PAGE, 4)[:cnt]
+        vals[t:t + cnt] = (e2m1_decode(nib) * e8m0_value(sc)[:, :, None]).reshape(cnt, IDX_DIM)
+    return vals
+
+
 def read_latents(latent_pool: np.ndarray, slots: np.ndarray) -> np.ndarray:
     """Latent codes [len(slots), 576] of physical slots (page * 64 + offset)."""
     pool = np.asarray(latent_pool, dtype=np.uint8)
@@ -222,6 +269,18 @@ def index_scores(q_idx: np.ndarray, head_w: np.ndarray, key_codes: np.ndarray,
     k = e4m3_decode(key_codes)                                  # [n, 128]
     logits = (q @ k.T) * np.asarray(key_scales, np.float64)[None, :]   # [32, n]
     w = np.asarray(head_w, dtype=np.float64)[:, None]           # [32, 1]
+    score = np.sum(w * np.maximum(logits, 0.0), axis=0)
+    return score.astype(np.float32)
+
+
+def index_scores_values(q_idx: np.ndarray, head_w: np.ndarray, key_values: np.ndarray,
+                        quantize_query: bool = True) -> np.ndarray:
+    """The same score for keys given as values k_t [n, 128] (the MXFP4 keys of the "Native
+    MXFP4 indexer" section, whose block scales are part of the values, so there is no
+    per-token scale): score_t = sum_h w_h * ReLU(q_h . k_t), fp64, rounded once to fp32."""
+    q = dequantized_query(q_idx) if quantize_query else np.asarray(q_idx, np.float64)
+    logits = q @ np.asarray(key_values, np.float64).T                # [32, n]
+    w = np.asarray(head_w, dtype=np.float64)[:, None]
     score = np.sum(w * np.maximum(logits, 0.0), axis=0)
     return score.astype(np.float32)
 

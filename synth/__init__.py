@@ -46,6 +46,7 @@ MLA_HEADS = 96
 LAT_DIM = 576
 V_DIM = 512
 IDX_PAGE_BYTES = PAGE * IDX_DIM + PAGE * 4   # 8448
+MX_PAGE_BYTES = PAGE * IDX_DIM // 2 + PAGE * 4   # 4352: MXFP4 index keys, 68 B per token
 LAT_PAGE_BYTES = PAGE * LAT_DIM              # 36864
 E4M3_NAN = 0x7F
 E4M3_MAX = 448.0
@@ -62,6 +63,7 @@ class Workload:
     topk: int = 2048
     num_splits: int = 1        # split count used for the sparse-attention stage
     seed: int = 0
+    key_format: str = "e4m3"   # index-key cache: "e4m3" (132 B/token) or "mxfp4" (68 B/token)
 
     @property
     def num_seqs(self) -> int:
@@ -101,15 +103,18 @@ def workload(name: str) -> Workload:
         return Workload("million", (1048576,), (5,), 2048, 32, seed=3)
     if name == "prefill":
         return Workload("prefill", (152048,), (2048,), 2048, 1, seed=4)
+    if name.endswith("-mxfp4") and name[:-6] in WORKLOADS:
+        return dataclasses.replace(workload(name[:-6]), name=name, key_format="mxfp4")
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny", "spec", "long", "million", "prefill")
 
 
-def custom(seq_lens, q_per_seq, topk=2048, num_splits=1, seed=12345, name="custom") -> Workload:
+def custom(seq_lens, q_per_seq, topk=2048, num_splits=1, seed=12345, name="custom",
+           key_format="e4m3") -> Workload:
     return Workload(name, tuple(int(x) for x in seq_lens), tuple(int(x) for x in q_per_seq),
-                    int(topk), int(num_splits), int(seed))
+                    int(topk), int(num_splits), int(seed), key_format)
 
 
 @dataclasses.dataclass
@@ -119,7 +124,7 @@ class Batch:
     cu_q: torch.Tensor          # int32 [B+1]
     seq_lens: torch.Tensor      # int32 [B]
     block_table: torch.Tensor   # int32 [B, bt_stride], -1 past the last page
-    key_pool: torch.Tensor      # uint8 [P, 8448]
+    key_pool: torch.Tensor      # uint8 [P, 8448] (E4M3 keys) or [P, 4352] (MXFP4 keys)
     latent_pool: torch.Tensor   # uint8 [P, 36864]
     latent_scale: float         # per-tensor fp32 scale of the latents
     q_idx: torch.Tensor         # bf16 [n_q, 32, 128]
@@ -127,7 +132,8 @@ class Batch:
     q_mla: torch.Tensor         # bf16 [n_q, 96, 576]
     softmax_scale: float
     # logical (unpaged) copies, kept only when asked for (small workloads)
-    keys_logical: Optional[list] = None      # per request uint8 [L, 128]
+    keys_logical: Optional[list] = None      # per request uint8 [L, 128] codes (E4M3) or
+                                             # the unquantised fp32 [L, 128] keys (MXFP4)
     scales_logical: Optional[list] = None    # per request fp32 [L]
     latents_logical: Optional[list] = None   # per request uint8 [L, 576]
 
@@ -146,6 +152,31 @@ def _gen(device, seed, stream, idx):
 def _to_e4m3(x: torch.Tensor) -> torch.Tensor:
     """fp32 -> E4M3 codes (uint8); |x| is at most 448 here, so no saturation happens."""
     return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+_E2M1_TIES_ODD = (1, 3, 5)  # boundaries between codes i and i+1 where i is odd: ties go up
+
+
+def _to_mxfp4(x: torch.Tensor):
+    """fp32 [n, 128] -> (E2M1 codes [n, 128] as int, E8M0 scale bytes [n, 4]) by the OCP MX
+    recipe: per block of 32, shared exponent floor(log2 absmax) - 2 (E2M1's largest
+    exponent), elements rounded to nearest even on the E2M1 grid and saturated at 6; an
+    all-zero block gets scale 2^0 and zero codes."""
+    blk = x.view(x.shape[0], 4, 32)
+    amax = blk.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                        # amax = m * 2^ex, m in [0.5, 1)
+    e = torch.where(amax > 0, ex.to(torch.int32) - 3, torch.zeros_like(ex, dtype=torch.int32))
+    e = e.clamp(-127, 127)
+    q = blk / torch.ldexp(torch.ones_like(amax), e.to(amax.dtype))[:, :, None]
+    a = q.abs()
+    bounds = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+    code = torch.zeros_like(a, dtype=torch.int32)
+    for i, bnd in enumerate(bounds):
+        code += (a > bnd).to(torch.int32)
+        if i in _E2M1_TIES_ODD:
+            code += (a == bnd).to(torch.int32)
+    code = code | (torch.signbit(q).to(torch.int32) << 3)
+    return code.view(x.shape[0], 128), (e + 127).to(torch.uint8)
 
 
 def _chunks(n, step):
@@ -169,15 +200,44 @@ def make_batch(wl: Workload, device: str = "cpu", keep_logical: bool = False,
         bt[b, :n] = perm[off:off + n].to(torch.int32)
         off += n
 
-    key_pool = torch.full((total, IDX_PAGE_BYTES), E4M3_NAN, dtype=torch.uint8, device=dev)
-    nan_scales = torch.full((total, PAGE), float("nan"), dtype=torch.float32, device=dev)
-    key_pool[:, PAGE * IDX_DIM:] = nan_scales.view(torch.uint8)
+    mx = wl.key_format == "mxfp4"
+    if mx:
+        # poison: maximal codes and E8M0 NaN scales
+        key_pool = torch.full((total, MX_PAGE_BYTES), 0x77, dtype=torch.uint8, device=dev)
+        key_pool[:, PAGE * IDX_DIM // 2:] = 0xFF
+    else:
+        key_pool = torch.full((total, IDX_PAGE_BYTES), E4M3_NAN, dtype=torch.uint8, device=dev)
+        nan_scales = torch.full((total, PAGE), float("nan"), dtype=torch.float32, device=dev)
+        key_pool[:, PAGE * IDX_DIM:] = nan_scales.view(torch.uint8)
     latent_pool = torch.full((total, LAT_PAGE_BYTES), E4M3_NAN, dtype=torch.uint8, device=dev)
 
     keys_log, scales_log, lat_log = ([] if keep_logical else None for _ in range(3))
 
+    # ---- index keys: MXFP4 (block scales) ------------------------------------------------
+    for b, L in enumerate(wl.seq_lens if mx else ()):
+        g = _gen(dev, seed, _S_KEYS, b)
+        phys = bt[b, :n_pages[b]].to(dev).long()
+        nb = torch.full((n_pages[b] * PAGE, 64), 0x77, dtype=torch.uint8, device=dev)
+        sb = torch.full((n_pages[b] * PAGE, 4), 0xFF, dtype=torch.uint8, device=dev)
+        raw = [] if keep_logical else None
+        for s, e in _chunks(L, chunk_tokens):
+            k = torch.randn((e - s, IDX_DIM), generator=g, device=dev, dtype=torch.float32)
+            codes, scl = _to_mxfp4(k)
+            pair = codes.view(e - s, 64, 2)
+            nb[s:e] = (pair[:, :, 0] | (pair[:, :, 1] << 4)).to(torch.uint8)
+            sb[s:e] = scl
+            if keep_logical:
+                raw.append(k.cpu())
+        # 16-byte blocks (one per 32 dims): [page, token, 4, 16] -> [page, 4, token, 16]
+        blk = nb.view(n_pages[b], PAGE, 4, 16).permute(0, 2, 1, 3)
+        key_pool[phys, :PAGE * IDX_DIM // 2] = blk.reshape(n_pages[b], PAGE * IDX_DIM // 2)
+        key_pool[phys, PAGE * IDX_DIM // 2:] = sb.view(n_pages[b], PAGE * 4)
+        if keep_logical:
+            keys_log.append(torch.cat(raw))     # the unquantised fp32 keys
+            scales_log.append(None)
+
     # ---- index keys: per-token scale absmax/448 --------------------------------------
-    for b, L in enumerate(wl.seq_lens):
+    for b, L in enumerate(() if mx else wl.seq_lens):
         g = _gen(dev, seed, _S_KEYS, b)
         phys = bt[b, :n_pages[b]].to(dev).long()
         codes_all = torch.empty((n_pages[b] * PAGE, IDX_DIM), dtype=torch.uint8, device=dev)

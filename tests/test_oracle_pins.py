@@ -388,3 +388,70 @@ def test_cache_append_codes_scales_and_layout():
     assert s7[o7] == 1.0 and (c7[o7] == 0).all()
     c0, s0 = O.read_index_keys(key_pool, np.array([int(slots[0] // 64)]), 64)
     assert np.abs(O.e4m3_decode(c0[int(slots[0] % 64)])).max() == 448.0
+
+
+# ------------------------------------------------------------------------ MXFP4 index keys
+def test_e8m0_matches_torch():
+    b = torch.arange(256, dtype=torch.uint8)
+    ref = b.view(torch.float8_e8m0fnu).double().numpy()
+    got = O.e8m0_value(np.arange(256))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_e2m1_decode_is_the_ocp_table():
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]     # OCP MX v1.0, E2M1 magnitudes
+    got = O.e2m1_decode(np.arange(16))
+    assert np.array_equal(got[:8], table)
+    assert np.array_equal(got[8:], [-v for v in table])
+    assert np.signbit(got[8])                               # -0
+
+
+def _mx_reference(raw):
+    """Brute-force OCP MX quantisation of fp32 keys [n, 128] -> dequantised values: per
+    block of 32 the scale 2^(floor(log2 absmax) - 2) (exactly, via frexp), each element the
+    nearest E2M1 value of x / scale (ties to the even code), saturated at 6."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    out = np.empty(raw.shape, dtype=np.float64)
+    for t in range(raw.shape[0]):
+        for blk in range(4):
+            x = raw[t, 32 * blk:32 * blk + 32].astype(np.float64)
+            amax = np.abs(x).max()
+            e = (math.frexp(amax)[1] - 1 - 2) if amax > 0 else 0
+            sc = 2.0 ** e
+            for j, v in enumerate(x):
+                a = min(abs(v) / sc, 6.0)
+                best = min(range(8), key=lambda c: (abs(grid[c] - a), c % 2))
+                out[t, 32 * blk + j] = math.copysign(grid[best] * sc, v)
+    return out
+
+
+def test_mxfp4_cache_reader_matches_reference_quantisation():
+    wl = synth.custom([130, 64], [1, 1], topk=16, seed=17, key_format="mxfp4")
+    b = synth.make_batch(wl, "cpu", keep_logical=True)
+    pool, bt = b.key_pool.numpy(), b.block_table.numpy()
+    for r, L in enumerate(wl.seq_lens):
+        got = O.read_index_keys_mxfp4(pool, bt[r], L)
+        raw = b.keys_logical[r].numpy()
+        ref = _mx_reference(raw)
+        assert np.array_equal(got, ref), r
+        # within the MX error: half a grid step, or the saturation at 6 * scale
+        assert np.isfinite(got).all()
+
+
+def test_index_scores_values_brute_force():
+    rng = np.random.default_rng(5)
+    q = torch.from_numpy(rng.normal(size=(32, 128)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    w = (rng.normal(size=32) / math.sqrt(32)).astype(np.float32)
+    kv = O.e2m1_decode(rng.integers(0, 16, size=(12, 128))) * 2.0 ** rng.integers(-3, 3, size=(12, 1))
+    got = O.index_scores_values(q, w, kv).astype(np.float64)
+    qd = O.dequantized_query(q).tolist()
+    for t in range(12):
+        acc = 0.0
+        for h in range(32):
+            dot = 0.0
+            for d in range(128):
+                dot += qd[h][d] * kv[t][d]
+            acc += float(w[h]) * (dot if dot > 0 else 0.0)
+        assert abs(got[t] - acc) <= 1e-6 * max(1.0, abs(acc)), t
