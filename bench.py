@@ -25,6 +25,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, vendor figure
 PAGE = 64
 IDX_BYTES_PER_TOKEN = 132        # 128 B E4M3 key + 4 B fp32 scale
+MX_IDX_BYTES_PER_TOKEN = 68      # MXFP4 key: 64 B of E2M1 codes + 4 E8M0 block scales
+
+
+def idx_bytes_per_token(key_format):
+    return MX_IDX_BYTES_PER_TOKEN if key_format == "mxfp4" else IDX_BYTES_PER_TOKEN
 LAT_BYTES_PER_TOKEN = 576        # E4M3 latent
 QIDX_BYTES_PER_ROW = 32 * 128 * 2 + 32 * 4     # bf16 indexer query + fp32 head weights
 QMLA_BYTES_PER_ROW = 96 * 576 * 2              # bf16 MLA query
@@ -32,12 +37,13 @@ OUT_BYTES_PER_ROW = 96 * 512 * 2 + 96 * 4      # bf16 output + fp32 LSE
 BT_BYTES_PER_PAGE = 4
 
 
-def algorithmic_bytes(seq_lens, q_per_seq, topk):
+def algorithmic_bytes(seq_lens, q_per_seq, topk, key_format="e4m3"):
     """Bytes the method itself must move for one step (the byte model of the K3.1 page's
     "Sparse attention cuts long-context decode bandwidth" section: the whole context's
-    132-byte index keys once per request, 576 bytes for each selected token of each row,
-    plus queries, outputs and the block table).  Returns a dict of parts and the total."""
-    keys = sum(L * IDX_BYTES_PER_TOKEN for L in seq_lens)
+    132-byte index keys (68 with MXFP4 keys) once per request, 576 bytes for each selected
+    token of each row, plus queries, outputs and the block table).  Returns a dict of parts
+    and the total."""
+    keys = sum(L * idx_bytes_per_token(key_format) for L in seq_lens)
     lat = 0
     n_rows = 0
     for L, nq in zip(seq_lens, q_per_seq):
@@ -53,10 +59,10 @@ def algorithmic_bytes(seq_lens, q_per_seq, topk):
     return parts
 
 
-def index_score_bytes(seq_lens):
-    """Algorithmic bytes of one dsa_index_score launch: 132 B per context token of every
-    request (keys are read once and shared by that request's rows)."""
-    return sum(L * IDX_BYTES_PER_TOKEN for L in seq_lens)
+def index_score_bytes(seq_lens, key_format="e4m3"):
+    """Algorithmic bytes of one dsa_index_score launch: 132 B (MXFP4: 68 B) per context
+    token of every request (keys are read once and shared by that request's rows)."""
+    return sum(L * idx_bytes_per_token(key_format) for L in seq_lens)
 
 
 def dense_mla_bytes(seq_lens, q_per_seq):
@@ -98,19 +104,24 @@ def cache_append_timing(torch, dsa, batch, wl, steps):
     g = torch.Generator(device="cuda").manual_seed(99)
     key = torch.randn((n, 128), generator=g, device="cuda").to(torch.bfloat16)
     lat = torch.randn((n, 576), generator=g, device="cuda").to(torch.bfloat16)
+    mx = wl.key_format == "mxfp4"   # the append writes E4M3 index keys: latents only here
+    kk, kp = (None, None) if mx else (key, batch.key_pool)
     for _ in range(3):
-        dsa.dsa_cache_append(slots_d, key, lat, batch.latent_scale, batch.key_pool, batch.latent_pool)
+        dsa.dsa_cache_append(slots_d, kk, lat, batch.latent_scale, kp, batch.latent_pool)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        dsa.dsa_cache_append(slots_d, key, lat, batch.latent_scale, batch.key_pool, batch.latent_pool)
+        dsa.dsa_cache_append(slots_d, kk, lat, batch.latent_scale, kp, batch.latent_pool)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     return {"tokens": n, "us_per_call": round(us, 2),
-            "note": "one new token per query row: its index key (132 B) and latent (576 B) "
-                    "quantised into the paged caches; calls back to back, caches warm"}
+            "note": ("one new token per query row: " +
+                     ("its latent (576 B; MXFP4 keys are not appended by this library)" if mx
+                      else "its index key (132 B) and latent (576 B)") +
+                     " quantised into the paged caches; calls back to back from Python, caches "
+                     "warm")}
 
 
 def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
@@ -139,8 +150,12 @@ def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
                          batch.latent_pool[pages].cpu().numpy())
         key_pages, bt_local, qi, w, qm, lat_pages = host[row]
         t0 = time.perf_counter()
-        kc, ks = O.read_index_keys(key_pages, bt_local, L)
-        scores = O.index_scores(qi, w, kc[: pos + 1], ks[: pos + 1])
+        if wl.key_format == "mxfp4":
+            kv = O.read_index_keys_mxfp4(key_pages, bt_local, L)
+            scores = O.index_scores_values(qi, w, kv[: pos + 1])
+        else:
+            kc, ks = O.read_index_keys(key_pages, bt_local, L)
+            scores = O.index_scores(qi, w, kc[: pos + 1], ks[: pos + 1])
         sel = O.topk_indices(scores, wl.topk)
         lat = O.read_latents(lat_pages, O.physical_slot(bt_local, sel))
         parts = [O.mla_attend(qm, lat[a:e], batch.latent_scale, batch.softmax_scale)
@@ -150,7 +165,7 @@ def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
         # the row's share of the algorithmic bytes: its request's keys divided over the
         # request's rows, its selected latents, its query / output
         nq = wl.q_per_seq[b]
-        byts += (L * IDX_BYTES_PER_TOKEN) / nq + min(wl.topk, pos + 1) * LAT_BYTES_PER_TOKEN \
+        byts += (L * idx_bytes_per_token(wl.key_format)) / nq + min(wl.topk, pos + 1) * LAT_BYTES_PER_TOKEN \
             + QIDX_BYTES_PER_ROW + QMLA_BYTES_PER_ROW + OUT_BYTES_PER_ROW
         done += 1
         if t_total > budget_s:
@@ -239,7 +254,8 @@ def main():
     step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
                           query_on_side_stream=args.query_side_stream,
                           select_in_attention=not (args.separate_topk or args.unfused),
-                          store_scores=args.store_scores or args.unfused,
+                          store_scores=True if (args.store_scores or args.unfused) else None,
+                          key_format=wl.key_format,
                           write_selection=False)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
@@ -320,11 +336,11 @@ def main():
     mean_us = sum(step_us) / len(step_us)
     stage_mean = [sum(s) / len(s) for s in stage]
 
-    ab = algorithmic_bytes(wl.seq_lens, wl.q_per_seq, wl.topk)
+    ab = algorithmic_bytes(wl.seq_lens, wl.q_per_seq, wl.topk, wl.key_format)
     value = ab["total"] / (mean_us * 1e-6) / 1e9
-    idx_bytes = index_score_bytes(wl.seq_lens)
+    idx_bytes = index_score_bytes(wl.seq_lens, wl.key_format)
     idx_gbps = idx_bytes / (stage_mean[0] * 1e-6) / 1e9
-    traffic = _traffic_from_profile()
+    traffic = _traffic_from_profile() if wl.name == "long" else None  # counted on `long`
     ceiling = stream_read_ceiling(torch)
     if args.copy_calibration:
         src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
@@ -352,12 +368,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 MFMA, fp32 accumulate, bf16 in/out",
-        "data": "synthetic (seeded N(0,1) queries/keys/latents, E4M3-quantised caches, "
-                "shuffled 64-token pages)",
+        "dtype": ("fp8e4m3 x mxfp4 MFMA (indexer), fp8e4m3 MFMA (attention), fp32 accumulate, "
+                  "bf16 in/out" if wl.key_format == "mxfp4" else
+                  "fp8e4m3 MFMA, fp32 accumulate, bf16 in/out"),
+        "data": ("synthetic (seeded N(0,1) queries/keys/latents, MXFP4 index keys, E4M3 "
+                 "latents, shuffled 64-token pages)" if wl.key_format == "mxfp4" else
+                 "synthetic (seeded N(0,1) queries/keys/latents, E4M3-quantised caches, "
+                 "shuffled 64-token pages)"),
         "config": {"workload": wl.name, "batch": wl.num_seqs, "query_rows": wl.n_q,
                    "context": wl.max_seq_len if len(set(wl.seq_lens)) == 1 else "ragged",
                    "topk": wl.topk, "num_splits": S, "page_size": PAGE,
+                   "index_key_format": wl.key_format,
                    "indexer_emits_topk_candidates": not args.unfused,
                    "scores_stored": step.store_scores,
                    "topk_final_in_attention": step.select_in_attention,

@@ -7,6 +7,7 @@
  * exactly over those only, and split partial outputs are merged by log-sum-exp.
  *
  *   dsa_index_score       stage 1  indexer scores           ("What changed in Kimi K3.1 Pro")
+ *   dsa_index_score_mxfp4 stage 1 on MXFP4 index keys        ("Native MXFP4 indexer")
  *   dsa_topk              stage 2  exact top-k select       ("Exact top-k merge with ~10x less traffic")
  *                         Stage 1 can also emit each 256-token group's top-k candidates while
  *                         its scores are on chip; stage 2 then only runs its final pass (the
@@ -76,6 +77,7 @@ typedef enum {
 #define DSA_IDX_HEADS 32
 #define DSA_IDX_DIM 128
 #define DSA_IDX_PAGE_BYTES 8448
+#define DSA_IDX_MXFP4_PAGE_BYTES 4352
 #define DSA_MLA_HEADS 96
 #define DSA_LATENT_DIM 576
 #define DSA_V_DIM 512
@@ -119,6 +121,29 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
                            int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
                            float* scores, int64_t score_stride, int32_t cand_k,
                            void* cand_workspace, size_t cand_workspace_bytes, void* stream);
+
+/*
+ * Stage 1 on MXFP4 index keys (68 bytes per token: the opt-in MXFP4 index key of "Packed KV
+ * cache for three kinds of state", scored with FP4 matrix instructions and FP32
+ * accumulation as in "Native MXFP4 indexer").
+ *   score[i][t] = sum_h w'[i][h] * ReLU(sum_d q8[i][h][d] * k[t][d]),  k = E2M1 * 2^(E8M0-127)
+ * (the block scales are inside the product; there is no per-token scale).  The query is
+ * E4M3 as for dsa_index_score.
+ *   MXFP4 index-key page (at key_pages + page * key_page_stride, 16-byte aligned,
+ *   key_page_stride >= 4352): block b (dims 32b .. 32b+31) of token o is 16 bytes at
+ *   b * 1024 + o * 16, byte j holding dims 32b + 2j (low nibble) and 32b + 2j + 1 (high
+ *   nibble) as E2M1 (OCP MX); the E8M0 scale of block b of token o is the byte at
+ *   4096 + 4 * o + b.
+ *   Every other argument as for dsa_index_score, except that scores must be given (the
+ *   final top-k pass recomputes missing scores from E4M3 keys only).
+ */
+dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                                 int32_t max_q_per_seq, const int32_t* cu_q,
+                                 const int32_t* seq_lens, const void* q_bf16, const float* head_w,
+                                 const void* key_pages, int64_t key_page_stride,
+                                 const int32_t* block_table, int32_t bt_stride, float* scores,
+                                 int64_t score_stride, int32_t cand_k, void* cand_workspace,
+                                 size_t cand_workspace_bytes, void* stream);
 
 /*
  * Stage 2 — exact top-k over each row's visible scores (tokens 0..position).

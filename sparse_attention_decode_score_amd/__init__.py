@@ -48,6 +48,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.dsa_index_score.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32,
                                       _P, _I64, _I32, _P, _SZ, _P]
+        L.dsa_index_score_mxfp4.argtypes = L.dsa_index_score.argtypes
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
@@ -64,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
-        for f in ("dsa_index_score", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
+        for f in ("dsa_index_score", "dsa_index_score_mxfp4", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
                   "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -116,11 +117,16 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
                     head_w: torch.Tensor, key_pages: torch.Tensor, block_table: torch.Tensor,
                     scores: Optional[torch.Tensor], *, max_seq_len: int, max_q_per_seq: int,
                     key_page_stride: Optional[int] = None, cand_k: int = 0,
-                    cand_workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                    cand_workspace: Optional[torch.Tensor] = None, key_format: str = "e4m3",
+                    stream=None) -> None:
     """Indexer scores into scores [n_q, score_stride] (fp32); with cand_workspace, also the
     per-chunk top-k candidates for a top-k of cand_k (consumed by dsa_topk with
     from_candidates=True).  scores=None with cand_workspace: candidates only (no scores
-    stored; pass rescore=(q_idx, head_w, key_pages) to the final top-k pass)."""
+    stored; pass rescore=(q_idx, head_w, key_pages) to the final top-k pass).
+    key_format "mxfp4": the key cache holds MXFP4 keys (dsa_index_score_mxfp4; scores
+    must then be given)."""
+    if key_format not in ("e4m3", "mxfp4"):
+        raise ValueError(f"key_format must be 'e4m3' or 'mxfp4' (got {key_format!r})")
     num_seqs = seq_lens.shape[0]
     n_q = q_idx.shape[0]
     _expect(cu_q, "cu_q", torch.int32, (num_seqs + 1,))
@@ -135,7 +141,8 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
     stride = key_page_stride if key_page_stride is not None else key_pages.stride(0) * key_pages.element_size()
     if cand_workspace is not None:
         _expect(cand_workspace, "cand_workspace", torch.uint8)
-    _check(lib().dsa_index_score(num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q),
+    fn = lib().dsa_index_score_mxfp4 if key_format == "mxfp4" else lib().dsa_index_score
+    _check(fn(num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q),
                                  _ptr(seq_lens), _ptr(q_idx), _ptr(head_w), _ptr(key_pages),
                                  int(stride), _ptr(block_table), block_table.shape[1],
                                  _ptr(scores), scores.shape[1] if scores is not None else 0,
@@ -330,7 +337,12 @@ class DecodeStep:
     def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
                  fused: bool = True, query_on_side_stream: bool = False,
                  select_in_attention: Optional[bool] = None, write_selection: bool = True,
-                 store_scores: Optional[bool] = None):
+                 store_scores: Optional[bool] = None, key_format: str = "e4m3"):
+        self.key_format = key_format
+        if key_format == "mxfp4":
+            if store_scores is False:
+                raise ValueError("MXFP4 keys need stored scores")
+            store_scores = True
         if select_in_attention is None:
             select_in_attention = fused
         if store_scores is None:
@@ -371,7 +383,7 @@ class DecodeStep:
                         self.scores if self.store_scores else None,
                         max_seq_len=self.max_seq_len, max_q_per_seq=max_q_per_seq,
                         cand_k=self.k, cand_workspace=self.workspace if self.fused else None,
-                        stream=stream)
+                        key_format=self.key_format, stream=stream)
 
     def select(self, cu_q, seq_lens, block_table, stream=None):
         """Stage 2."""

@@ -128,26 +128,40 @@ dsa_status dsa_quantize_q(int32_t rows, int32_t heads, int32_t dim, const void* 
                   "dsa_quantize_q");
 }
 
-dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
-                           int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
-                           const void* q_bf16, const float* head_w, const void* key_pages,
-                           int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
-                           float* scores, int64_t score_stride, int32_t cand_k,
-                           void* cand_workspace, size_t cand_workspace_bytes, void* stream) {
+namespace {
+
+dsa_status index_score_checked(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                               int32_t max_q_per_seq, const int32_t* cu_q,
+                               const int32_t* seq_lens, const void* q_bf16, const float* head_w,
+                               const void* key_pages, int64_t key_page_stride,
+                               const int32_t* block_table, int32_t bt_stride, float* scores,
+                               int64_t score_stride, int32_t cand_k, void* cand_workspace,
+                               size_t cand_workspace_bytes, bool mxfp4, void* stream) {
   dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(max_q_per_seq >= 1 && max_q_per_seq <= n_q,
               "max_q_per_seq must be in 1..n_q (got %d)", max_q_per_seq);
   DSA_REQUIRE(q_bf16 && head_w && key_pages && block_table,
               "q_bf16, head_w, key_pages and block_table must be non-null");
-  DSA_REQUIRE(scores || cand_workspace,
-              "scores may be NULL only when cand_workspace is given (candidates only)");
+  if (mxfp4) {
+    DSA_REQUIRE(scores, "scores must be non-null with MXFP4 keys (the final top-k pass "
+                        "recomputes scores from E4M3 keys only)");
+  } else {
+    DSA_REQUIRE(scores || cand_workspace,
+                "scores may be NULL only when cand_workspace is given (candidates only)");
+  }
   DSA_REQUIRE(aligned(q_bf16, 16), "q_bf16 must be 16-byte aligned");
   DSA_REQUIRE(aligned(head_w, 16), "head_w must be 16-byte aligned");
   DSA_REQUIRE(aligned(key_pages, 16), "key_pages must be 16-byte aligned");
-  DSA_REQUIRE(key_page_stride >= DSA_IDX_PAGE_BYTES && key_page_stride % 16 == 0,
-              "key_page_stride must be >= 8448 and a multiple of 16 (got %lld)",
-              (long long)key_page_stride);
+  if (mxfp4) {
+    DSA_REQUIRE(key_page_stride >= DSA_IDX_MXFP4_PAGE_BYTES && key_page_stride % 16 == 0,
+                "key_page_stride must be >= 4352 and a multiple of 16 (got %lld)",
+                (long long)key_page_stride);
+  } else {
+    DSA_REQUIRE(key_page_stride >= DSA_IDX_PAGE_BYTES && key_page_stride % 16 == 0,
+                "key_page_stride must be >= 8448 and a multiple of 16 (got %lld)",
+                (long long)key_page_stride);
+  }
   DSA_REQUIRE(bt_stride >= (max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE,
               "bt_stride (%d) must cover max_seq_len (%d) in pages of 64", bt_stride, max_seq_len);
   if (scores)
@@ -166,8 +180,35 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
                                           static_cast<const uint16_t*>(q_bf16), head_w,
                                           static_cast<const uint8_t*>(key_pages), key_page_stride,
                                           block_table, bt_stride, scores, score_stride, cand_k,
-                                          cand_workspace, static_cast<hipStream_t>(stream)),
-                  "dsa_index_score");
+                                          cand_workspace, mxfp4, static_cast<hipStream_t>(stream)),
+                  mxfp4 ? "dsa_index_score_mxfp4" : "dsa_index_score");
+}
+
+}  // namespace
+
+dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                           int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
+                           const void* q_bf16, const float* head_w, const void* key_pages,
+                           int64_t key_page_stride, const int32_t* block_table, int32_t bt_stride,
+                           float* scores, int64_t score_stride, int32_t cand_k,
+                           void* cand_workspace, size_t cand_workspace_bytes, void* stream) {
+  return index_score_checked(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens, q_bf16,
+                             head_w, key_pages, key_page_stride, block_table, bt_stride, scores,
+                             score_stride, cand_k, cand_workspace, cand_workspace_bytes, false,
+                             stream);
+}
+
+dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                                 int32_t max_q_per_seq, const int32_t* cu_q,
+                                 const int32_t* seq_lens, const void* q_bf16, const float* head_w,
+                                 const void* key_pages, int64_t key_page_stride,
+                                 const int32_t* block_table, int32_t bt_stride, float* scores,
+                                 int64_t score_stride, int32_t cand_k, void* cand_workspace,
+                                 size_t cand_workspace_bytes, void* stream) {
+  return index_score_checked(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens, q_bf16,
+                             head_w, key_pages, key_page_stride, block_table, bt_stride, scores,
+                             score_stride, cand_k, cand_workspace, cand_workspace_bytes, true,
+                             stream);
 }
 
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k) {

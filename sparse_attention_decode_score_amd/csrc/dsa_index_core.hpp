@@ -112,4 +112,79 @@ __device__ __forceinline__ float score_key_page(const uint8_t* q8, const float* 
   return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * cur.s;
 }
 
+// ---------------------------------------------------------------------------------------
+// MXFP4 index keys (68 B per token: the "Native MXFP4 indexer" of the K3.1 page, with its
+// FP4 matrix instructions and FP32 accumulation).  Page of 4,352 B: block b (dims 32b ..
+// 32b+31) of token o is 16 bytes of E2M1 codes at b * 1024 + o * 16 (byte j: dims 32b + 2j,
+// low nibble, and 32b + 2j + 1); the E8M0 scale of block b is the byte at 4096 + 4 o + b.
+constexpr int kMxPageKeyBytes = kPage * kIdxDim / 2;  // 4096
+constexpr int kMxPageBytes = kMxPageKeyBytes + kPage * 4;  // 4352
+
+// The scaled FP8 x FP4 MFMA of gfx950 takes, in lane (n, g) of a 32x32x64 product, 32 E2M1
+// values of column n at k positions 16g .. 16g+15 (nibbles 0..15, low nibble first) and
+// 32+16g .. 32+16g+15 (nibbles 16..31), scaled by that lane's E8M0 byte.  So chunk c of a key
+// (dims 64c .. 64c+63) is laid out with lane g holding MX block 2c+g as it is stored, and the
+// FP8 query lane g holds dims 64c+16g .. +15 and 64c+32+16g .. +15 in k order, which pairs
+// every query dim with the same key dim.
+struct KeyPageMx {
+  v4i k[2][2];     // [half][chunk]: 16 bytes = MX block 2 * chunk + g of token l%32 of the half
+  uint32_t sw[2];  // [half]: the four E8M0 block scales of that token
+};
+
+__device__ __forceinline__ void load_key_page(KeyPageMx& kp, const uint8_t* base, int lane) {
+  const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const uint8_t* tok = base + (32 * hf + n) * 16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      kp.k[hf][c] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tok + (2 * c + g) * 1024));
+    kp.sw[hf] = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(base + kMxPageKeyBytes + 4 * (32 * hf + n)));
+  }
+}
+
+__device__ __forceinline__ v16f mfma_32x32x64_fp8_mxfp4(const v8i& a, const v4i& b, int scale_b,
+                                                        const v16f& c) {
+  const v8i bb = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  // A: FP8 E4M3 with unit scale (E8M0 127); B: FP4 E2M1 (format 4) with its block scale
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, c, 0, 4, 0, 127, 0, scale_b);
+}
+
+// Score of token `lane` of an MXFP4 key page (same head reduction as the FP8 page; the block
+// scales are inside the product, so there is no per-token scale).
+__device__ __forceinline__ float score_key_page(const uint8_t* q8, const float* w,
+                                                const KeyPageMx& cur, int lane) {
+  const int n = lane & 31, g = lane >> 5;
+  const uint8_t* qa = q8 + n * kQRowStride + 16 * g;
+  const v4i a0 = *reinterpret_cast<const v4i*>(qa);
+  const v4i a1 = *reinterpret_cast<const v4i*>(qa + 32);
+  const v4i a2 = *reinterpret_cast<const v4i*>(qa + 64);
+  const v4i a3 = *reinterpret_cast<const v4i*>(qa + 96);
+  const v8i A0 = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  const v8i A1 = v8i{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+  const v16f z = {};
+  v16f d[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int s0 = (int)((cur.sw[hf] >> (8 * g)) & 0xFFu);
+    const int s1 = (int)((cur.sw[hf] >> (8 * (2 + g))) & 0xFFu);
+    d[hf] = mfma_32x32x64_fp8_mxfp4(A0, cur.k[hf][0], s0, z);
+    d[hf] = mfma_32x32x64_fp8_mxfp4(A1, cur.k[hf][1], s1, d[hf]);
+  }
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const v4f wv = *reinterpret_cast<const v4f*>(w + 8 * a + 4 * g);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc0 = fmaf(wv[c], relu(d[0][4 * a + c]), acc0);
+      acc1 = fmaf(wv[c], relu(d[1][4 * a + c]), acc1);
+    }
+  }
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc0), __float_as_uint(acc1),
+                                                   false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 }  // namespace dsa

@@ -45,12 +45,14 @@ hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, ui
                              float* scales, hipStream_t st);
 
 // topk_ws == nullptr: scores only.  Otherwise the kernel also writes every 256-token group's
-// top-k candidates for a top-k of k into topk_ws (see topk_buffers).
+// top-k candidates for a top-k of k into topk_ws (see topk_buffers).  mxfp4: the key cache
+// holds MXFP4 keys (4,352-byte pages) instead of E4M3 keys with an fp32 scale.
 hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_per_seq,
                               const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
                               const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
                               const int32_t* block_table, int bt_stride, float* scores,
-                              int64_t score_stride, int k, void* topk_ws, hipStream_t st);
+                              int64_t score_stride, int k, void* topk_ws, bool mxfp4,
+                              hipStream_t st);
 
 hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu_q,
                        const int32_t* seq_lens, const float* scores, int64_t score_stride, int k,

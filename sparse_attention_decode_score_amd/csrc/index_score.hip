@@ -21,6 +21,7 @@
 // wave access.  The head reduction is 16 in-register FMAs, then one permlane32 swap that
 // also places token l of the page in lane l for a coalesced 256-byte score store.
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
@@ -63,7 +64,7 @@ struct CandOut {
 // loads and stores in one counter that may complete out of order, so a store in flight,
 // or loads under data-dependent branches, would force a full drain of the ring at every
 // wait instead of a wait for the oldest page only.
-template <int R, bool CAND>
+template <int R, bool CAND, bool MX>
 __global__ __launch_bounds__(256) void index_score_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ head_w,
@@ -131,7 +132,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   };
   // (unconditional, also for a wave without groups in a request's last segment: a branch
   // here would leave the block-table load in doubt at every later wait)
-  KeyPage kp[NF];
+  using Page = std::conditional_t<MX, KeyPageMx, KeyPage>;  // MXFP4 or E4M3 + scale keys
+  Page kp[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) load_key_page(kp[j], page_ptr(j), lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   // 4. the wave's groups: score each ring slot, refill it at once, and after four pages
   //    select the group's candidates while the next group's keys stream in
   uint32_t keys[R][4];
-  auto score_page = [&](int s, int jj, const KeyPage& cur) {
+  auto score_page = [&](int s, int jj, const Page& cur) {
     const int p = page_of(s);
     const bool valid = p < p_end;
     const int t = p * kPage + lane;
@@ -305,7 +307,8 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
                               const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
                               const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
                               const int32_t* block_table, int bt_stride, float* scores,
-                              int64_t score_stride, int k, void* topk_ws, hipStream_t st) {
+                              int64_t score_stride, int k, void* topk_ws, bool mxfp4,
+                              hipStream_t st) {
   const int max_pages = (max_seq_len + kPage - 1) / kPage;
   int R = 8;
   if (max_q_per_seq <= 1) R = 1;
@@ -329,10 +332,17 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
     const TopkBuffers t = topk_buffers(topk_ws, n_q, max_seq_len, k);
     cand = CandOut{t.cand_key, t.cand_idx, t.info, (int64_t)t.plan.row_cap, t.plan.num_groups, k};
   }
-#define DSA_LAUNCH_IDX(RR, CC)                                                                   \
-  hipLaunchKernelGGL((index_score_kernel<RR, CC>), grid, block, 0, st, cu_q, seq_lens, q, head_w, \
-                     key_pages, key_page_stride, block_table, bt_stride, scores, score_stride, G,  \
-                     cand)
+#define DSA_LAUNCH_IDX(RR, CC)                                                                    \
+  do {                                                                                           \
+    if (mxfp4)                                                                                   \
+      hipLaunchKernelGGL((index_score_kernel<RR, CC, true>), grid, block, 0, st, cu_q, seq_lens, \
+                         q, head_w, key_pages, key_page_stride, block_table, bt_stride, scores,  \
+                         score_stride, G, cand);                                                  \
+    else                                                                                         \
+      hipLaunchKernelGGL((index_score_kernel<RR, CC, false>), grid, block, 0, st, cu_q,          \
+                         seq_lens, q, head_w, key_pages, key_page_stride, block_table, bt_stride, \
+                         scores, score_stride, G, cand);                                          \
+  } while (0)
 #define DSA_LAUNCH_R(CC)                 \
   switch (R) {                           \
     case 1: DSA_LAUNCH_IDX(1, CC); break; \

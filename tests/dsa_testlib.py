@@ -29,22 +29,29 @@ def host(batch):
 
 
 def request_keys(batch, b, key_pool=None, bt=None):
-    """Oracle-read index keys of request b (codes, scales)."""
+    """Oracle-read index keys of request b: (codes, scales) for E4M3 keys, or the key values
+    [L, 128] for MXFP4 keys."""
+    mx = batch.wl.key_format == "mxfp4"
+    read = O.read_index_keys_mxfp4 if mx else O.read_index_keys
     if key_pool is None:
         # pull only this request's pages from the device
         pages = batch.block_table[b, : (batch.wl.seq_lens[b] + 63) // 64].long()
         sub = batch.key_pool[pages].cpu().numpy()
-        return O.read_index_keys(sub, np.arange(len(pages)), batch.wl.seq_lens[b])
-    return O.read_index_keys(key_pool, bt[b], batch.wl.seq_lens[b])
+        return read(sub, np.arange(len(pages)), batch.wl.seq_lens[b])
+    return read(key_pool, bt[b], batch.wl.seq_lens[b])
 
 
 def oracle_scores(batch, row, keys=None):
     """Oracle fp32 scores of query row `row` over its visible tokens, plus the magnitude
     bound A used by the tolerance."""
     b, pos = batch.wl.row_positions()[row]
-    kc, ks = keys if keys is not None else request_keys(batch, b)
+    keys = keys if keys is not None else request_keys(batch, b)
     q = batch.q_idx[row].cpu().double().numpy()
     w = batch.head_w[row].cpu().numpy()
+    if batch.wl.key_format == "mxfp4":
+        kv = keys[: pos + 1]
+        return O.index_scores_values(q, w, kv), O.index_scores_values(q, np.abs(w), kv)
+    kc, ks = keys
     s = O.index_scores(q, w, kc[: pos + 1], ks[: pos + 1])
     a = O.index_scores(q, np.abs(w), kc[: pos + 1], ks[: pos + 1])
     return s, a

@@ -196,3 +196,16 @@ def test_cache_append_rejects_bad_host_args(L):
     args[3], args[7], args[8] = None, None, 0
     args[0] = -1
     assert f(*args) == 1 and "n_tok" in _err()
+
+
+def test_index_score_mxfp4_rejects_bad_host_args(L):
+    f = L.dsa_index_score_mxfp4
+    ok_args = [2, 3, 1000, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 4352, FAKE, 16, FAKE, 1000, 0,
+               None, 0, None]
+    for patch, word in [({9: 4351}, "key_page_stride"), ({12: None}, "scores"),
+                        ({9: 4360}, "key_page_stride")]:
+        args = list(ok_args)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == 1, (patch, _err())
+        assert word in _err(), (patch, _err())

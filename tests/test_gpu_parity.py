@@ -40,7 +40,7 @@ def run_scores(batch):
     scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
     dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
                         batch.block_table, scores, max_seq_len=wl.max_seq_len,
-                        max_q_per_seq=max(wl.q_per_seq))
+                        max_q_per_seq=max(wl.q_per_seq), key_format=wl.key_format)
     torch.cuda.synchronize()
     return scores
 
@@ -345,7 +345,7 @@ def _end_to_end(wl, rows, num_splits=None):
     S = num_splits or wl.num_splits
     say("e2e", wl.name, "rows", rows, "S", S)
     batch = synth.make_batch(wl, DEV)
-    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S)
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, key_format=wl.key_format)
     out, lse = step.run(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
                         batch.block_table, batch.q_mla, batch.latent_pool, batch.latent_scale,
                         batch.softmax_scale, max(wl.q_per_seq))
@@ -462,7 +462,8 @@ def _fused(batch, k):
     ws = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k))
     dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
                         batch.block_table, scores, max_seq_len=wl.max_seq_len,
-                        max_q_per_seq=max(wl.q_per_seq), cand_k=k, cand_workspace=ws)
+                        max_q_per_seq=max(wl.q_per_seq), cand_k=k, cand_workspace=ws,
+                        key_format=wl.key_format)
     dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, idx, slot, ws,
                  max_seq_len=wl.max_seq_len, from_candidates=True)
     torch.cuda.synchronize()
@@ -759,3 +760,57 @@ def test_cache_append_keys_only_leaves_latents_and_feeds_the_indexer():
         mag = O.index_scores(batch.q_idx[row].cpu().double().numpy(),
                              np.abs(batch.head_w[row].cpu().numpy()), kc, ks)
         check_scores(scores[row, : pos + 1].cpu().numpy(), ref, mag, f"append row {row}")
+
+
+# ------------------------------------------------------------------------ MXFP4 index keys
+MX_SMALL = [
+    synth.custom([300, 64, 129, 1000], [1, 2, 3, 8], topk=128, seed=81, name="mx-ragged",
+                 key_format="mxfp4"),
+    synth.custom([5000, 4097], [4, 5], topk=2048, seed=82, name="mx-spec-small",
+                 key_format="mxfp4"),
+    synth.custom([1, 63, 65], [1, 1, 1], topk=16, seed=83, name="mx-tiny-tails",
+                 key_format="mxfp4"),
+]
+
+
+@pytest.mark.parametrize("wl", MX_SMALL, ids=lambda w: w.name)
+def test_index_scores_mxfp4_small(wl):
+    say("mx index", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    scores = run_scores(batch)
+    h = host(batch)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref, mag = oracle_scores(batch, row, keys=request_keys(batch, b, h["key_pool"], h["bt"]))
+        check_scores(scores[row, : pos + 1].cpu().numpy(), ref, mag, f"{wl.name} row {row}")
+
+
+@pytest.mark.parametrize("wl", MX_SMALL[:2] + [synth.custom([131072], [1], topk=2048, seed=84,
+                                                             name="mx-128k", key_format="mxfp4")],
+                         ids=lambda w: w.name)
+def test_index_mxfp4_fused_candidates_are_bitwise_the_stage_by_stage_path(wl):
+    say("mx fused", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    s1, i1, t1 = _stage_by_stage(batch, wl.topk)
+    s2, i2, t2 = _fused(batch, wl.topk)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        assert torch.equal(s1[row, : pos + 1], s2[row, : pos + 1]), row
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+
+
+def test_index_mxfp4_requires_stored_scores():
+    wl = MX_SMALL[0]
+    batch = synth.make_batch(wl, DEV)
+    ws = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, wl.topk))
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                            batch.block_table, None, max_seq_len=wl.max_seq_len,
+                            max_q_per_seq=max(wl.q_per_seq), cand_k=wl.topk, cand_workspace=ws,
+                            key_format="mxfp4")
+
+
+def test_end_to_end_tiny_mxfp4():
+    _end_to_end(synth.workload("tiny-mxfp4"), rows=[0])
+
+
+def test_end_to_end_long_mxfp4_full_size():
+    _end_to_end(synth.workload("long-mxfp4"), rows=[0, 17])
