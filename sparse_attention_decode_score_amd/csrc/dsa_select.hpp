@@ -17,7 +17,10 @@ constexpr int kGroupTok = 256;      // tokens per first-pass group (one wave, 4 
 constexpr int kFinalThreads = DSA_FINAL_THREADS;  // threads of the final pass
 constexpr int kFinalWaves = kFinalThreads / 64;
 constexpr int kFinalPerThread = 32;  // at most, in registers
-constexpr int kBucketMax = 512;      // keys of the last search bucket, finished from LDS
+#ifndef DSA_BUCKET_MAX
+#define DSA_BUCKET_MAX 512
+#endif
+constexpr int kBucketMax = DSA_BUCKET_MAX;  // keys of the last search bucket, finished from LDS
 constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds on chip
 
 // Per-group record of the first selection pass.
