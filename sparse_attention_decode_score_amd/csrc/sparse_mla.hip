@@ -214,14 +214,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         if (lane == 0) valid_mask[buf] = m;
       }
     };
-    // Every wave executes the same barriers: barrier 1, three per tile (A, B, C) and the two
-    // of the compute waves' finalize step.  Tile i lives in ring[i % kRing].  Under load a
-    // gather request can wait a long time to issue (every workgroup of the chip gathers at
-    // once), and a loader wave late for a barrier holds all six compute waves, so the
-    // loader requests one tile per step and at most two are in flight: tile 0 alone
-    // first, tile 1 after barrier 1; in the step of tile t it writes tile t+1 to the free
-    // LDS buffer between A and B, and requests tile t+kRing between B and C.  Steps past
-    // the last tile only move zero rows, after the compute waves are done with the ring.
+    // Every wave executes the same barriers: barrier 1, two per tile (A, B), one after the
+    // last tile and the two of the compute waves' finalize step.  Tile i lives in
+    // ring[i % kRing].  Under load a gather request can wait a long time to issue (every
+    // workgroup of the chip gathers at once), and a loader wave late for a barrier holds
+    // all six compute waves, so the loader requests one tile per step and at most two are
+    // in flight: tile 0 alone first, tile 1 after barrier 1; in the step of tile t it writes
+    // tile t+1 into the other LDS buffer between A and B (every wave has finished tile t-1,
+    // which read that buffer, before A), and requests tile t+kRing after B.  It stops at the
+    // last tile: requests past it (zero rows) are left unread.
     static_assert(kRing == 3, "the schedule below is written for a ring of three tiles");
     TileRegs ring[kRing];
     issue(0, ring[0]);
@@ -233,20 +234,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     store(1, ring[1], 1);
     __syncthreads();  // B
     issue(3, ring[0]);
-    __syncthreads();  // C
 #pragma unroll 1
     for (int t0 = 1; t0 < n_tiles; t0 += kRing) {
 #pragma unroll
       for (int u = 0; u < kRing; ++u) {
         const int t = t0 + u;  // t % kRing == (1 + u) % kRing
-        const bool live = t < n_tiles;
-        if (live) __syncthreads();  // A
+        if (t >= n_tiles) break;  // uniform
+        __syncthreads();  // A
         store(t + 1, ring[(u + 2) % kRing], (t + 1) & 1);
-        if (live) __syncthreads();  // B
+        __syncthreads();  // B
         issue(t + kRing, ring[(u + 1) % kRing]);
-        if (live) __syncthreads();  // C
       }
     }
+    __syncthreads();  // after the last tile
     __syncthreads();
     __syncthreads();
     return;
@@ -422,8 +422,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         acc[dt] = mfma_32x32x64_fp8(pl, B, acc[dt]);
       }
     }
-    __syncthreads();
+    // (no barrier here: the next tile's maxima and probabilities are written only after
+    // its barrier A, which every wave reaches after this tile's values product)
   }
+  __syncthreads();  // after the last tile
 
   // ------------------------------------------------------------------ finalize
   // each wave summed the probabilities of its own token halves: add the partner's
