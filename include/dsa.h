@@ -134,8 +134,8 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
  *   b * 1024 + o * 16, byte j holding dims 32b + 2j (low nibble) and 32b + 2j + 1 (high
  *   nibble) as E2M1 (OCP MX); the E8M0 scale of block b of token o is the byte at
  *   4096 + 4 * o + b.
- *   Every other argument as for dsa_index_score, except that scores must be given (the
- *   final top-k pass recomputes missing scores from E4M3 keys only).
+ *   Every other argument as for dsa_index_score (with scores = NULL, pass key_format = 1
+ *   to the final top-k pass).
  */
 dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
                                  int32_t max_q_per_seq, const int32_t* cu_q,
@@ -164,12 +164,13 @@ dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_
  *   workspace: device memory of at least dsa_topk_workspace_size(n_q, max_seq_len, k)
  *   bytes, 256-byte aligned; with from_candidates = 0 its contents need no
  *   initialisation.  It is scratch after the call.
- *   q_idx_bf16, head_w, key_pages, key_page_stride: all NULL / 0 when the scores were
- *   stored.  When dsa_index_score stored none (scores = NULL there), pass its query, head
- *   weights and index-key cache here (from_candidates = 1 and block_table required): the
- *   groups that must be re-read are recomputed with the indexer's own arithmetic (bitwise
- *   its scores) into `scores`, which is then scratch of [n_q][score_stride] fp32 whose
- *   contents need no initialisation.
+ *   q_idx_bf16, head_w, key_pages, key_page_stride, key_format: all NULL / 0 when the
+ *   scores were stored.  When dsa_index_score or dsa_index_score_mxfp4 stored none
+ *   (scores = NULL there), pass its query, head weights and index-key cache here, with
+ *   key_format 0 (E4M3 keys) or 1 (MXFP4 keys) (from_candidates = 1 and block_table
+ *   required): the groups that must be re-read are recomputed with the indexer's own
+ *   arithmetic (bitwise its scores) into `scores`, which is then scratch of
+ *   [n_q][score_stride] fp32 whose contents need no initialisation.
  */
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k);
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
@@ -177,7 +178,8 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
                     int32_t* topk_slot, void* workspace, size_t workspace_bytes,
                     int32_t from_candidates, const void* q_idx_bf16, const float* head_w,
-                    const void* key_pages, int64_t key_page_stride, void* stream);
+                    const void* key_pages, int64_t key_page_stride, int32_t key_format,
+                    void* stream);
 
 /*
  * Stage 3 — exact MLA (NoPE) over the selected slots, one query row at a time.
@@ -225,8 +227,8 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
  * row repeats it) removes one launch and the wait on a single workgroup per row.
  *   Batch, scores, k, block_table (required here): as for dsa_topk.
  *   cand_workspace: dsa_topk_workspace_size(n_q, max_seq_len, k) bytes, 256-byte aligned,
- *   read only.  q_idx_bf16, head_w, key_pages, key_page_stride: as for dsa_topk (scores
- *   not stored: `scores` is scratch).
+ *   read only.  q_idx_bf16, head_w, key_pages, key_page_stride, key_format: as for
+ *   dsa_topk (scores not stored: `scores` is scratch).
  *   topk_idx, topk_slot: optional outputs (each may be NULL), as dsa_topk writes them.
  *   Query, latent cache, softmax_scale, num_splits (S <= k), out_bf16 [n_q][96][512] bf16,
  *   lse [n_q][96] fp32, workspace (S > 1: dsa_sparse_mla_workspace_size(n_q, S) bytes,
@@ -239,7 +241,7 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                                int32_t bt_stride, const void* cand_workspace,
                                size_t cand_workspace_bytes, const void* q_idx_bf16,
                                const float* head_w, const void* key_pages,
-                               int64_t key_page_stride, int32_t* topk_idx,
+                               int64_t key_page_stride, int32_t key_format, int32_t* topk_idx,
                                int32_t* topk_slot, const void* q_bf16, const void* q8,
                                const float* q_scale, const void* latent_pages,
                                int64_t latent_page_stride, float latent_scale,

@@ -52,13 +52,13 @@ def lib() -> ctypes.CDLL:
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
-                               _I32, _P, _P, _P, _I64, _P]
+                               _I32, _P, _P, _P, _I64, _I32, _P]
         L.dsa_sparse_mla_workspace_size.argtypes = [_I32, _I32]
         L.dsa_sparse_mla_workspace_size.restype = _SZ
         L.dsa_sparse_mla_decode.argtypes = [_I32, _P, _P, _P, _P, _I64, _F32, _P, _I32, _F32, _I32,
                                             _P, _P, _P, _P, _P, _SZ, _P]
         L.dsa_topk_sparse_mla.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P,
-                                          _SZ, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I64,
+                                          _SZ, _P, _P, _P, _I64, _I32, _P, _P, _P, _P, _P, _P, _I64,
                                           _F32, _F32, _I32, _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_cache_append.argtypes = [_I32, _P, _P, _P, _F32, _P, _I64, _P, _I64, _P]
@@ -122,9 +122,9 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
     """Indexer scores into scores [n_q, score_stride] (fp32); with cand_workspace, also the
     per-chunk top-k candidates for a top-k of cand_k (consumed by dsa_topk with
     from_candidates=True).  scores=None with cand_workspace: candidates only (no scores
-    stored; pass rescore=(q_idx, head_w, key_pages) to the final top-k pass).
-    key_format "mxfp4": the key cache holds MXFP4 keys (dsa_index_score_mxfp4; scores
-    must then be given)."""
+    stored; pass rescore=(q_idx, head_w, key_pages) and the same key_format to the final
+    top-k pass).  key_format "mxfp4": the key cache holds MXFP4 keys
+    (dsa_index_score_mxfp4)."""
     if key_format not in ("e4m3", "mxfp4"):
         raise ValueError(f"key_format must be 'e4m3' or 'mxfp4' (got {key_format!r})")
     num_seqs = seq_lens.shape[0]
@@ -152,16 +152,22 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
                                  _stream(stream)))
 
 
-def _rescore_args(rescore):
-    """(q_idx, head_w, key_pages[, key_page_stride]) -> C arguments, or NULLs."""
+_KEY_FORMATS = {"e4m3": 0, "mxfp4": 1}
+
+
+def _rescore_args(rescore, key_format):
+    """(q_idx, head_w, key_pages[, key_page_stride]) and the key cache's format -> C
+    arguments, or NULLs."""
+    if key_format not in _KEY_FORMATS:
+        raise ValueError(f"key_format must be 'e4m3' or 'mxfp4' (got {key_format!r})")
     if rescore is None:
-        return (None, None, None, 0)
+        return (None, None, None, 0, 0)
     q_idx, head_w, key_pages = rescore[:3]
     _expect(q_idx, "q_idx", torch.bfloat16)
     _expect(head_w, "head_w", torch.float32)
     stride = (rescore[3] if len(rescore) > 3
               else key_pages.stride(0) * key_pages.element_size())
-    return (_ptr(q_idx), _ptr(head_w), _ptr(key_pages), int(stride))
+    return (_ptr(q_idx), _ptr(head_w), _ptr(key_pages), int(stride), _KEY_FORMATS[key_format])
 
 
 def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
@@ -171,9 +177,11 @@ def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
 def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,
              block_table: Optional[torch.Tensor], topk_idx: torch.Tensor,
              topk_slot: Optional[torch.Tensor], workspace: torch.Tensor, *, max_seq_len: int,
-             from_candidates: bool = False, rescore=None, stream=None) -> None:
+             from_candidates: bool = False, rescore=None, key_format: str = "e4m3",
+             stream=None) -> None:
     """Exact top-k token indices (and physical slots) of every row's visible scores.
-    rescore=(q_idx, head_w, key_pages): the indexer stored no scores; scores is scratch."""
+    rescore=(q_idx, head_w, key_pages): the indexer stored no scores; scores is scratch
+    (key_format: that of the index-key cache, "e4m3" or "mxfp4")."""
     num_seqs = seq_lens.shape[0]
     n_q = scores.shape[0]
     _expect(scores, "scores", torch.float32)
@@ -185,7 +193,8 @@ def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k
                           scores.shape[1], int(k), _ptr(block_table),
                           block_table.shape[1] if block_table is not None else 0,
                           _ptr(topk_idx), _ptr(topk_slot), _ptr(workspace), workspace.numel(),
-                          int(bool(from_candidates)), *_rescore_args(rescore), _stream(stream)))
+                          int(bool(from_candidates)), *_rescore_args(rescore, key_format),
+                          _stream(stream)))
 
 
 def dsa_sparse_mla_workspace_size(n_q: int, num_splits: int) -> int:
@@ -251,11 +260,12 @@ def dsa_topk_sparse_mla(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torc
                         q8: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None,
                         latent_page_stride: Optional[int] = None, rescore=None,
-                        stream=None) -> None:
+                        key_format: str = "e4m3", stream=None) -> None:
     """Final top-k pass and sparse MLA in one launch: every attention workgroup selects its
     row's top k from the candidates dsa_index_score left in cand_workspace (cand_k = k), then
     attends over its split of them.  topk_idx / topk_slot, when given, receive the selection.
-    rescore=(q_idx, head_w, key_pages): the indexer stored no scores; scores is scratch."""
+    rescore=(q_idx, head_w, key_pages): the indexer stored no scores; scores is scratch
+    (key_format: that of the index-key cache)."""
     num_seqs = seq_lens.shape[0]
     n_q = scores.shape[0]
     _expect(scores, "scores", torch.float32)
@@ -281,7 +291,7 @@ def dsa_topk_sparse_mla(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torc
     _check(lib().dsa_topk_sparse_mla(
         num_seqs, n_q, int(max_seq_len), _ptr(cu_q), _ptr(seq_lens), _ptr(scores),
         scores.shape[1], int(k), _ptr(block_table), block_table.shape[1], _ptr(cand_workspace),
-        cand_workspace.numel(), *_rescore_args(rescore), _ptr(topk_idx), _ptr(topk_slot),
+        cand_workspace.numel(), *_rescore_args(rescore, key_format), _ptr(topk_idx), _ptr(topk_slot),
         _ptr(q_mla), _ptr(q8),
         _ptr(q_scale), _ptr(latent_pages), int(stride), float(latent_scale),
         float(softmax_scale), int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace),
@@ -338,11 +348,9 @@ class DecodeStep:
                  fused: bool = True, query_on_side_stream: bool = False,
                  select_in_attention: Optional[bool] = None, write_selection: bool = True,
                  store_scores: Optional[bool] = None, key_format: str = "e4m3"):
+        if key_format not in _KEY_FORMATS:
+            raise ValueError(f"key_format must be 'e4m3' or 'mxfp4' (got {key_format!r})")
         self.key_format = key_format
-        if key_format == "mxfp4":
-            if store_scores is False:
-                raise ValueError("MXFP4 keys need stored scores")
-            store_scores = True
         if select_in_attention is None:
             select_in_attention = fused
         if store_scores is None:
@@ -389,7 +397,7 @@ class DecodeStep:
         """Stage 2."""
         dsa_topk(cu_q, seq_lens, self.scores, self.k, block_table, self.topk_idx, self.topk_slot,
                  self.workspace, max_seq_len=self.max_seq_len, from_candidates=self.fused,
-                 rescore=self._rescore, stream=stream)
+                 rescore=self._rescore, key_format=self.key_format, stream=stream)
 
     def prepare_query(self, q_mla, stream=None):
         """E4M3 codes and scales of the MLA query (stage 3's own quantisation)."""
@@ -419,7 +427,7 @@ class DecodeStep:
                             out=self.out, lse=self.lse,
                             topk_idx=self.topk_idx if self.write_selection else None,
                             topk_slot=self.topk_slot if self.write_selection else None,
-                            rescore=self._rescore,
+                            rescore=self._rescore, key_format=self.key_format,
                             q8=self.q8 if prepared else None,
                             q_scale=self.q_scale if prepared else None,
                             workspace=self.mla_workspace, stream=stream)

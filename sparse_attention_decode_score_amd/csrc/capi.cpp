@@ -78,18 +78,21 @@ dsa_status check_mla_inputs(int32_t n_q, const void* q_bf16, const void* q8,
 
 // The indexer inputs the final top-k pass recomputes scores from (all NULL: scores stored).
 dsa_status check_rescore(const void* q_idx_bf16, const float* head_w, const void* key_pages,
-                         int64_t key_page_stride, const int32_t* block_table,
-                         int32_t from_candidates) {
+                         int64_t key_page_stride, int32_t key_format,
+                         const int32_t* block_table, int32_t from_candidates) {
   if (!q_idx_bf16 && !head_w && !key_pages) return DSA_OK;
+  if (key_format != 0 && key_format != 1)
+    return fail(DSA_ERR_UNSUPPORTED, "key_format must be 0 (E4M3) or 1 (MXFP4) (got %d)", key_format);
   DSA_REQUIRE(q_idx_bf16 && head_w && key_pages,
               "q_idx_bf16, head_w and key_pages must all be given (scores not stored) or all be NULL");
   DSA_REQUIRE(from_candidates, "recomputing scores needs the indexer's candidates (from_candidates)");
   DSA_REQUIRE(block_table, "recomputing scores needs block_table");
   DSA_REQUIRE(aligned(q_idx_bf16, 16) && aligned(head_w, 16) && aligned(key_pages, 16),
               "q_idx_bf16, head_w and key_pages must be 16-byte aligned");
-  DSA_REQUIRE(key_page_stride >= DSA_IDX_PAGE_BYTES && key_page_stride % 16 == 0,
-              "key_page_stride must be >= 8448 and a multiple of 16 (got %lld)",
-              (long long)key_page_stride);
+  const int64_t page_bytes = key_format ? DSA_IDX_MXFP4_PAGE_BYTES : DSA_IDX_PAGE_BYTES;
+  DSA_REQUIRE(key_page_stride >= page_bytes && key_page_stride % 16 == 0,
+              "key_page_stride must be >= %lld and a multiple of 16 (got %lld)",
+              (long long)page_bytes, (long long)key_page_stride);
   return DSA_OK;
 }
 
@@ -143,13 +146,8 @@ dsa_status index_score_checked(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
               "max_q_per_seq must be in 1..n_q (got %d)", max_q_per_seq);
   DSA_REQUIRE(q_bf16 && head_w && key_pages && block_table,
               "q_bf16, head_w, key_pages and block_table must be non-null");
-  if (mxfp4) {
-    DSA_REQUIRE(scores, "scores must be non-null with MXFP4 keys (the final top-k pass "
-                        "recomputes scores from E4M3 keys only)");
-  } else {
-    DSA_REQUIRE(scores || cand_workspace,
-                "scores may be NULL only when cand_workspace is given (candidates only)");
-  }
+  DSA_REQUIRE(scores || cand_workspace,
+              "scores may be NULL only when cand_workspace is given (candidates only)");
   DSA_REQUIRE(aligned(q_bf16, 16), "q_bf16 must be 16-byte aligned");
   DSA_REQUIRE(aligned(head_w, 16), "head_w must be 16-byte aligned");
   DSA_REQUIRE(aligned(key_pages, 16), "key_pages must be 16-byte aligned");
@@ -221,10 +219,12 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,
                     int32_t* topk_slot, void* workspace, size_t workspace_bytes,
                     int32_t from_candidates, const void* q_idx_bf16, const float* head_w,
-                    const void* key_pages, int64_t key_page_stride, void* stream) {
+                    const void* key_pages, int64_t key_page_stride, int32_t key_format,
+                    void* stream) {
   dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
   if (st != DSA_OK) return st;
-  st = check_rescore(q_idx_bf16, head_w, key_pages, key_page_stride, block_table, from_candidates);
+  st = check_rescore(q_idx_bf16, head_w, key_pages, key_page_stride, key_format, block_table,
+                     from_candidates);
   if (st != DSA_OK) return st;
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k must be in 1..4096 (got %d)", k);
   DSA_REQUIRE(scores && topk_idx, "scores and topk_idx must be non-null");
@@ -244,7 +244,8 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
   if (from_candidates) {
     const dsa::TopkBuffers t = dsa::topk_buffers(workspace, n_q, max_seq_len, k);
     const dsa::IndexRescore rs{static_cast<const uint16_t*>(q_idx_bf16), head_w,
-                               static_cast<const uint8_t*>(key_pages), key_page_stride};
+                               static_cast<const uint8_t*>(key_pages), key_page_stride,
+                               key_format};
     return launched(dsa::launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k,
                                            t, rs, block_table, bt_stride, topk_idx, topk_slot, hs),
                     "dsa_topk");
@@ -296,7 +297,7 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                                int32_t bt_stride, const void* cand_workspace,
                                size_t cand_workspace_bytes, const void* q_idx_bf16,
                                const float* head_w, const void* key_pages,
-                               int64_t key_page_stride, int32_t* topk_idx,
+                               int64_t key_page_stride, int32_t key_format, int32_t* topk_idx,
                                int32_t* topk_slot, const void* q_bf16, const void* q8,
                                const float* q_scale, const void* latent_pages,
                                int64_t latent_page_stride, float latent_scale,
@@ -308,7 +309,7 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                         k, softmax_scale, num_splits);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(scores && block_table, "scores and block_table must be non-null");
-  st = check_rescore(q_idx_bf16, head_w, key_pages, key_page_stride, block_table, 1);
+  st = check_rescore(q_idx_bf16, head_w, key_pages, key_page_stride, key_format, block_table, 1);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(score_stride >= max_seq_len, "score_stride (%lld) must be >= max_seq_len (%d)",
               (long long)score_stride, max_seq_len);
@@ -325,7 +326,7 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
   const dsa::TopkBuffers t =
       dsa::topk_buffers(const_cast<void*>(cand_workspace), n_q, max_seq_len, k);
   const dsa::IndexRescore rs{static_cast<const uint16_t*>(q_idx_bf16), head_w,
-                             static_cast<const uint8_t*>(key_pages), key_page_stride};
+                             static_cast<const uint8_t*>(key_pages), key_page_stride, key_format};
   return launched(dsa::launch_topk_sparse_mla(
                       num_seqs, n_q, cu_q, seq_lens, scores, score_stride, t,
                       rs, block_table,

@@ -21,6 +21,7 @@ struct IndexRescore {
   const float* head_w;     // [n_q][32]
   const uint8_t* key_pages;
   int64_t page_stride;
+  int mxfp4;               // key cache format: 0 E4M3 + fp32 scale, 1 MXFP4
 };
 
 struct TopkBuffers {

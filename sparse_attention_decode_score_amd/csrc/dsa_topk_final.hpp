@@ -94,9 +94,17 @@ __device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n
   for (int g = wave; g < n_groups; g += kFinalWaves) {
     if (!need(g)) continue;  // the same for every lane of the wave
     for (int p = g * kPagesPerGroup; p < min(n_pages, (g + 1) * kPagesPerGroup); ++p) {
-      KeyPage kp;
-      load_key_page(kp, rs.key_pages + (int64_t)bt_row[p] * rs.page_stride, lane);
-      const float sc = score_key_page(q8, w, kp, lane);
+      const uint8_t* page = rs.key_pages + (int64_t)bt_row[p] * rs.page_stride;
+      float sc;
+      if (rs.mxfp4) {
+        KeyPageMx kp;
+        load_key_page(kp, page, lane);
+        sc = score_key_page(q8, w, kp, lane);
+      } else {
+        KeyPage kp;
+        load_key_page(kp, page, lane);
+        sc = score_key_page(q8, w, kp, lane);
+      }
       const int t = p * kPage + lane;
       if (t < n_vis) row_scores[t] = sc;
     }

@@ -151,7 +151,7 @@ hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k, t,
-                           IndexRescore{nullptr, nullptr, nullptr, 0}, block_table, bt_stride,
+                           IndexRescore{nullptr, nullptr, nullptr, 0, 0}, block_table, bt_stride,
                            topk_idx, topk_slot, st);
 }
 

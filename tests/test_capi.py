@@ -75,7 +75,7 @@ def test_topk_rejects_bad_host_args(L):
         need = L.dsa_topk_workspace_size(3, 1000, 2048)
         assert need > 0
         base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE,
-                ctypes.c_void_p(0x10000), need, fused, None, None, None, 0, None]
+                ctypes.c_void_p(0x10000), need, fused, None, None, None, 0, 0, None]
         for patch, status in [({7: 0}, 2), ({7: 4097}, 2), ({8: None}, 1), ({6: 10}, 1),
                               ({13: need - 1}, 3), ({12: None}, 3),
                               ({12: ctypes.c_void_p(0x10010)}, 1)]:
@@ -86,14 +86,18 @@ def test_topk_rejects_bad_host_args(L):
     # recomputation inputs: all or none, only with candidates, with a block table
     base = [2, 3, 1000, FAKE, FAKE, FAKE, 1000, 2048, FAKE, 16, FAKE, FAKE,
             ctypes.c_void_p(0x10000), L.dsa_topk_workspace_size(3, 1000, 2048), 1,
-            FAKE, FAKE, FAKE, 8448, None]
-    for patch, word in [({16: None}, "all"), ({14: 0}, "from_candidates"),
-                        ({8: None, 11: None}, "block_table"), ({18: 8447}, "key_page_stride"),
-                        ({15: FAKE_ODD}, "aligned")]:
+            FAKE, FAKE, FAKE, 8448, 0, None]
+    for patch, status, word in [
+            ({16: None}, 1, "all"), ({14: 0}, 1, "from_candidates"),
+            ({8: None, 11: None}, 1, "block_table"), ({18: 8447}, 1, "key_page_stride"),
+            ({15: FAKE_ODD}, 1, "aligned"), ({19: 2}, 2, "key_format"),
+            ({19: -1}, 2, "key_format"),
+            # MXFP4 keys: 4,352-byte pages; E4M3 keys need 8,448
+            ({18: 4351, 19: 1}, 1, "key_page_stride"), ({18: 4352}, 1, "key_page_stride")]:
         args = list(base)
         for i, v in patch.items():
             args[i] = v
-        assert f(*args) == 1, (patch, _err())
+        assert f(*args) == status, (patch, _err())
         assert word in _err(), (patch, _err())
     assert L.dsa_topk_workspace_size(0, 10, 10) == 0
     assert L.dsa_topk_workspace_size(4, 10, 5000) == 0
@@ -140,21 +144,24 @@ def test_topk_sparse_mla_rejects_bad_host_args(L):
     need = L.dsa_sparse_mla_workspace_size(4, 4)
     CW, WS = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
     # num_seqs, n_q, max_seq_len, cu_q, seq_lens, scores, score_stride, k, block_table,
-    # bt_stride, cand_ws, cand_bytes, q_idx, head_w, key_pages, key_stride, topk_idx,
-    # topk_slot, q_bf16, q8, q_scale, latent, latent_stride, latent_scale, softmax_scale, S,
-    # out, lse, workspace, ws_bytes, stream
-    base = [2, 4, 1000, FAKE, FAKE, FAKE, 1000, 512, FAKE, 16, CW, cand, None, None, None, 0,
+    # bt_stride, cand_ws, cand_bytes, q_idx, head_w, key_pages, key_stride, key_format,
+    # topk_idx, topk_slot, q_bf16, q8, q_scale, latent, latent_stride, latent_scale,
+    # softmax_scale, S, out, lse, workspace, ws_bytes, stream
+    base = [2, 4, 1000, FAKE, FAKE, FAKE, 1000, 512, FAKE, 16, CW, cand, None, None, None, 0, 0,
             None, None, FAKE, None, None, FAKE, 36864, ctypes.c_float(0.01),
             ctypes.c_float(0.04), 4, FAKE, FAKE, WS, need, None]
+    RS = {12: FAKE, 13: FAKE, 14: FAKE}
     cases = [({0: 0}, 1, "num_seqs"), ({7: 0}, 2, "k"), ({7: 4097}, 2, "k"),
-             ({25: 65}, 2, "num_splits"), ({8: None}, 1, "block_table"),
+             ({26: 65}, 2, "num_splits"), ({8: None}, 1, "block_table"),
              ({5: None}, 1, "scores"), ({6: 999}, 1, "score_stride"), ({9: 15}, 1, "bt_stride"),
              ({10: None}, 3, "candidate"), ({11: cand - 1}, 3, "candidate"),
              ({10: ctypes.c_void_p(0x10010)}, 1, "cand_workspace"),
-             ({12: FAKE}, 1, "all"), ({12: FAKE, 13: FAKE, 14: FAKE, 15: 100}, 1, "key_page_stride"),
-             ({18: None}, 1, "query"), ({19: FAKE}, 1, "q8"), ({21: None}, 1, "latent_pages"),
-             ({22: 36863}, 1, "latent_page_stride"), ({26: None}, 1, "out_bf16"),
-             ({28: None}, 3, "workspace"), ({29: need - 1}, 3, "workspace")]
+             ({12: FAKE}, 1, "all"), ({**RS, 15: 100}, 1, "key_page_stride"),
+             ({**RS, 15: 8448, 16: 3}, 2, "key_format"),
+             ({**RS, 15: 4351, 16: 1}, 1, "key_page_stride"),
+             ({19: None}, 1, "query"), ({20: FAKE}, 1, "q8"), ({22: None}, 1, "latent_pages"),
+             ({23: 36863}, 1, "latent_page_stride"), ({27: None}, 1, "out_bf16"),
+             ({29: None}, 3, "workspace"), ({30: need - 1}, 3, "workspace")]
     for patch, status, word in cases:
         args = list(base)
         for i, v in patch.items():
@@ -162,7 +169,7 @@ def test_topk_sparse_mla_rejects_bad_host_args(L):
         assert f(*args) == status, (patch, _err())
         assert word in _err(), (patch, _err())
     args = list(base)
-    args[7], args[25] = 3, 4                     # more splits than selected tokens
+    args[7], args[26] = 3, 4                     # more splits than selected tokens
     assert f(*args) == 1 and "num_splits" in _err()
 
 

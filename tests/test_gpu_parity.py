@@ -513,7 +513,8 @@ def _select_attend(batch, k, num_splits, prepared=False, outputs=True):
     ws = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k))
     dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
                         batch.block_table, scores, max_seq_len=wl.max_seq_len,
-                        max_q_per_seq=max(wl.q_per_seq), cand_k=k, cand_workspace=ws)
+                        max_q_per_seq=max(wl.q_per_seq), cand_k=k, cand_workspace=ws,
+                        key_format=wl.key_format)
     idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
     slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
     out = torch.full((wl.n_q, 96, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
@@ -608,7 +609,7 @@ def _index(batch, k, store_scores, ws_fill=0):
     dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
                         batch.block_table, scores if store_scores else None,
                         max_seq_len=wl.max_seq_len, max_q_per_seq=max(wl.q_per_seq),
-                        cand_k=k, cand_workspace=ws)
+                        cand_k=k, cand_workspace=ws, key_format=wl.key_format)
     torch.cuda.synchronize()
     return scores, ws
 
@@ -619,16 +620,23 @@ def _final(batch, k, scores, ws, rescore):
     slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
     dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, idx, slot, ws,
                  max_seq_len=wl.max_seq_len, from_candidates=True,
-                 rescore=(batch.q_idx, batch.head_w, batch.key_pool) if rescore else None)
+                 rescore=(batch.q_idx, batch.head_w, batch.key_pool) if rescore else None,
+                 key_format=wl.key_format)
     torch.cuda.synchronize()
     return idx, slot
 
 
 def _boost_pages(batch, b, pages, factor=1000.0):
-    """Multiplies the key scales of logical pages `pages` of request b (scores scale too)."""
+    """Multiplies the key scales of logical pages `pages` of request b (scores scale too):
+    fp32 scales by `factor`; MXFP4 E8M0 block scales by 2^10."""
     bt = batch.block_table.cpu().numpy()
     for page in pages:
-        batch.key_pool[int(bt[b, page]), 8192:].view(torch.float32).mul_(factor)
+        if batch.wl.key_format == "mxfp4":
+            sc = batch.key_pool[int(bt[b, page]), 4096:4352]
+            assert int(sc.max().item()) <= 244          # stays below the NaN code 0xFF
+            sc.add_(10)
+        else:
+            batch.key_pool[int(bt[b, page]), 8192:].view(torch.float32).mul_(factor)
     torch.cuda.synchronize()
 
 
@@ -649,7 +657,8 @@ def _check_no_scores_matches(batch, k, expect_rescored):
         done = ~torch.isnan(got)
         n_rescored += int(done.sum().item())
         assert torch.equal(got[done], s_ref[row, : pos + 1][done]), row
-    assert (n_rescored > 0) == expect_rescored, n_rescored
+    if expect_rescored is not None:
+        assert (n_rescored > 0) == expect_rescored, n_rescored
     return i2, n_rescored
 
 
@@ -682,9 +691,12 @@ def test_no_stored_scores_recomputes_the_whole_row_when_the_resend_is_too_large(
     assert n == L
 
 
+@pytest.mark.parametrize("key_format", ["e4m3", "mxfp4"])
 @pytest.mark.parametrize("num_splits", [1, 4])
-def test_select_in_attention_with_no_stored_scores(num_splits):
-    wl = synth.custom([40000, 9000], [2, 1], topk=2048, seed=66, name="rescore-attend")
+def test_select_in_attention_with_no_stored_scores(num_splits, key_format):
+    say("select+attend no scores", num_splits, key_format)
+    wl = synth.custom([40000, 9000], [2, 1], topk=2048, seed=66, name="rescore-attend",
+                      key_format=key_format)
     batch = synth.make_batch(wl, DEV)
     _boost_pages(batch, 0, range(80, 96))
     i1, t1, o1, l1 = _select_attend(batch, 2048, num_splits)
@@ -698,7 +710,8 @@ def test_select_in_attention_with_no_stored_scores(num_splits):
                             batch.q_mla, batch.latent_pool, batch.latent_scale,
                             batch.softmax_scale, num_splits, max_seq_len=wl.max_seq_len,
                             out=out, lse=lse, topk_idx=idx, topk_slot=slot,
-                            rescore=(batch.q_idx, batch.head_w, batch.key_pool))
+                            rescore=(batch.q_idx, batch.head_w, batch.key_pool),
+                            key_format=key_format)
     torch.cuda.synchronize()
     assert torch.equal(i1, idx) and torch.equal(t1, slot)
     assert torch.equal(o1, out) and torch.equal(l1, lse)
@@ -797,15 +810,45 @@ def test_index_mxfp4_fused_candidates_are_bitwise_the_stage_by_stage_path(wl):
     assert torch.equal(i1, i2) and torch.equal(t1, t2)
 
 
-def test_index_mxfp4_requires_stored_scores():
-    wl = MX_SMALL[0]
+@pytest.mark.parametrize("wl", MX_SMALL[:2] + [synth.custom([131072], [1], topk=2048, seed=85,
+                                                             name="mx-128k", key_format="mxfp4")],
+                         ids=lambda w: w.name)
+def test_no_stored_scores_mxfp4_is_bitwise_the_stored_scores_path(wl):
+    say("mx no scores", wl.name)
     batch = synth.make_batch(wl, DEV)
-    ws = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, wl.topk))
-    with pytest.raises(dsa.DsaError):
-        dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
-                            batch.block_table, None, max_seq_len=wl.max_seq_len,
-                            max_q_per_seq=max(wl.q_per_seq), cand_k=wl.topk, cand_workspace=ws,
-                            key_format="mxfp4")
+    _check_no_scores_matches(batch, wl.topk, expect_rescored=None)
+
+
+def test_no_stored_scores_mxfp4_recomputes_flagged_groups_exactly():
+    wl = synth.custom([40000], [2], topk=2048, seed=86, name="mx-rescore-skew",
+                      key_format="mxfp4")
+    batch = synth.make_batch(wl, DEV)
+    _boost_pages(batch, 0, range(80, 96))
+    idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
+    assert n <= 2 * 4 * 256
+    assert ((idx[0] >= 5120) & (idx[0] < 6144)).sum().item() > 200
+
+
+def test_no_stored_scores_mxfp4_recomputes_the_whole_row_when_the_resend_is_too_large():
+    L = 131072
+    wl = synth.custom([L], [1], topk=2048, seed=87, name="mx-rescore-all", key_format="mxfp4")
+    batch = synth.make_batch(wl, DEV)
+    _boost_pages(batch, 0, range(0, L // 64, 16))
+    idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
+    assert n == L
+
+
+def test_mxfp4_cache_with_the_e4m3_rescore_format_is_refused():
+    # an MXFP4 pool (4,352-byte pages) read as E4M3 keys (8,448-byte pages) fails the host check
+    wl = MX_SMALL[1]
+    batch = synth.make_batch(wl, DEV)
+    assert batch.key_pool.stride(0) == 4352
+    s_none, ws = _index(batch, wl.topk, False)
+    idx = torch.empty((wl.n_q, wl.topk), dtype=torch.int32, device=DEV)
+    with pytest.raises(dsa.DsaError, match="key_page_stride"):
+        dsa.dsa_topk(batch.cu_q, batch.seq_lens, s_none, wl.topk, batch.block_table, idx, None,
+                     ws, max_seq_len=wl.max_seq_len, from_candidates=True,
+                     rescore=(batch.q_idx, batch.head_w, batch.key_pool), key_format="e4m3")
 
 
 def test_end_to_end_tiny_mxfp4():
