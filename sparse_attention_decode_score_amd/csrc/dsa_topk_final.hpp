@@ -30,12 +30,12 @@ __device__ __forceinline__ void row_of(const int32_t* cu_q, const int32_t* seq_l
   pos = seq_lens[b] - (c1 - c0) + (row - c0);
 }
 
-// Copies, in element order, every element of get(0 .. n-1) whose key is >= K into
-// lkey / lidx (key, element index) while they fit in kFinalTile slots.  Returns the number of
-// such elements (more than kFinalTile: the copy is incomplete).
-template <class Get>
-__device__ int gather_at_least(const Get& get, int n, uint32_t K, uint32_t* lkey, int32_t* lidx,
-                               int* red, int& parity) {
+// Copies, in element order, every element e < n with keep(key, token) into lkey / lidx, where
+// get(e, key, token) gives element e, while they fit in kFinalTile slots.  Returns the number
+// of such elements (more than kFinalTile: the copy is incomplete).
+template <class Get, class Keep>
+__device__ int gather_kept(const Get& get, int n, const Keep& keep, uint32_t* lkey, int32_t* lidx,
+                           int* red, int& parity) {
   const int tid = threadIdx.x;
   constexpr int E = 16;
   constexpr int kTile = kFinalThreads * E;
@@ -43,21 +43,26 @@ __device__ int gather_at_least(const Get& get, int n, uint32_t K, uint32_t* lkey
 #pragma unroll 1
   for (int base = 0; base < n; base += kTile) {
     uint32_t tk[E];
+    int ti[E];
     int c = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const int e = base + tid * E + j;
-      tk[j] = e < n ? get(e) : kSentinel;
-      c += tk[j] >= K ? 1 : 0;
+      tk[j] = kSentinel;
+      ti[j] = 0;
+      if (e < n) get(e, tk[j], ti[j]);
+      const bool in = e < n && keep(tk[j], ti[j]);
+      tk[j] = in ? tk[j] : kSentinel;
+      c += in ? 1 : 0;
     }
     int tot;
     int pos = kept + block_excl_scan(c, &tot, red, parity);
     if (kept + tot <= kFinalTile) {
 #pragma unroll
       for (int j = 0; j < E; ++j) {
-        if (tk[j] >= K) {
+        if (tk[j] != kSentinel) {
           lkey[pos] = tk[j];
-          lidx[pos] = base + tid * E + j;
+          lidx[pos] = ti[j];
           ++pos;
         }
       }
@@ -91,8 +96,13 @@ __device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n
   __syncthreads();
   constexpr int kPagesPerGroup = kGroupTok / kPage;
   const int n_pages = (n_vis + kPage - 1) / kPage;
-  for (int g = wave; g < n_groups; g += kFinalWaves) {
-    if (!need(g)) continue;  // the same for every lane of the wave
+  // each wave tests 64 groups at once (one per lane) and scores the ones that need it
+#pragma unroll 1
+  for (int base = wave * 64; base < n_groups; base += kFinalWaves * 64) {
+    uint64_t todo = __ballot(base + lane < n_groups && need(base + lane));
+    while (todo) {
+    const int g = base + (int)__builtin_ctzll(todo);
+    todo &= todo - 1;
     for (int p = g * kPagesPerGroup; p < min(n_pages, (g + 1) * kPagesPerGroup); ++p) {
       const uint8_t* page = rs.key_pages + (int64_t)bt_row[p] * rs.page_stride;
       float sc;
@@ -107,6 +117,7 @@ __device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n
       }
       const int t = p * kPage + lane;
       if (t < n_vis) row_scores[t] = sc;
+    }
     }
   }
   __syncthreads();
@@ -241,44 +252,65 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
         total = kFinalTile + 1;
       }
       __syncthreads();
-      if (rs.q) {
-        // no stored scores: recompute the groups the resend reads (all of them when the
-        // resend does not fit on chip)
-        const bool all = total > kFinalTile;
-        rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
-                       [&](int g) { return all || flagged(g); }, rq8, rw);
-      }
+      // no stored scores: the flagged groups, which the resend reads in full, are recomputed
+      if (rs.q) rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores, flagged, rq8, rw);
+      // element e of the resend list (flagged groups in full, the others' candidates), found
+      // by a binary search over the group starts in out[]
+      auto resend_at = [&](int e, uint32_t& key, int& t) {
+        int lo = 0, hi = n_groups - 1;  // the last group starting at or before e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (out[mid] <= e) lo = mid;
+          else hi = mid - 1;
+        }
+        const int i = e - out[lo];
+        if (flagged(lo)) {
+          t = lo * kGroupTok + i;
+          key = score_key(src[t]);
+        } else {
+          key = ck[(int64_t)lo * m + i];
+          t = ci[(int64_t)lo * m + i];
+        }
+      };
       if (total <= kFinalTile) {
 #pragma unroll 8
         for (int e = tid; e < total; e += kFinalThreads) {
-          int lo = 0, hi = n_groups - 1;  // the last group starting at or before e
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (out[mid] <= e) lo = mid;
-            else hi = mid - 1;
-          }
-          const int i = e - out[lo];
-          if (flagged(lo)) {
-            const int t = lo * kGroupTok + i;
-            lkey[e] = score_key(src[t]);
-            lidx[e] = t;
-          } else {
-            lkey[e] = ck[(int64_t)lo * m + i];
-            lidx[e] = ci[(int64_t)lo * m + i];
-          }
+          uint32_t key;
+          int t;
+          resend_at(e, key, t);
+          lkey[e] = key;
+          lidx[e] = t;
         }
         __syncthreads();
         block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, total, k,
                    out, red, note_p, bucket);
       } else {
-        // Too many to hold: every winner has a key >= K (the candidates' k-th is a lower
-        // bound of the true k-th), so keep those, in token order, if they fit on chip.
-        const int kept = gather_at_least(score_get, n_vis, K, lkey, lidx, red, parity);
+        // Too many to hold.  Every winner ranks at or above the candidates' k-th (K, I) (the
+        // k-th of a subset is a lower bound of the true k-th), so only those elements of the
+        // resend list are kept; if even they do not fit, the whole row is filtered by K.
+        auto ranked = [K, I](uint32_t key, int t) { return key > K || (key == K && t <= I); };
+        int kept = kFinalTile + 1;
+        if (n_groups <= kMaxTopk) kept = gather_kept(resend_at, total, ranked, lkey, lidx, red, parity);
         if (kept <= kFinalTile) {
           block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
                      k, out, red, note_p, bucket);
         } else {
-          block_topk(score_get, ident, n_vis, k, out, red, note_p, bucket);
+          // no stored scores: the rest of the row is recomputed first
+          if (rs.q)
+            rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
+                           [&](int g) { return !flagged(g); }, rq8, rw);
+          auto score_at = [src](int e, uint32_t& key, int& t) {
+            key = score_key(src[e]);
+            t = e;
+          };
+          auto at_least = [K](uint32_t key, int) { return key >= K; };
+          kept = gather_kept(score_at, n_vis, at_least, lkey, lidx, red, parity);
+          if (kept <= kFinalTile) {
+            block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
+                       k, out, red, note_p, bucket);
+          } else {
+            block_topk(score_get, ident, n_vis, k, out, red, note_p, bucket);
+          }
         }
       }
     }

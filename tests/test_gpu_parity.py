@@ -213,10 +213,11 @@ def test_topk_winners_in_few_groups_are_resent_in_full():
     assert np.array_equal(idx[0].cpu().numpy(), ref)
 
 
-def test_topk_too_many_flagged_groups_falls_back_to_all_scores():
+def test_topk_resend_too_large_keeps_only_elements_ranked_above_the_candidate_kth():
     # 40 boosted tokens in each of 128 groups: the groups hold 2,048 winners between them,
-    # ~16 each, and send their best 16; all but one are flagged, and re-reading them would
-    # not fit on chip: the row is filtered by the candidates' k-th key and re-selected
+    # ~16 each, and send their best 16; all but one are flagged, and re-reading them in full
+    # would not fit on chip: only their elements ranked at or above the candidates' k-th are
+    # kept, and selected again
     L = 131072
     wl = synth.custom([L], [1], topk=2048, seed=33)
     batch = synth.make_batch(wl, DEV)
@@ -225,6 +226,23 @@ def test_topk_too_many_flagged_groups_falls_back_to_all_scores():
         sc[0, g * 256: g * 256 + 40] += 100.0
     idx, _ = run_topk(batch, sc.to(DEV), 2048)
     ref = np.sort(O.topk_indices(sc[0].numpy(), 2048))
+    assert np.array_equal(idx[0].cpu().numpy(), ref)
+
+
+def test_topk_ranked_resend_too_large_falls_back_to_the_whole_row():
+    # every fourth group holds 256 equal scores far above the rest: each sends its first 16,
+    # the candidates' k-th is the last of those, and every other boosted group is flagged
+    # with all 256 elements tied with it, so even the ranked resend (32,528) does not fit on
+    # chip: the whole row is filtered by the k-th key and selected again
+    L = 131072
+    wl = synth.custom([L], [1], topk=2048, seed=34)
+    batch = synth.make_batch(wl, DEV)
+    sc = torch.randn((1, L), generator=torch.Generator().manual_seed(5))
+    for g in range(0, 512, 4):
+        sc[0, g * 256: (g + 1) * 256] = 100.0
+    idx, _ = run_topk(batch, sc.to(DEV), 2048)
+    ref = np.sort(O.topk_indices(sc[0].numpy(), 2048))
+    assert np.array_equal(ref, np.concatenate([np.arange(g * 256, (g + 1) * 256) for g in range(0, 32, 4)]))
     assert np.array_equal(idx[0].cpu().numpy(), ref)
 
 
@@ -679,16 +697,49 @@ def test_no_stored_scores_recomputes_flagged_groups_exactly():
     assert ((idx[0] >= 5120) & (idx[0] < 6144)).sum().item() > 200
 
 
-def test_no_stored_scores_recomputes_the_whole_row_when_the_resend_is_too_large():
+def test_no_stored_scores_recomputes_only_flagged_groups_when_the_resend_is_too_large():
     # one boosted page in every fourth group: 128 groups each hold ~32 winners and send 16,
-    # so nearly all are flagged and the resend would not fit on chip: the whole row is
-    # recomputed, filtered by the candidates' k-th key and selected again
+    # so nearly all are flagged and their full resend would not fit on chip: only they are
+    # recomputed, and their elements ranked at or above the candidates' k-th are kept
     L = 131072
-    wl = synth.custom([L], [1], topk=2048, seed=65, name="rescore-all")
+    wl = synth.custom([L], [1], topk=2048, seed=65, name="rescore-ranked")
     batch = synth.make_batch(wl, DEV)
     _boost_pages(batch, 0, range(0, L // 64, 16))
     idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
+    assert 0 < n <= 128 * 256
+
+
+def _copy_token_to_pages(batch, b, t_src, pages, factor):
+    """Writes the E4M3 index key of token t_src of request b into every token of logical
+    pages `pages` of request b, with its fp32 scale multiplied by `factor`."""
+    bt = batch.block_table.cpu().numpy()
+    src = batch.key_pool[int(bt[b, t_src // 64])]
+    o = t_src % 64
+    codes = src[:8192].view(8, 64, 16)[:, o, :].clone()          # [column block][16 bytes]
+    scale = float(src[8192:].view(torch.float32)[o].item()) * factor
+    for page in pages:
+        pg = batch.key_pool[int(bt[b, page])]
+        pg[:8192].view(8, 64, 16).copy_(codes[:, None, :].expand(8, 64, 16))
+        pg[8192:].view(torch.float32).fill_(scale)
+    torch.cuda.synchronize()
+
+
+def test_no_stored_scores_recomputes_the_whole_row_when_even_the_ranked_resend_is_too_large():
+    # every token of every fourth group gets the key of the row's best token, with its scale
+    # raised: 128 groups of 256 tied scores far above the rest, so even the ranked resend does
+    # not fit on chip and the whole row is recomputed, filtered and selected again
+    L = 131072
+    wl = synth.custom([L], [1], topk=2048, seed=67, name="rescore-all")
+    batch = synth.make_batch(wl, DEV)
+    s0 = run_scores(batch)
+    t_best = int(torch.argmax(s0[0, :L]).item())
+    assert s0[0, t_best].item() > 0
+    _copy_token_to_pages(batch, 0, t_best, [p for g in range(0, 512, 4) for p in range(4 * g, 4 * g + 4)],
+                         1000.0)
+    idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
     assert n == L
+    want = np.concatenate([np.arange(g * 256, (g + 1) * 256) for g in range(0, 32, 4)])
+    assert np.array_equal(np.sort(idx[0].cpu().numpy()), want)
 
 
 @pytest.mark.parametrize("key_format", ["e4m3", "mxfp4"])
@@ -829,13 +880,13 @@ def test_no_stored_scores_mxfp4_recomputes_flagged_groups_exactly():
     assert ((idx[0] >= 5120) & (idx[0] < 6144)).sum().item() > 200
 
 
-def test_no_stored_scores_mxfp4_recomputes_the_whole_row_when_the_resend_is_too_large():
+def test_no_stored_scores_mxfp4_recomputes_only_flagged_groups_when_the_resend_is_too_large():
     L = 131072
-    wl = synth.custom([L], [1], topk=2048, seed=87, name="mx-rescore-all", key_format="mxfp4")
+    wl = synth.custom([L], [1], topk=2048, seed=87, name="mx-rescore-ranked", key_format="mxfp4")
     batch = synth.make_batch(wl, DEV)
     _boost_pages(batch, 0, range(0, L // 64, 16))
     idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
-    assert n == L
+    assert 0 < n <= 128 * 256
 
 
 def test_mxfp4_cache_with_the_e4m3_rescore_format_is_refused():
