@@ -76,7 +76,8 @@ __device__ int gather_kept(const Get& get, int n, const Keep& keep, uint32_t* lk
 
 // Recomputes into row_scores (the row's score buffer, [0, n_vis)) the scores of every
 // group g of row `row` with need(g), with the indexer's own arithmetic, so the values are
-// bitwise those the indexer would have stored.  q8 / w: LDS for the row's quantised query
+// bitwise those the indexer would have stored.  need() is called by every wave for every
+// group (keep it cheap: an LDS read).  q8 / w: LDS for the row's quantised query
 // (32 * kQRowStride bytes, 16-byte aligned) and folded head weights (32 floats, 16-byte
 // aligned).  Starts and ends with a barrier; every thread of the workgroup calls it.
 template <class Need>
@@ -96,28 +97,33 @@ __device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n
   __syncthreads();
   constexpr int kPagesPerGroup = kGroupTok / kPage;
   const int n_pages = (n_vis + kPage - 1) / kPage;
-  // each wave tests 64 groups at once (one per lane) and scores the ones that need it
+  // the pages of the needed groups are dealt to the waves in turn: every wave walks the
+  // groups 64 at a time (one per lane) and counts the pages dealt so far
+  int dealt = 0;  // wave-uniform
 #pragma unroll 1
-  for (int base = wave * 64; base < n_groups; base += kFinalWaves * 64) {
+  for (int base = 0; base < n_groups; base += 64) {
     uint64_t todo = __ballot(base + lane < n_groups && need(base + lane));
     while (todo) {
-    const int g = base + (int)__builtin_ctzll(todo);
-    todo &= todo - 1;
-    for (int p = g * kPagesPerGroup; p < min(n_pages, (g + 1) * kPagesPerGroup); ++p) {
-      const uint8_t* page = rs.key_pages + (int64_t)bt_row[p] * rs.page_stride;
-      float sc;
-      if (rs.mxfp4) {
-        KeyPageMx kp;
-        load_key_page(kp, page, lane);
-        sc = score_key_page(q8, w, kp, lane);
-      } else {
-        KeyPage kp;
-        load_key_page(kp, page, lane);
-        sc = score_key_page(q8, w, kp, lane);
+      const int g = base + (int)__builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int pg0 = g * kPagesPerGroup, pg1 = min(n_pages, pg0 + kPagesPerGroup);
+      const int first = pg0 + ((wave - dealt) % kFinalWaves + kFinalWaves) % kFinalWaves;
+      dealt += pg1 - pg0;
+      for (int p = first; p < pg1; p += kFinalWaves) {
+        const uint8_t* page = rs.key_pages + (int64_t)bt_row[p] * rs.page_stride;
+        float sc;
+        if (rs.mxfp4) {
+          KeyPageMx kp;
+          load_key_page(kp, page, lane);
+          sc = score_key_page(q8, w, kp, lane);
+        } else {
+          KeyPage kp;
+          load_key_page(kp, page, lane);
+          sc = score_key_page(q8, w, kp, lane);
+        }
+        const int t = p * kPage + lane;
+        if (t < n_vis) row_scores[t] = sc;
       }
-      const int t = p * kPage + lane;
-      if (t < n_vis) row_scores[t] = sc;
-    }
     }
   }
   __syncthreads();
@@ -230,41 +236,48 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
       // Rebuild the candidate list in token order, flagged groups in full and the others as
       // sent: group starts go to LDS (`out` is free until the next selection), then every
       // thread fills its own elements, locating each one's group by binary search.
+      // out[g] = start of group g in the resend list | kFlagBit if g is flagged; the
+      // entries past the last group hold kStartMask, so a fixed-depth search needs no bound
+      constexpr uint32_t kFlagBit = 0x80000000u, kStartMask = 0x7FFFFFFFu;
+      uint32_t* const starts = reinterpret_cast<uint32_t*>(out);
       int total = 0;
       if (n_groups <= kMaxTopk) {
         constexpr int GPT = kMaxTopk / kFinalThreads;  // groups per thread
         int len[GPT], sum = 0;
+        uint32_t fl = 0;
 #pragma unroll
         for (int q = 0; q < GPT; ++q) {
           const int g = GPT * tid + q;
-          len[q] = g >= n_groups ? 0
-                                 : (flagged(g) ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
+          const bool f = g < n_groups && flagged(g);
+          fl |= f ? 1u << q : 0u;
+          len[q] = g >= n_groups ? 0 : (f ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
           sum += len[q];
         }
         int at = block_excl_scan(sum, &total, red, parity);
 #pragma unroll
         for (int q = 0; q < GPT; ++q) {
-          const int g = GPT * tid + q;
-          if (g < n_groups) out[g] = at;  // every group has >= 1 element: starts increase
+          const int g = GPT * tid + q;  // every group has >= 1 element: starts increase
+          starts[g] = g < n_groups ? ((uint32_t)at | (((fl >> q) & 1u) ? kFlagBit : 0u)) : kStartMask;
           at += len[q];
         }
       } else {
         total = kFinalTile + 1;
       }
       __syncthreads();
+      auto flagged_lds = [starts](int g) { return (starts[g] & kFlagBit) != 0u; };
       // no stored scores: the flagged groups, which the resend reads in full, are recomputed
-      if (rs.q) rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores, flagged, rq8, rw);
-      // element e of the resend list (flagged groups in full, the others' candidates), found
-      // by a binary search over the group starts in out[]
+      if (rs.q && n_groups <= kMaxTopk)
+        rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores, flagged_lds, rq8, rw);
+      // element e of the resend list (flagged groups in full, the others' candidates): its
+      // group by a fixed-depth search over the starts
       auto resend_at = [&](int e, uint32_t& key, int& t) {
-        int lo = 0, hi = n_groups - 1;  // the last group starting at or before e
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (out[mid] <= e) lo = mid;
-          else hi = mid - 1;
-        }
-        const int i = e - out[lo];
-        if (flagged(lo)) {
+        int lo = 0;  // the last group starting at or before e
+#pragma unroll
+        for (int step = kMaxTopk / 2; step >= 1; step >>= 1)
+          lo += (int)(starts[lo + step] & kStartMask) <= e ? step : 0;
+        const uint32_t st = starts[lo];
+        const int i = e - (int)(st & kStartMask);
+        if (st & kFlagBit) {
           t = lo * kGroupTok + i;
           key = score_key(src[t]);
         } else {
@@ -296,9 +309,14 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
                      k, out, red, note_p, bucket);
         } else {
           // no stored scores: the rest of the row is recomputed first
-          if (rs.q)
-            rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
-                           [&](int g) { return !flagged(g); }, rq8, rw);
+          if (rs.q) {
+            if (n_groups <= kMaxTopk)
+              rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
+                             [&](int g) { return !flagged_lds(g); }, rq8, rw);
+            else
+              rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
+                             [](int) { return true; }, rq8, rw);
+          }
           auto score_at = [src](int e, uint32_t& key, int& t) {
             key = score_key(src[e]);
             t = e;

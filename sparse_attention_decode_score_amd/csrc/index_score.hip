@@ -314,6 +314,9 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
   if (max_q_per_seq <= 1) R = 1;
   else if (max_q_per_seq <= 2) R = 2;
   else if (max_q_per_seq <= 4) R = 4;
+#ifdef DSA_INDEX_MAX_ROWS  // build-time override for tuning sweeps: rows per workgroup at most
+  R = std::min(R, DSA_INDEX_MAX_ROWS);
+#endif
   const unsigned gz = (unsigned)((max_q_per_seq + R - 1) / R);
   // groups per wave: the longest segments (up to the staging limit of R) that still give
   // >= 1,024 workgroups (4 per CU)
