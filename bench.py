@@ -65,6 +65,21 @@ def index_score_bytes(seq_lens, key_format="e4m3"):
     return sum(L * idx_bytes_per_token(key_format) for L in seq_lens)
 
 
+FP8_MFMA_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix peak (no sparsity), vendor figure
+IDX_FLOP_PER_ROW_TOKEN = 32 * 128 * 2      # indexer q.k over 32 heads x 128 dims
+MLA_FLOP_PER_ROW_TOKEN = 96 * (576 + 512) * 2  # logits over 576 dims + values over 512, 96 heads
+
+
+def index_score_flops(wl):
+    """Algorithmic FLOPs of one dsa_index_score launch: 8,192 per (row, visible token)."""
+    return sum((pos + 1) * IDX_FLOP_PER_ROW_TOKEN for _, pos in wl.row_positions())
+
+
+def sparse_mla_flops(wl):
+    """Algorithmic FLOPs of the sparse MLA: 208,896 per (row, selected token)."""
+    return sum(min(wl.topk, pos + 1) * MLA_FLOP_PER_ROW_TOKEN for _, pos in wl.row_positions())
+
+
 def dense_mla_bytes(seq_lens, q_per_seq):
     """Bytes a dense-MLA decode reads for the same batch: every context token's latent."""
     return sum(L * LAT_BYTES_PER_TOKEN for L in seq_lens)
@@ -340,6 +355,11 @@ def main():
     value = ab["total"] / (mean_us * 1e-6) / 1e9
     idx_bytes = index_score_bytes(wl.seq_lens, wl.key_format)
     idx_gbps = idx_bytes / (stage_mean[0] * 1e-6) / 1e9
+    idx_flops = index_score_flops(wl)
+    idx_tflops = idx_flops / (stage_mean[0] * 1e-6) / 1e12
+    # the indexer is MFMA-bound when its FLOP per byte exceeds the FP8 ridge (peak FLOP/s over
+    # peak B/s = 625): many query rows per request, as in a prefill append
+    mfma_bound = idx_flops / idx_bytes > FP8_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     traffic = _traffic_from_profile() if wl.name == "long" else None  # counted on `long`
     ceiling = stream_read_ceiling(torch)
     if args.copy_calibration:
@@ -393,10 +413,17 @@ def main():
                       "sparse_mla_and_merge": round(stage_mean[2], 2)}),
         "algorithmic_bytes": ab,
         "dsa_vs_dense_mla_bytes": round(ab["total"] / dense_mla_bytes(wl.seq_lens, wl.q_per_seq), 4),
-        "roofline": {"kernel": "dsa_index_score", "bound": "hbm", "achieved": round(idx_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": idx_bytes,
-                     "avg_launch_us": round(stage_mean[0], 2)},
+        "roofline": ({"kernel": "dsa_index_score", "bound": "mfma", "achieved": round(idx_tflops, 1),
+                      "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(idx_tflops / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                      "algorithmic_flops_per_launch": idx_flops,
+                      "avg_launch_us": round(stage_mean[0], 2)} if mfma_bound else
+                     {"kernel": "dsa_index_score", "bound": "hbm", "achieved": round(idx_gbps, 1),
+                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(idx_gbps / HBM_PEAK_GBPS, 4),
+                      "traffic": traffic, "algorithmic_bytes_per_launch": idx_bytes,
+                      "avg_launch_us": round(stage_mean[0], 2)}),
+        "algorithmic_tflop": {"index_score": round(idx_flops / 1e12, 4),
+                              "sparse_mla": round(sparse_mla_flops(wl) / 1e12, 4)},
         "stream_read_ceiling_GBps": round(ceiling, 1),
         "wall_s_timed_loop": round(t_wall, 4),
         "cpu_baseline": cpu,

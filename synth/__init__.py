@@ -96,7 +96,7 @@ def workload(name: str) -> Workload:
     if name == "tiny":
         return Workload("tiny", (4096,), (1,), 2048, 8, seed=0)
     if name == "spec":
-        return Workload("spec", _spec_lens(1), (5,) * 32, 2048, 4, seed=1)
+        return Workload("spec", _spec_lens(1), (5,) * 32, 2048, 1, seed=1)
     if name == "long":
         return Workload("long", (131072,) * 32, (1,) * 32, 2048, 8, seed=2)
     if name == "million":
