@@ -153,6 +153,11 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const int t = p * kPage + lane;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      // a group of eight rows holding fewer (five verification rows, say) skips the rest
+      if (R > 4 && r >= nr) {  // uniform
+        keys[r][jj] = kSentinel;
+        continue;
+      }
       const float score = score_key_page(&q8s[r][0][0], &wps[r][0], cur, lane);
       if constexpr (STAGE) {
         if (valid && scores) sbuf[r][(p - p0) * kPage + lane] = score;
