@@ -348,6 +348,8 @@ def main():
             stage[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
     step_us_sorted = sorted(step_us)
     med = step_us_sorted[len(step_us_sorted) // 2]
+    p10 = step_us_sorted[int(0.1 * (len(step_us_sorted) - 1))]
+    p90 = step_us_sorted[int(round(0.9 * (len(step_us_sorted) - 1)))]
     mean_us = sum(step_us) / len(step_us)
     stage_mean = [sum(s) / len(s) for s in stage]
 
@@ -405,6 +407,7 @@ def main():
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),
         "us_per_layer_median": round(med, 2),
+        "us_per_layer_p10_p90": [round(p10, 2), round(p90, 2)],
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "stage_us": ({"index_score": round(stage_mean[0], 2),
                       "topk_final_in_sparse_mla_and_merge": round(stage_mean[2], 2)}
