@@ -94,7 +94,7 @@ def _spec_lens(seed: int):
 def workload(name: str) -> Workload:
     """The five named workloads.  Master seed = position in the list below."""
     if name == "tiny":
-        return Workload("tiny", (4096,), (1,), 2048, 8, seed=0)
+        return Workload("tiny", (4096,), (1,), 2048, 16, seed=0)
     if name == "spec":
         return Workload("spec", _spec_lens(1), (5,) * 32, 2048, 1, seed=1)
     if name == "long":
