@@ -100,7 +100,7 @@ def workload(name: str) -> Workload:
     if name == "long":
         return Workload("long", (131072,) * 32, (1,) * 32, 2048, 8, seed=2)
     if name == "million":
-        return Workload("million", (1048576,), (5,), 2048, 32, seed=3)
+        return Workload("million", (1048576,), (5,), 2048, 16, seed=3)
     if name == "prefill":
         return Workload("prefill", (152048,), (2048,), 2048, 1, seed=4)
     if name.endswith("-mxfp4") and name[:-6] in WORKLOADS:
