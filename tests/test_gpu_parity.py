@@ -742,6 +742,24 @@ def test_no_stored_scores_recomputes_the_whole_row_when_even_the_ranked_resend_i
     assert np.array_equal(np.sort(idx[0].cpu().numpy()), want)
 
 
+def test_resend_beyond_4096_groups_rereads_the_whole_row():
+    # 1,049,000 tokens = 4,098 groups of 256, more group starts than the final pass holds in
+    # LDS: a flagged group (one boosted page holds the positive-scoring of its tokens among
+    # the winners, the group sends 4) makes it recompute and re-read the whole row; the selection is bitwise the stored-scores path's
+    # and the exact top-k of those scores
+    L = 1049000
+    wl = synth.custom([L], [1], topk=2048, seed=68, name="resend-4098-groups")
+    batch = synth.make_batch(wl, DEV)
+    _boost_pages(batch, 0, [9000])
+    idx, n = _check_no_scores_matches(batch, 2048, expect_rescored=True)
+    assert n == L
+    s_ref, _ = _index(batch, 2048, True)
+    ref = np.sort(O.topk_indices(s_ref[0, :L].cpu().numpy(), 2048))
+    assert np.array_equal(idx[0].cpu().numpy(), ref)
+    # more winners from the boosted page than its group's 4 candidates: the resend counted
+    assert ((idx[0] >= 9000 * 64) & (idx[0] < 9001 * 64)).sum().item() > 4
+
+
 @pytest.mark.parametrize("key_format", ["e4m3", "mxfp4"])
 @pytest.mark.parametrize("num_splits", [1, 4])
 def test_select_in_attention_with_no_stored_scores(num_splits, key_format):
