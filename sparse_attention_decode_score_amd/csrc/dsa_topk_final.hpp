@@ -235,7 +235,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
     if (block_sum(any, red, parity) > 0) {
       // Rebuild the candidate list in token order, flagged groups in full and the others as
       // sent: group starts go to LDS (`out` is free until the next selection), then every
-      // thread fills its own elements, locating each one's group by binary search.
+      // thread fills its own elements, locating each one's group by a fixed-depth search.
       // out[g] = start of group g in the resend list | kFlagBit if g is flagged; the
       // entries past the last group hold kStartMask, so a fixed-depth search needs no bound
       constexpr uint32_t kFlagBit = 0x80000000u, kStartMask = 0x7FFFFFFFu;
