@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       v4i a1 = *reinterpret_cast<const v4i*>(arow + 16);
       v4i b0 = *reinterpret_cast<const v4i*>(qrow);
       v4i b1 = *reinterpret_cast<const v4i*>(qrow + 16);
-#pragma unroll 1
+#pragma unroll
       for (int kb = 0; kb < 9; ++kb) {
         const v8i A = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         const v8i B = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
