@@ -37,12 +37,14 @@ constexpr int kGroupPages = kGroupTok / kPage;  // 4
 
 // Pages each wave keeps in flight: four for one or two rows, two for larger row groups
 // (register budget).  Groups per wave at most: the staged scores of a workgroup are
-// 16 KB of LDS for up to four rows; eight rows store directly.
+// 16 KB of LDS for up to four rows; eight rows store directly and take up to four groups,
+// which the grid rule below gives them only when there are many row groups (a prefill),
+// where long segments amortise the eight rows' query set-up.
 template <int R>
 struct IdxCfg {
   static constexpr int kInFlight = R <= 2 ? 4 : 2;
   static constexpr bool kStage = R <= 4;
-  static constexpr int kMaxGroups = R == 1 ? 4 : (R == 2 ? 2 : 1);
+  static constexpr int kMaxGroups = (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1);
   static constexpr int kSegTok = kWaves * kGroupTok * kMaxGroups;  // tokens per workgroup
   static constexpr int kCandSlots = kWaves * kMaxGroups * kGroupTok;  // worst case (m = 256)
 };
@@ -325,13 +327,13 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
   const unsigned gz = (unsigned)((max_q_per_seq + R - 1) / R);
   // groups per wave: the longest segments (up to the staging limit of R) that still give
   // >= 1,024 workgroups (4 per CU)
-  int G = R == 1 ? 4 : (R == 2 ? 2 : 1);
+  int G = (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1);
   while (G > 1 && (int64_t)num_seqs * gz *
                           ((max_pages + kWaves * kGroupPages * G - 1) / (kWaves * kGroupPages * G)) <
                       1024)
     G >>= 1;
 #ifdef DSA_INDEX_GROUPS_PER_WAVE  // build-time override for tuning sweeps (at most the limit)
-  G = std::min(DSA_INDEX_GROUPS_PER_WAVE, R == 1 ? 4 : (R == 2 ? 2 : 1));
+  G = std::min(DSA_INDEX_GROUPS_PER_WAVE, (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1));
 #endif
   const unsigned gx = (unsigned)((max_pages + kWaves * kGroupPages * G - 1) / (kWaves * kGroupPages * G));
   const dim3 grid(gx, (unsigned)num_seqs, gz), block(256);
