@@ -289,7 +289,7 @@ def _mla_small_case(num_splits):
     return wl, batch, slots
 
 
-@pytest.mark.parametrize("num_splits", [1, 3, 16])
+@pytest.mark.parametrize("num_splits", [1, 3, 16, 40, 64])
 def test_sparse_mla_small(num_splits):
     say("mla", num_splits)
     wl, batch, slots = _mla_small_case(num_splits)
@@ -307,7 +307,7 @@ def test_sparse_mla_small(num_splits):
                                 f"row {row} split {s_}")
 
 
-@pytest.mark.parametrize("num_splits", [1, 3, 16])
+@pytest.mark.parametrize("num_splits", [1, 3, 16, 40, 64])
 @pytest.mark.parametrize("prepared", [False, True], ids=["bf16-query", "prepared-query"])
 def test_sparse_mla_merged_in_call(num_splits, prepared):
     # fp16 split partials merged inside the call, against the oracle; and the prepared
