@@ -124,7 +124,7 @@ __device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, i
     if (lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
     return;
   }
-  // K = the m-th largest key: the largest T with #{keys >= T} >= m, one bit at a time.  The
+  // K = the m-th largest key: the largest T with #{keys >= T} >= m, two bits at a time.  The
   // visible keys (>= 1) share the bits of their maximum and minimum above the highest bit
   // where those differ, so the search starts below it with the bracket [K, K_hi) around
   // every key; it ends early when one key is left in the bracket (that key is the m-th).
@@ -165,18 +165,53 @@ __device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, i
       K = x;
       break;
     }
-    const uint32_t T = K | (1u << bit);
-    int c = 0;
+    if (bit == 0) {  // the last bit alone
+      const uint32_t T = K | 1u;
+      int c = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c += __popcll(__ballot(kv[j] >= T));
-    if (c >= m) {
-      K = T;
-      c_K = c;
-    } else {
-      K_hi = T;
-      has_hi = true;
-      c_hi = c;
+      for (int j = 0; j < 4; ++j) c += __popcll(__ballot(kv[j] >= T));
+      if (c >= m) {
+        K = T;
+        c_K = c;
+      } else {
+        K_hi = T;
+        has_hi = true;
+        c_hi = c;
+      }
+      break;
     }
+    // two bits per step: the counts against the three thresholds of the next two bits are
+    // independent (their ballots overlap); they fall as the threshold rises
+    const int sh = bit - 1;
+    const uint32_t T1 = K | (1u << sh), T2 = K | (2u << sh), T3 = K | (3u << sh);
+    int c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c1 += __popcll(__ballot(kv[j] >= T1));
+      c2 += __popcll(__ballot(kv[j] >= T2));
+      c3 += __popcll(__ballot(kv[j] >= T3));
+    }
+    if (c3 >= m) {
+      K = T3;
+      c_K = c3;
+    } else if (c2 >= m) {
+      K = T2;
+      c_K = c2;
+      K_hi = T3;
+      has_hi = true;
+      c_hi = c3;
+    } else if (c1 >= m) {
+      K = T1;
+      c_K = c1;
+      K_hi = T2;
+      has_hi = true;
+      c_hi = c2;
+    } else {
+      K_hi = T1;
+      has_hi = true;
+      c_hi = c1;
+    }
+    --bit;  // with the loop's decrement: two bits settled
   }
   int gt = 0;
 #pragma unroll
