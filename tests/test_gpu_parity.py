@@ -405,6 +405,17 @@ def test_end_to_end_tiny():
     _end_to_end(synth.workload("tiny"), rows=[0])
 
 
+@pytest.mark.parametrize("num_splits", [1, 8])
+def test_end_to_end_degenerate_contexts(num_splits):
+    # a request of one token (its row sees only token 0), rows at positions 0 and 1 of a
+    # two-token request, a partial first page, exactly one page, one page and one token,
+    # and a context just above k: the whole default step (fused first pass, no stored
+    # scores, final pass inside the attention), splits with no selected token included
+    wl = synth.custom([1, 2, 63, 64, 65, 2049], [1, 2, 1, 1, 1, 1], topk=2048,
+                      num_splits=num_splits, seed=71, name="degenerate")
+    _end_to_end(wl, rows=list(range(wl.n_q)))
+
+
 def test_end_to_end_spec_full_size():
     wl = synth.workload("spec")
     _end_to_end(wl, rows=[0, 4, 77, 159])
