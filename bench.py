@@ -150,6 +150,7 @@ def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
     wl = batch.wl
     rowpos = wl.row_positions()
     done, t_total, byts = 0, 0.0, 0
+    stage_s = [0.0, 0.0, 0.0, 0.0]  # indexer, top-k, sparse MLA, LSE combine
     rows = list(rows)
     host = {}  # each sampled row's inputs, copied to the host once (outside the timing)
     for i in range(len(rows) * max_passes):
@@ -171,12 +172,20 @@ def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
         else:
             kc, ks = O.read_index_keys(key_pages, bt_local, L)
             scores = O.index_scores(qi, w, kc[: pos + 1], ks[: pos + 1])
+        t1 = time.perf_counter()
         sel = O.topk_indices(scores, wl.topk)
+        t2 = time.perf_counter()
         lat = O.read_latents(lat_pages, O.physical_slot(bt_local, sel))
         parts = [O.mla_attend(qm, lat[a:e], batch.latent_scale, batch.softmax_scale)
                  for a, e in O.split_ranges(len(sel), wl.num_splits)]
+        t3 = time.perf_counter()
         O.lse_combine(parts)
-        t_total += time.perf_counter() - t0
+        t4 = time.perf_counter()
+        stage_s[0] += t1 - t0
+        stage_s[1] += t2 - t1
+        stage_s[2] += t3 - t2
+        stage_s[3] += t4 - t3
+        t_total += t4 - t0
         # the row's share of the algorithmic bytes: its request's keys divided over the
         # request's rows, its selected latents, its query / output
         nq = wl.q_per_seq[b]
@@ -188,6 +197,8 @@ def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
+            "stage_s": {"index_score": round(stage_s[0], 3), "topk": round(stage_s[1], 3),
+                        "sparse_mla": round(stage_s[2], 3), "lse_combine": round(stage_s[3], 3)},
             "sample": f"{done} query-row passes over the {len(rows)} rows of the {wl.name} "
                       f"workload taken in turn, whole path per row, {t_total:.1f} s of CPU "
                       f"time; GB/s = those rows' share of the algorithmic bytes / time"}
