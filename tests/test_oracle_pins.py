@@ -109,6 +109,75 @@ def test_quantize_heads_error_bound_and_exact_cases():
     assert (sz == 1.0).all() and (O.e4m3_decode(z) == 0).all()
 
 
+def _query_by_definition(q):
+    """The dequantised query q_hat = E4M3(q / sq) * sq written from the definition, without
+    the oracle: sq = the smallest 2^e with max|q_h| <= 448 * 2^e (found by stepping e over
+    exact powers of two, 1 for an all-zero head), codes by torch's float8_e4m3fn conversion
+    of q / sq (exact in fp32 for bf16 inputs), decoded by torch."""
+    q = np.asarray(q, np.float64)
+    out = np.empty_like(q)
+    for h in range(q.shape[0]):
+        a = float(np.max(np.abs(q[h])))
+        sq = 1.0
+        if a > 0.0:
+            e = -160
+            while a > 448.0 * math.ldexp(1.0, e):
+                e += 1
+            sq = math.ldexp(1.0, e)
+        codes = torch.from_numpy((q[h] / sq).astype(np.float32)).to(torch.float8_e4m3fn)
+        out[h] = codes.to(torch.float64).numpy() * sq
+    return out
+
+
+def _bf16_heads(rng, heads, dim):
+    """bf16 query heads whose magnitudes span many powers of two (one head all zero)."""
+    q = rng.normal(size=(heads, dim)) * np.exp2(rng.integers(-30, 30, size=(heads, 1)))
+    q[heads // 2] = 0.0
+    return torch.from_numpy(q.astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def test_dequantized_query_matches_definition():
+    # Query quantisation of the fused indexer front ("Fused low-latency decode for DSA
+    # layers"): every value of the oracle's q_hat equals the definition, bit for bit.
+    rng = np.random.default_rng(21)
+    for heads, dim in ((32, 128), (96, 576)):
+        q = _bf16_heads(rng, heads, dim)
+        assert np.array_equal(O.dequantized_query(q), _query_by_definition(q))
+    # a head that is already on the E4M3 grid times a power of two comes back unchanged
+    g = O.E4M3_TABLE[rng.integers(0, 0x7F, size=(1, 128))] * 2.0 ** 7
+    g[0, 5] = 448.0 * 2.0 ** 7
+    assert np.array_equal(O.dequantized_query(g), g)
+
+
+def test_index_scores_with_quantised_query_brute_force():
+    # score_t = sum_h w_h ReLU(q_hat_h . k_t s_t) with q_hat from the definition above
+    rng = np.random.default_rng(22)
+    q = _bf16_heads(rng, 32, 128)
+    _, w, codes, sc = _rand_idx_inputs(23, 24)
+    got = O.index_scores(q, w, codes, sc).astype(np.float64)
+    ref = _brute_scores(_query_by_definition(q).tolist(), w, codes, sc)
+    np.testing.assert_allclose(got, ref, rtol=2e-7, atol=1e-30)
+
+
+def test_mla_attend_with_quantised_query_matches_torch_softmax_attention():
+    rng = np.random.default_rng(24)
+    q = torch.from_numpy(rng.normal(size=(96, 576)).astype(np.float32) * 3.0).to(torch.bfloat16)
+    q = q.double().numpy()
+    x = rng.normal(size=(60, 576)).astype(np.float32)
+    c = np.float32(np.abs(x).max() / 448)
+    codes = _torch_e4m3(x / c)
+    sm = float(np.float32(1 / math.sqrt(576)))
+    o, lse = O.mla_attend(q, codes, float(c), sm)
+    kv = torch.from_numpy(codes).view(torch.float8_e4m3fn).double() * float(c)
+    logits = (torch.from_numpy(_query_by_definition(q)) @ kv.T) * sm
+    np.testing.assert_allclose(o, (torch.softmax(logits, -1) @ kv[:, :512]).numpy(), rtol=1e-12,
+                               atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).numpy(), rtol=1e-12, atol=1e-12)
+    # and the dense-MLA routine on the same query
+    o_d, l_d = O.dense_mla(q, codes, float(c), sm)
+    np.testing.assert_allclose(o_d, o, rtol=1e-11, atol=1e-14)
+
+
 # -------------------------------------------------------------------------- paging
 @pytest.fixture(scope="module")
 def small_batch():
