@@ -3,7 +3,7 @@ sparse MLA over the selected latents -> LSE combine of the split partials, for e
 row of one synthetic batch (the four library calls on one stream).
 
 Default workload: decode of 32 requests x 1 query row at 131,072 tokens of context each
-(FP8 index keys 132 B/token, FP8 latents 576 B/token, top-2048, 16 splits).  Prints ONE
+(FP8 index keys 132 B/token, FP8 latents 576 B/token, top-2048, 8 attention splits).  Prints ONE
 JSON line.  `value` is the whole step's algorithmic HBM traffic divided by its time (GB/s);
 the JSON also carries us/layer, the indexer kernel's roofline, and the CPU oracle timed on
 a bounded sample of the same workload.

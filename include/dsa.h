@@ -290,6 +290,31 @@ dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key
 dsa_status dsa_quantize_q(int32_t rows, int32_t heads, int32_t dim, const void* q_bf16,
                           uint8_t* codes, float* scales, void* stream);
 
+/*
+ * Host-side checks of the device-array CONTENTS the calls above trust without checking (the
+ * block tables and slots that the serving stack translates to page addresses before each step,
+ * "Packed KV cache for three kinds of state").  They run on the CPU over HOST copies of those
+ * arrays (every pointer here is a host pointer), touch no GPU and launch nothing; a caller
+ * runs them when debugging a batch, before the device calls.  DSA_OK, or DSA_ERR_INVALID_ARG
+ * with the first violation in dsa_last_error().
+ *
+ * dsa_validate_batch: the batch description of stages 1-2 and the block table:
+ *   cu_q[0] == 0, every request has 1..max_q_per_seq rows, cu_q[num_seqs] == n_q;
+ *   1 <= seq_lens[b] <= max_seq_len and at least the request's row count;
+ *   bt_stride >= ceil(max_seq_len / 64), and block_table[b][j] in 0..num_pages-1 for every
+ *   page j holding a token of request b.
+ *   topk_slot [n_q][k] (may be NULL: not checked): every entry is -1 or the slot of a token
+ *   the row sees (page block_table[b][j], offset o, 64 j + o <= the row's position), and the
+ *   valid entries of a row are distinct.
+ * dsa_validate_slots: the slots of dsa_cache_append: each -1 or page * 64 + offset with
+ *   page < num_pages, and no valid slot twice.
+ */
+dsa_status dsa_validate_batch(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                              int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
+                              const int32_t* block_table, int32_t bt_stride, int64_t num_pages,
+                              const int32_t* topk_slot, int32_t k);
+dsa_status dsa_validate_slots(int32_t n_tok, const int32_t* slots, int64_t num_pages);
+
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* dsa_last_error(void);
 

@@ -63,10 +63,13 @@ def lib() -> ctypes.CDLL:
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_cache_append.argtypes = [_I32, _P, _P, _P, _F32, _P, _I64, _P, _I64, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
+        L.dsa_validate_batch.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32]
+        L.dsa_validate_slots.argtypes = [_I32, _P, _I64]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
         for f in ("dsa_index_score", "dsa_index_score_mxfp4", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
-                  "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append"):
+                  "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append", "dsa_validate_batch",
+                  "dsa_validate_slots"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -98,6 +101,39 @@ def _expect(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _host_i32(a, name):
+    """A contiguous host int32 array (numpy or CPU tensor) and its address."""
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError(f"{name}: the validators take host copies (call .cpu() first)")
+        a = a.numpy()
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+def dsa_validate_batch(cu_q, seq_lens, block_table, num_pages: int, *, max_seq_len: int,
+                       max_q_per_seq: int, topk_slot=None) -> None:
+    """Checks host copies of a batch description, its block table and (optionally) selected
+    slots [n_q, k] on the CPU; raises DsaError naming the first violation."""
+    cu, cu_p = _host_i32(cu_q, "cu_q")
+    sl, sl_p = _host_i32(seq_lens, "seq_lens")
+    bt, bt_p = _host_i32(block_table, "block_table")
+    ts, ts_p, k = None, None, 0
+    if topk_slot is not None:
+        ts, ts_p = _host_i32(topk_slot, "topk_slot")
+        k = ts.shape[1]
+    _check(lib().dsa_validate_batch(sl.shape[0], int(cu[-1]) if cu.size else 0, int(max_seq_len),
+                                    int(max_q_per_seq), cu_p, sl_p, bt_p, bt.shape[1],
+                                    int(num_pages), ts_p, int(k)))
+
+
+def dsa_validate_slots(slots, num_pages: int) -> None:
+    """Checks host copies of dsa_cache_append slots on the CPU; raises DsaError."""
+    s, s_p = _host_i32(slots, "slots")
+    _check(lib().dsa_validate_slots(s.shape[0], s_p, int(num_pages)))
 
 
 def dsa_version() -> str:

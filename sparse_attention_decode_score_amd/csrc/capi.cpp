@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <unordered_map>
+#include <unordered_set>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.hpp"
@@ -369,6 +371,83 @@ dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key
                                            key_page_stride, static_cast<uint8_t*>(latent_pages),
                                            latent_page_stride, static_cast<hipStream_t>(stream)),
                   "dsa_cache_append");
+}
+
+dsa_status dsa_validate_batch(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                              int32_t max_q_per_seq, const int32_t* cu_q, const int32_t* seq_lens,
+                              const int32_t* block_table, int32_t bt_stride, int64_t num_pages,
+                              const int32_t* topk_slot, int32_t k) {
+  dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
+  if (st != DSA_OK) return st;
+  DSA_REQUIRE(max_q_per_seq >= 1, "max_q_per_seq must be >= 1 (got %d)", max_q_per_seq);
+  DSA_REQUIRE(block_table, "block_table must be non-null");
+  DSA_REQUIRE(num_pages >= 1, "num_pages must be >= 1 (got %lld)", (long long)num_pages);
+  const int64_t max_pages = ((int64_t)max_seq_len + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE;
+  DSA_REQUIRE(bt_stride >= max_pages, "bt_stride (%d) must be >= ceil(max_seq_len / 64) = %lld",
+              bt_stride, (long long)max_pages);
+  DSA_REQUIRE(cu_q[0] == 0, "cu_q[0] must be 0 (got %d)", cu_q[0]);
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t nb = cu_q[b + 1] - cu_q[b];
+    DSA_REQUIRE(nb >= 1 && nb <= max_q_per_seq,
+                "request %d has %d query rows (cu_q must increase, by 1..max_q_per_seq = %d)", b,
+                nb, max_q_per_seq);
+    const int32_t L = seq_lens[b];
+    DSA_REQUIRE(L >= 1 && L <= max_seq_len, "seq_lens[%d] = %d is outside 1..max_seq_len (%d)", b,
+                L, max_seq_len);
+    DSA_REQUIRE(nb <= L, "request %d has %d rows but only %d tokens (its rows are its last tokens)",
+                b, nb, L);
+    const int32_t* bt = block_table + (int64_t)b * bt_stride;
+    for (int32_t j = 0; j < (L + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE; ++j)
+      DSA_REQUIRE(bt[j] >= 0 && bt[j] < num_pages,
+                  "block_table[%d][%d] = %d is not a page of the pool (0..%lld)", b, j, bt[j],
+                  (long long)num_pages - 1);
+  }
+  DSA_REQUIRE(cu_q[num_seqs] == n_q, "cu_q[num_seqs] = %d must equal n_q = %d", cu_q[num_seqs], n_q);
+  if (!topk_slot) return ok();
+  DSA_REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, "k must be in 1..4096 (got %d)", k);
+  // every slot of row i must hold a token the row sees: page BT[b][j] and offset o with
+  // 64 j + o <= position; valid slots of a row are distinct
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t* bt = block_table + (int64_t)b * bt_stride;
+    const int32_t nb = cu_q[b + 1] - cu_q[b];
+    std::unordered_map<int32_t, int32_t> first_page;  // physical page -> lowest logical page
+    for (int32_t j = (seq_lens[b] + DSA_PAGE_SIZE - 1) / DSA_PAGE_SIZE - 1; j >= 0; --j)
+      first_page[bt[j]] = j;
+    for (int32_t r = 0; r < nb; ++r) {
+      const int32_t row = cu_q[b] + r;
+      const int64_t pos = (int64_t)seq_lens[b] - nb + r;
+      const int32_t* sl = topk_slot + (int64_t)row * k;
+      std::unordered_set<int32_t> seen;
+      for (int32_t i = 0; i < k; ++i) {
+        const int32_t s = sl[i];
+        if (s == -1) continue;
+        DSA_REQUIRE(s >= 0, "topk_slot[%d][%d] = %d is neither -1 nor a slot", row, i, s);
+        const auto it = first_page.find(s / DSA_PAGE_SIZE);
+        DSA_REQUIRE(it != first_page.end() &&
+                        (int64_t)it->second * DSA_PAGE_SIZE + s % DSA_PAGE_SIZE <= pos,
+                    "topk_slot[%d][%d] = %d is not a token row %d sees (position %lld)", row, i, s,
+                    row, (long long)pos);
+        DSA_REQUIRE(seen.insert(s).second, "topk_slot[%d] holds slot %d twice", row, s);
+      }
+    }
+  }
+  return ok();
+}
+
+dsa_status dsa_validate_slots(int32_t n_tok, const int32_t* slots, int64_t num_pages) {
+  DSA_REQUIRE(n_tok >= 0, "n_tok must be >= 0 (got %d)", n_tok);
+  DSA_REQUIRE(n_tok == 0 || slots, "slots must be non-null");
+  DSA_REQUIRE(num_pages >= 1, "num_pages must be >= 1 (got %lld)", (long long)num_pages);
+  std::unordered_set<int32_t> seen;
+  for (int32_t i = 0; i < n_tok; ++i) {
+    const int32_t s = slots[i];
+    if (s == -1) continue;
+    DSA_REQUIRE(s >= 0 && s / DSA_PAGE_SIZE < num_pages,
+                "slots[%d] = %d is neither -1 nor a slot of the pool (%lld pages)", i, s,
+                (long long)num_pages);
+    DSA_REQUIRE(seen.insert(s).second, "slot %d appears twice (entry %d)", s, i);
+  }
+  return ok();
 }
 
 dsa_status dsa_lse_combine(int32_t num_splits, int32_t n_q, const float* o_part,

@@ -1,6 +1,6 @@
 // Exact selection primitives of the top-k stage: order-preserving keys, the per-group
 // candidate rule, one wave's top-m of a 256-token group (ballots only, keys in registers)
-// and one 1,024-thread workgroup's top-k of up to 16,384 keys (bitwise threshold search).
+// and one 512-thread workgroup's top-k of up to 16,384 keys (bitwise threshold search).
 //
 // Total order everywhere: larger key first, equal keys by lower element index (token order).
 #pragma once

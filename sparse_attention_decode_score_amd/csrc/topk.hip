@@ -11,7 +11,7 @@
 //          group_cand_count) in token order, plus the group's m-th element.  The fused
 //          indexer runs this pass while the scores are still in registers; the kernel below
 //          runs it from stored scores.
-//  pass 2  one 1,024-thread workgroup per row selects the top k of the candidates.  A group
+//  pass 2  one 512-thread workgroup per row selects the top k of the candidates.  A group
 //          that had more than m visible tokens can hide winners exactly when its m-th
 //          element beats the selection's k-th; those groups (only) are re-read in full from
 //          the scores and the row is selected again, which is exact (every unsent token of

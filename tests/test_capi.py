@@ -216,3 +216,70 @@ def test_index_score_mxfp4_rejects_bad_host_args(L):
             args[i] = v
         assert f(*args) == 1, (patch, _err())
         assert word in _err(), (patch, _err())
+
+
+# ------------------------------------------------------------------ host-side validators
+def _valid_batch():
+    import numpy as np
+    import synth
+    import oracle as O
+    wl = synth.custom([300, 130, 64], [1, 3, 2], topk=64, seed=7)
+    b = synth.make_batch(wl, "cpu")
+    bt = b.block_table.numpy()
+    slots = np.full((wl.n_q, 64), -1, dtype=np.int32)
+    for row, (r, pos) in enumerate(wl.row_positions()):
+        sel = np.sort(np.random.default_rng(row).permutation(pos + 1)[:64])
+        slots[row, :len(sel)] = O.physical_slot(bt[r], sel)
+    return wl, b, slots
+
+
+def test_validate_batch_accepts_a_valid_batch_and_names_each_violation(L):
+    import numpy as np
+    wl, b, slots = _valid_batch()
+    cu, sl, bt = b.cu_q.numpy(), b.seq_lens.numpy(), b.block_table.numpy()
+    kw = dict(max_seq_len=wl.max_seq_len, max_q_per_seq=3)
+    dsa.dsa_validate_batch(cu, sl, bt, b.num_pages, topk_slot=slots, **kw)
+    dsa.dsa_validate_batch(cu, sl, bt, b.num_pages, **kw)
+
+    def bad(word, **over):
+        args = dict(cu_q=cu, seq_lens=sl, block_table=bt, num_pages=b.num_pages, topk_slot=slots)
+        args.update(over)
+        with pytest.raises(dsa.DsaError) as e:
+            dsa.dsa_validate_batch(args["cu_q"], args["seq_lens"], args["block_table"],
+                                   args["num_pages"], topk_slot=args["topk_slot"], **kw)
+        assert e.value.status == 1 and word in str(e.value), str(e.value)
+
+    c2 = cu.copy(); c2[2] = c2[1]
+    bad("query rows", cu_q=c2)                       # a request with no row
+    s2 = sl.copy(); s2[1] = wl.max_seq_len + 1
+    bad("seq_lens[1]", seq_lens=s2)
+    s3 = sl.copy(); s3[2] = 1
+    bad("only 1 tokens", seq_lens=s3)                # 2 rows on 1 token
+    bt2 = bt.copy(); bt2[0, 4] = b.num_pages
+    bad("block_table[0][4]", block_table=bt2)
+    bt3 = bt.copy(); bt3[1, 1] = -1
+    bad("block_table[1][1]", block_table=bt3)
+    t2 = slots.copy(); t2[0, 5] = t2[0, 6]
+    bad("twice", topk_slot=t2)
+    t3 = slots.copy(); t3[0, 0] = -7
+    bad("neither -1", topk_slot=t3)
+    # a slot of the request's own pages but past the row's position (row 1 sits at 127;
+    # token 129 is offset 1 of its third page)
+    t4 = slots.copy(); t4[1, 0] = int(bt[1][2]) * 64 + 1
+    bad("not a token row 1 sees", topk_slot=t4)
+    # a slot of another request's page
+    t5 = slots.copy(); t5[4, 0] = int(bt[0][0]) * 64
+    bad("not a token row 4 sees", topk_slot=t5)
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_validate_batch(cu, sl, bt[:, :2], b.num_pages, **kw)  # bt_stride too small
+    assert "bt_stride" in _err()
+
+
+def test_validate_slots(L):
+    import numpy as np
+    dsa.dsa_validate_slots(np.array([0, 5, -1, 64 * 9 + 63], np.int32), 10)
+    dsa.dsa_validate_slots(np.zeros(0, np.int32), 1)
+    for slots, word in (([3, 3], "twice"), ([640], "neither -1"), ([-2], "neither -1")):
+        with pytest.raises(dsa.DsaError) as e:
+            dsa.dsa_validate_slots(np.array(slots, np.int32), 10)
+        assert word in str(e.value)
