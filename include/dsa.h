@@ -217,6 +217,25 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
                                  void* stream);
 
 /*
+ * dsa_sparse_mla_decode without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Every
+ * argument means what it means for dsa_sparse_mla_decode and the kernels are the same, so the
+ * results are bitwise those of that call.  When the splits are merged inside the call
+ * (num_splits > 1, o_part NULL) their fp16 partials go to a scratch array the library holds
+ * in device memory, 64 MiB per GPU, kept until the process ends: calls needing more than that,
+ * dsa_sparse_mla_workspace_size(n_q, num_splits) > 64 MiB (about n_q * num_splits > 680), return
+ * DSA_ERR_WORKSPACE.  Nothing is allocated and nothing is cleared: every split writes its whole
+ * partial.  All calls on one GPU share that GPU's scratch, so calls that overlap in time on one
+ * GPU (on different streams, or from different threads) race; issue them on one stream.
+ */
+dsa_status dsa_sparse_mla_decode_noalloc(int32_t n_q, const void* q_bf16, const void* q8,
+                                         const float* q_scale, const void* latent_pages,
+                                         int64_t latent_page_stride, float latent_scale,
+                                         const int32_t* topk_slot, int32_t k, float softmax_scale,
+                                         int32_t num_splits, void* out_bf16, float* lse,
+                                         float* o_part, float* lse_part, void* stream);
+
+/*
  * Stages 2 + 3 (+ 4) in one launch: the final top-k pass and the sparse MLA.  Every
  * (split, row) workgroup of the attention first selects its row's top k from the
  * candidates dsa_index_score wrote (cand_workspace, written with cand_k = k for this batch

@@ -63,13 +63,15 @@ def lib() -> ctypes.CDLL:
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_cache_append.argtypes = [_I32, _P, _P, _P, _F32, _P, _I64, _P, _I64, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
+        L.dsa_sparse_mla_decode_noalloc.argtypes = [_I32, _P, _P, _P, _P, _I64, _F32, _P, _I32,
+                                                    _F32, _I32, _P, _P, _P, _P, _P]
         L.dsa_validate_batch.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _I32, _I64, _P, _I32]
         L.dsa_validate_slots.argtypes = [_I32, _P, _I64]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
         for f in ("dsa_index_score", "dsa_index_score_mxfp4", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
                   "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append", "dsa_validate_batch",
-                  "dsa_validate_slots"):
+                  "dsa_validate_slots", "dsa_sparse_mla_decode_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -284,6 +286,41 @@ def dsa_sparse_mla_decode(q_mla: Optional[torch.Tensor], latent_pages: torch.Ten
                                        _ptr(lse_part), _ptr(workspace),
                                        workspace.numel() if workspace is not None else 0,
                                        _stream(stream)))
+
+
+def dsa_sparse_mla_decode_noalloc(q_mla: Optional[torch.Tensor], latent_pages: torch.Tensor,
+                                  latent_scale: float, topk_slot: torch.Tensor,
+                                  softmax_scale: float, num_splits: int, *,
+                                  out: Optional[torch.Tensor] = None,
+                                  lse: Optional[torch.Tensor] = None,
+                                  o_part: Optional[torch.Tensor] = None,
+                                  lse_part: Optional[torch.Tensor] = None,
+                                  q8: Optional[torch.Tensor] = None,
+                                  q_scale: Optional[torch.Tensor] = None,
+                                  latent_page_stride: Optional[int] = None, stream=None) -> None:
+    """dsa_sparse_mla_decode without a workspace: merged split partials go to the library's
+    static device scratch (64 MiB per GPU), so the call allocates nothing."""
+    n_q, k = topk_slot.shape
+    _expect(topk_slot, "topk_slot", torch.int32, (n_q, k))
+    if q8 is not None:
+        _expect(q8, "q8", torch.uint8, (n_q, MLA_HEADS, LATENT_DIM))
+        _expect(q_scale, "q_scale", torch.float32, (n_q, MLA_HEADS))
+    else:
+        _expect(q_mla, "q_mla", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+    if o_part is not None:
+        _expect(o_part, "o_part", torch.float32, (num_splits, n_q, MLA_HEADS, V_DIM))
+        _expect(lse_part, "lse_part", torch.float32, (num_splits, n_q, MLA_HEADS))
+    else:
+        _expect(out, "out", torch.bfloat16, (n_q, MLA_HEADS, V_DIM))
+        _expect(lse, "lse", torch.float32, (n_q, MLA_HEADS))
+    stride = (latent_page_stride if latent_page_stride is not None
+              else latent_pages.stride(0) * latent_pages.element_size())
+    _check(lib().dsa_sparse_mla_decode_noalloc(n_q, _ptr(q_mla), _ptr(q8), _ptr(q_scale),
+                                               _ptr(latent_pages), int(stride),
+                                               float(latent_scale), _ptr(topk_slot), int(k),
+                                               float(softmax_scale), int(num_splits), _ptr(out),
+                                               _ptr(lse), _ptr(o_part), _ptr(lse_part),
+                                               _stream(stream)))
 
 
 def dsa_topk_sparse_mla(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,

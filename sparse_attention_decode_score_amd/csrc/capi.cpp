@@ -293,6 +293,41 @@ dsa_status dsa_sparse_mla_decode(int32_t n_q, const void* q_bf16, const void* q8
                   "dsa_sparse_mla_decode");
 }
 
+dsa_status dsa_sparse_mla_decode_noalloc(int32_t n_q, const void* q_bf16, const void* q8,
+                                         const float* q_scale, const void* latent_pages,
+                                         int64_t latent_page_stride, float latent_scale,
+                                         const int32_t* topk_slot, int32_t k, float softmax_scale,
+                                         int32_t num_splits, void* out_bf16, float* lse,
+                                         float* o_part, float* lse_part, void* stream) {
+  dsa_status st = check_mla_inputs(n_q, q_bf16, q8, q_scale, latent_pages, latent_page_stride,
+                                   latent_scale, k, softmax_scale, num_splits);
+  if (st != DSA_OK) return st;
+  const bool prepared = q8 != nullptr;
+  DSA_REQUIRE(topk_slot, "topk_slot must be non-null");
+  DSA_REQUIRE((o_part == nullptr) == (lse_part == nullptr),
+              "o_part and lse_part must both be given or both be NULL");
+  if (o_part) {
+    DSA_REQUIRE(aligned(o_part, 16), "o_part must be 16-byte aligned");
+  } else {
+    DSA_REQUIRE(out_bf16 && lse, "out_bf16 and lse are needed when o_part is NULL");
+    DSA_REQUIRE(aligned(out_bf16, 16), "out_bf16 must be 16-byte aligned");
+    const size_t need = num_splits > 1 ? dsa::sparse_mla_workspace_bytes(n_q, num_splits) : 0;
+    if (need > dsa::sparse_mla_noalloc_scratch_bytes())
+      return fail(DSA_ERR_WORKSPACE,
+                  "n_q = %d rows x %d splits need %zu bytes of split partials; the library's "
+                  "static scratch holds %zu (use dsa_sparse_mla_decode with a workspace)",
+                  n_q, num_splits, need, dsa::sparse_mla_noalloc_scratch_bytes());
+  }
+  return launched(dsa::launch_sparse_mla_noalloc(
+                      n_q, static_cast<const uint16_t*>(q_bf16),
+                      prepared ? static_cast<const uint8_t*>(q8) : nullptr,
+                      prepared ? q_scale : nullptr, static_cast<const uint8_t*>(latent_pages),
+                      latent_page_stride, latent_scale, topk_slot, k, softmax_scale, num_splits,
+                      o_part, lse_part, static_cast<uint16_t*>(out_bf16), lse,
+                      static_cast<hipStream_t>(stream)),
+                  "dsa_sparse_mla_decode_noalloc");
+}
+
 dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
                                const int32_t* cu_q, const int32_t* seq_lens, float* scores,
                                int64_t score_stride, int32_t k, const int32_t* block_table,

@@ -71,6 +71,16 @@ hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, cons
                              float softmax_scale, int num_splits, float* o_part, float* lse_part,
                              uint16_t* out_bf16, float* lse, void* workspace, hipStream_t st);
 
+// The same without a workspace: the fp16 split partials go to the library's static device
+// scratch (sparse_mla_noalloc_scratch_bytes() bytes per device; calls on one GPU share it).
+size_t sparse_mla_noalloc_scratch_bytes();
+hipError_t launch_sparse_mla_noalloc(int n_q, const uint16_t* q, const uint8_t* q8,
+                                     const float* q_scale, const uint8_t* latent_pages,
+                                     int64_t latent_page_stride, float latent_scale,
+                                     const int32_t* topk_slot, int k, float softmax_scale,
+                                     int num_splits, float* o_part, float* lse_part,
+                                     uint16_t* out_bf16, float* lse, hipStream_t st);
+
 // Stage 2's final pass fused into the sparse MLA: every (split, row) workgroup selects its
 // row's top k from the candidates in t, then attends (out/lse, fp16-merged when S > 1).
 hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,

@@ -28,6 +28,8 @@
 // max exceeds it by more than 2^4, so the accumulator rescale is rare; probabilities stay
 // below 2^4 and are scaled by 2^4 before conversion to a two-term E4M3 pair (hi + residual),
 // which keeps about 8 significant bits through the value product.
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
 #include "dsa_select.hpp"
@@ -538,6 +540,54 @@ hipError_t launch_sparse_mla(int n_q, const uint16_t* q, const uint8_t* q8, cons
   return launch_mla_common(nullptr, n_q, q, q8, q_scale, latent_pages, latent_page_stride,
                            latent_scale, topk_slot, k, softmax_scale, num_splits, o_part,
                            lse_part, out_bf16, lse, workspace, st);
+}
+
+// ------------------------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the fp16 split partials and their LSEs live in
+// a file-scope device array instead of a caller workspace.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code `scratch` names a host-side stand-in, so
+// its device address is looked up once per device (with that device current) and only that
+// address is ever handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+size_t sparse_mla_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+static hipError_t noalloc_scratch_ptr(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_sparse_mla_noalloc(int n_q, const uint16_t* q, const uint8_t* q8,
+                                     const float* q_scale, const uint8_t* latent_pages,
+                                     int64_t latent_page_stride, float latent_scale,
+                                     const int32_t* topk_slot, int k, float softmax_scale,
+                                     int num_splits, float* o_part, float* lse_part,
+                                     uint16_t* out_bf16, float* lse, hipStream_t st) {
+  void* ws = nullptr;
+  if (!o_part && num_splits > 1) {  // the only case whose kernels use scratch
+    if (sparse_mla_workspace_bytes(n_q, num_splits) > kNoAllocScratchBytes)
+      return hipErrorInvalidValue;  // (the C ABI rejects this case before calling)
+    const hipError_t e = noalloc_scratch_ptr(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_sparse_mla(n_q, q, q8, q_scale, latent_pages, latent_page_stride, latent_scale,
+                           topk_slot, k, softmax_scale, num_splits, o_part, lse_part, out_bf16,
+                           lse, ws, st);
 }
 
 hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
