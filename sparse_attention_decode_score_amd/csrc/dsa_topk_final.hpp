@@ -145,13 +145,20 @@ struct FinalScratch {
 // min(k, n_vis).  Ends with a barrier, so out[] is visible to the whole workgroup.
 // rs.q set: the indexer stored no scores; the groups that must be re-read are first
 // recomputed into the row's score buffer (bt_row: the request's block-table row).
+// Only the resend uses sc.lkey / sc.lidx (and `out` before the selection): every thread
+// calls before_scratch() once before it does, so a caller can keep other data in that LDS
+// until then.
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <class Hook = NoHook>
 __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_t score_stride,
                                        int k, int num_groups, int64_t row_cap,
                                        const uint32_t* __restrict__ cand_key,
                                        const int32_t* __restrict__ cand_idx,
                                        const ChunkInfo* __restrict__ info,
                                        const IndexRescore& rs, const int32_t* bt_row, int* out,
-                                       const FinalScratch& sc) {
+                                       const FinalScratch& sc, Hook before_scratch = Hook{}) {
   const int tid = threadIdx.x;
   uint32_t* lkey = sc.lkey;
   int32_t* lidx = sc.lidx;
@@ -233,6 +240,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
     for (int g = tid + kFinalThreads; g < n_groups; g += kFinalThreads) any |= flagged(g) ? 1 : 0;
     int parity = 0;
     if (block_sum(any, red, parity) > 0) {
+      before_scratch();
       // Rebuild the candidate list in token order, flagged groups in full and the others as
       // sent: group starts go to LDS (`out` is free until the next selection), then every
       // thread fills its own elements, locating each one's group by a fixed-depth search.

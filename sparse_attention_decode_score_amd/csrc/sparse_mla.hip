@@ -8,27 +8,36 @@
 // batches add parallelism inside each row ("Context-parallel sparse-attention prefill"):
 // here that is the split index s of a (split, row) workgroup.
 //
-// Workgroup = 8 waves on one CU.  Waves 6, 7 gather 64-token latent tiles (slot -> page ->
-// 576 bytes, non-temporal loads): they keep three tiles in flight in registers and write
-// each into a double-buffered LDS ring one tile ahead of the compute waves.  Every gather is
-// issued unconditionally (a slot of -1 or a token past the split reads a zero row), so the
-// compiler's wait counts stay exact and only the oldest tile is ever waited for.  Waves
-// 0..5 each own 32 heads x 256 value dims of the row.  They quantise the row's query to
-// E4M3 with one power-of-two scale per head (as dsa_quantize_q does) straight into LDS,
-// where it is the B operand of
-//   S[token][head] = L8[32 tokens x 576] * Q8^T          (9 x v_mfma 32x32x64 per 32 tokens)
-// The two waves of a head tile each form the logits of one 32-token half of a tile; the A
-// rows are permuted so that lane l holds head l%32's logits for tokens 32*(l/32) + 16*half
-// + i.  They exchange per-head maxima and the probabilities through LDS, so each wave gets
-// the E4M3 A operand of
-//   O[head][dim] += P8[32 heads x 64 tokens] * V8[64 tokens x 256 dims]   (8 x v_mfma 32x32x64)
-// whose B operand comes from the same LDS tile through ds_read_b64_tr_b8 (8 tokens of one
-// dim per lane), so the value matrix is never transposed in memory.  Each compute wave keeps
-// its 32x256 fp32 accumulator in registers.  The running max is only raised when a tile's
-// max exceeds it by more than 2^4, so the accumulator rescale is rare; probabilities stay
-// below 2^4 and are scaled by 2^4 before conversion to a two-term E4M3 pair (hi + residual),
-// which keeps about 8 significant bits through the value product.
+// Workgroup = 8 waves, one per CU (two per SIMD).  The split's slots sit in LDS; 64-token
+// latent tiles are gathered straight into a 3-tile LDS ring with 16-byte global-to-LDS loads
+// (every wave moves 4 or 5 of a tile's 36 16-byte columns; lane l moves token l), so tile
+// t+2 is in flight while tile t is used and no register holds gathered bytes.  A tile is
+// stored column-blocked, [36 columns][64 tokens][16 B], which serves both products without
+// bank conflicts:
+//   logits  S[token][head] = L8[32 tokens x 576] * Q8^T   (9 x v_mfma 32x32x64 per 32 tokens)
+//           by waves 0..5, wave w for head tile w/2 (32 heads) and 32-token block w%2, with
+//           its head tile's E4M3 query held in registers (72 VGPRs);
+//   values  O^T[dim][head] += V8^T[32 dims x 64 tokens] * P8^T[64 tokens x 32 heads]
+//           by all 8 waves over 48 (head tile, 32-dim tile) accumulators (see the roles
+//           below), V read through ds_read_b64_tr_b8 (8 tokens of one dim per lane) so the
+//           latent is never transposed in memory; each lane's accumulators belong to one head,
+//           so per-head rescaling and normalisation are lane-local.
+// Softmax per (head, 32-token block): the block's maximum is rounded up to an integer m_b in
+// log2 units, p = 2^(x - m_b) in (0, 1], and p * 2^8 enters the value product as a two-term
+// E4M3 pair (hi, and the residual scaled by 2^4) whose scale 2^(m_b - m_ref - 8) (and 2^-4
+// less for the residual) is the E8M0 operand scale of the MFMA: one scale per lane, and a
+// lane holds exactly one head's 32-token block.  So every block keeps ~8 significant bits
+// however far its maximum lies below the row's, and the accumulator's reference m_ref (an
+// integer, raised only when a block exceeds it by more than 2^16) changes by exact powers of
+// two.  Block sums of the fp32 p give the softmax denominator and the LSE.
+//
+// One barrier per tile.  In the step of tile t every wave: waits for its own gathers of tile
+// t; barrier; requests tile t+2 into the buffer tile t-1 used; multiplies tile t-1's
+// probabilities (published before the barrier) with its value registers; then (waves 0..5)
+// forms tile t's logits and probabilities into a double-buffered LDS exchange, and (all)
+// reads tile t's values into registers, so the tile's LDS buffer is free at the next barrier.
 #include <mutex>
+#include <type_traits>
 
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
@@ -40,14 +49,18 @@ namespace dsa {
 namespace {
 
 constexpr int kTile = 64;
-constexpr int kRowStride = 592;  // LDS bytes per latent / query row (576 + 16: conflict-free b128 reads)
-constexpr int kThreads = 512;    // 6 compute waves + 2 loader waves
-constexpr int kRing = 3;         // tiles the loader waves keep in flight in registers
-constexpr int kSlotsLds = 4096;  // slots of a split held in LDS (k <= 4096)
+constexpr int kThreads = 512;     // 8 waves
+constexpr int kWaves = kThreads / 64;
+constexpr int kRing = 3;          // latent tiles in LDS: the one in use and two in flight
+constexpr int kCols = kLatDim / 16;          // 36 16-byte columns per latent row
+constexpr int kTileBytes = kTile * kLatDim;  // 36,864
+constexpr int kSlotsLds = 4096;   // slots of a split held in LDS (k <= 4096)
+constexpr int kDutyWaves = 6;     // waves forming logits: 3 head tiles x 2 token blocks
+constexpr int kQStride = 592;     // staging row of the query codes (576 + 16: conflict-free reads)
+constexpr int kTau = 16;          // accumulator reference slack, log2 units
+constexpr int kNoMax = -(1 << 29);  // block maximum of a block without a visible token
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 4.0f;      // running-max slack in log2 units
-constexpr float kPScale = 16.0f;  // probabilities are converted to E4M3 as P * 2^4 <= 2^8
 
 // The latent row gathered for padding: a slot of -1 or a position past the split.
 __device__ __attribute__((aligned(64))) uint8_t g_zero_row[kLatDim];
@@ -58,23 +71,99 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier for LDS data, after this wave's global-to-LDS gathers have completed down
+// to the newest `pending` instructions (the loads' completion is not tracked by the compiler).
+// The memory clobber keeps every LDS access on its side.
+template <int pending>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(pending >= 0 && pending < 16, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(pending) : "memory");
+}
+
+// The value operand of ND dim tiles, read with ds_read_b64_tr_b8 from LDS byte address
+// `addr` (+ 2048 per dim tile; + 0, 128, 512, 640 for tokens +0, +8, +32, +40: the operand's
+// K positions 16 g .. +15 and 32 + 16 g .. +15, see the probabilities).  The reads and their wait are one asm
+// block: written as builtins, the compiler orders these transposed reads after every
+// global-to-LDS gather in flight (it cannot tell they touch another buffer), which would
+// drain the ring at every tile.
+template <int ND>
+__device__ __forceinline__ void read_values(uint32_t addr, v8i (&vb)[ND]);
+
+#define DSA_TR(i, off) "ds_read_b64_tr_b8 %" #i ", %[a] offset:" #off "\n\t"
+template <>
+__device__ __forceinline__ void read_values<3>(uint32_t addr, v8i (&vb)[3]) {
+  v2i r[12];
+  asm volatile(DSA_TR(0, 0) DSA_TR(1, 128) DSA_TR(2, 512) DSA_TR(3, 640)
+               DSA_TR(4, 2048) DSA_TR(5, 2176) DSA_TR(6, 2560) DSA_TR(7, 2688)
+               DSA_TR(8, 4096) DSA_TR(9, 4224) DSA_TR(10, 4608) DSA_TR(11, 4736)
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                 "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+               : [a] "v"(addr)
+               : "memory");
+#pragma unroll
+  for (int d = 0; d < 3; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vb[d][2 * j] = r[4 * d + j][0];
+      vb[d][2 * j + 1] = r[4 * d + j][1];
+    }
+}
+template <>
+__device__ __forceinline__ void read_values<5>(uint32_t addr, v8i (&vb)[5]) {
+  v2i r[20];
+  asm volatile(DSA_TR(0, 0) DSA_TR(1, 128) DSA_TR(2, 512) DSA_TR(3, 640)
+               DSA_TR(4, 2048) DSA_TR(5, 2176) DSA_TR(6, 2560) DSA_TR(7, 2688)
+               DSA_TR(8, 4096) DSA_TR(9, 4224) DSA_TR(10, 4608) DSA_TR(11, 4736)
+               DSA_TR(12, 6144) DSA_TR(13, 6272) DSA_TR(14, 6656) DSA_TR(15, 6784)
+               DSA_TR(16, 8192) DSA_TR(17, 8320) DSA_TR(18, 8704) DSA_TR(19, 8832)
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+                 "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+                 "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]),
+                 "=&v"(r[17]), "=&v"(r[18]), "=&v"(r[19])
+               : [a] "v"(addr)
+               : "memory");
+#pragma unroll
+  for (int d = 0; d < 5; ++d)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vb[d][2 * j] = r[4 * d + j][0];
+      vb[d][2 * j + 1] = r[4 * d + j][1];
+    }
+}
+#undef DSA_TR
+
+// Two floats -> two bf16 (round to nearest even) / two fp16 in one dword, low half first.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {  // one v_cvt_pk_bf16_f32
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{x0, x1}, bf16x2_t));
+}
+__device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {  // one v_cvt_pk_f16_f32
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{x0, x1}, f16x2_t));
+}
+
+// Workgroup barrier for LDS data only (global loads and gathers stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Output of a workgroup: the row's bf16 O and LSE (one split), or its split's partial O
 // (fp32, or fp16 divided by the latent scale, which bounds it by 448) and LSE.
 enum PartMode { kDirect = 0, kPartF32 = 1, kPartF16 = 2 };
 
 struct MlaSmem {
-  uint8_t lat[2][kTile * kRowStride];
-  uint8_t q8s[kMlaHeads * kRowStride];
-  uint8_t pbuf[3][2][32][64];  // [head tile][hi/lo][head][token]
-  float xmax[3][2][32];
-  float xfer[6][32];
-  float qsc[kMlaHeads];
+  uint8_t lat[kRing][kTileBytes];            // [column][token][16 B] per tile
+  uint8_t pbuf[2][3][2][2][2][32][16];       // [tile parity][head tile][block][hi/lo][half][head][16 tokens]
+  int bmax[2][3][2][32];                     // integer block maxima (log2 units), kNoMax if empty
+  float bsum[2][3][2][32];                   // block sums of 2^(x - m_b)
+  uint8_t qtail[4][kMlaHeads][16];           // E4M3 query dims 512..575: [16-byte part][head][16 B]
   int32_t slot_l[kSlotsLds];
-  uint64_t valid_mask[2];
 };
 // The final top-k pass of the fused kernel runs before any of the above is used: its
-// scratch overlays the latent ring, the query and the probability buffers, and its output
-// (the row's selected token indices) is written straight into slot_l.
+// scratch overlays the latent ring and the exchange buffers, and its output (the row's
+// selected token indices) is written straight into slot_l.
 struct SelectSmem {
   uint32_t lkey[kFinalTile];
   int32_t lidx[kFinalTile];
@@ -84,6 +173,10 @@ struct SelectSmem {
 };
 static_assert(sizeof(SelectSmem) <= offsetof(MlaSmem, slot_l), "selection scratch overlaps slot_l");
 static_assert(kFinalThreads == kThreads, "the fused kernel runs the final pass on its own threads");
+static_assert(sizeof(MlaSmem) <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(kMlaHeads * kQStride <= kTileBytes + sizeof(MlaSmem::pbuf),
+              "query staging fits ring buffer 2 and the probability exchange");
+static_assert(offsetof(MlaSmem, pbuf) == 3 * kTileBytes, "staging spans buffer 2 and pbuf");
 
 // Inputs of the fused final top-k pass (stage 2) of the select-and-attend kernel.
 struct SelectArgs {
@@ -112,18 +205,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     int num_splits, int n_q, int mode, void* __restrict__ o_part, float* __restrict__ lse_part,
     uint16_t* __restrict__ out_bf16, float* __restrict__ lse_out) {
   __shared__ __attribute__((aligned(16))) MlaSmem sm;
-  auto& lat = sm.lat;
-  auto& q8s = sm.q8s;
-  auto& pbuf = sm.pbuf;
-  auto& xmax = sm.xmax;
-  auto& xfer = sm.xfer;
-  auto& qsc = sm.qsc;
   auto& slot_l = sm.slot_l;
-  auto& valid_mask = sm.valid_mask;
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; when the grid divides
-  // evenly, all splits of a row go to one XCD, so the row's query (read by every split)
-  // comes from that XCD's L2 after the first read.
+  // evenly, all splits of a row go to one XCD, so the row's query and candidates (read by
+  // every split) come from that XCD's L2 after the first read.
   int s = blockIdx.x, row = blockIdx.y;
   {
     const int total = num_splits * n_q;
@@ -142,6 +228,34 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
 
+  // The row's query goes out first, so that its latency hides behind the selection or the
+  // slot-list load.  Prepared E4M3 codes go to registers (4 threads per head, 144 dims
+  // each; waves 6, 7 load a copy of heads 0..31 that nobody uses, which keeps the loads
+  // outside any divergent branch).  A bf16 query goes to LDS by direct gathers: its 110,592
+  // bytes fill the three latent buffers exactly, which the selection leaves alone unless it
+  // resends groups (it then waits for the gathers first, and the query is staged again
+  // after it).
+  const bool qthread = threadIdx.x < 4 * kMlaHeads;
+  const int qh = (threadIdx.x >> 2) % kMlaHeads, qpart = threadIdx.x & 3;
+  v4i raw[18];
+  float qs_given = 0.f;
+  if (q8_in) {
+    const uint8_t* src = q8_in + ((int64_t)row * kMlaHeads + qh) * kLatDim + qpart * 144;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+    qs_given = qs_in[(int64_t)row * kMlaHeads + qh];
+  }
+  auto stage_query = [&]() {
+    constexpr int kQChunks = kMlaHeads * kLatDim * 2 / 1024;  // 108 chunks of 1 KB
+    static_assert(kQChunks * 1024 == kRing * kTileBytes, "the bf16 query fills the ring");
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t)row * kMlaHeads * kLatDim);
+    DSA_LDS uint8_t* dst = (DSA_LDS uint8_t*)(&sm.lat[0][0]);
+    for (int c = wave; c < kQChunks; c += kWaves)  // wave-uniform
+      __builtin_amdgcn_global_load_lds(qrow + 1024 * c + 16 * lane, dst + 1024 * c, 16, 0, 0);
+  };
+  if (!q8_in) stage_query();
+  bool q_in_lds = q8_in == nullptr;
+
   if constexpr (SELECT) {
     // stage 2 for this row (every split of the row runs it: it is latency-bound), then the
     // split's slice of the selected tokens -> physical slots in slot_l
@@ -150,9 +264,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     row_of(sel.cu_q, sel.seq_lens, sel.num_seqs, row, b, pos);
     const FinalScratch sc{ss.lkey, ss.lidx, ss.red, &ss.note, ss.bucket};
     const int32_t* bt = sel.block_table + (int64_t)b * sel.bt_stride;
+    // a resend overwrites the staged query: its gathers must have landed first
+    auto before_resend = [&]() {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      q_in_lds = false;
+    };
     const int n_out = final_select_row(row, pos + 1, sel.scores, sel.score_stride, k,
                                        sel.num_groups, sel.row_cap, sel.cand_key, sel.cand_idx,
-                                       sel.info, sel.rs, bt, slot_l, sc);
+                                       sel.info, sel.rs, bt, slot_l, sc, before_resend);
     auto to_slot = [&](int t) { return t < 0 ? -1 : bt[t >> 6] * kPage + (t & (kPage - 1)); };
     if (s == 0 && (sel.topk_idx || sel.topk_slot)) {
       for (int i = threadIdx.x; i < k; i += kThreads) {
@@ -174,317 +294,366 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       const int j = threadIdx.x + u * kThreads;
       if (j < n_tok) slot_l[j] = mine[u];
     }
-    __syncthreads();  // barrier 0: the selection scratch is dead, slot_l holds the split's slots
   } else {
-    // the split's slot list -> LDS (barrier 0)
+    // the split's slot list -> LDS
     const int32_t* slots = topk_slot + (int64_t)row * k + beg;
     for (int i = threadIdx.x; i < n_tok; i += kThreads) slot_l[i] = slots[i];
-    __syncthreads();
   }
-  auto slot_of = [&](int j) { return j < n_tok ? slot_l[j] : -1; };
+  // slot_l holds the split's slots, the selection scratch is dead, and every query gather
+  // has landed (a resend overwrote the staged query: it is staged again)
+  if (!q8_in && !q_in_lds) stage_query();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  if (wave >= 6) {
-    // ---------------------------------------------------------------- loader waves
-    // wave 6 moves tile rows 0..31, wave 7 rows 32..63; lane l moves 16-byte pieces
-    // (l%4) + 4c (c = 0..8) of rows 16*qq + l/4 of its half.
-    const int half = wave - 6;
-    typedef v4i TileRegs[2][9];
-    auto issue = [&](int t, TileRegs& d) {
+  // ---- gathers: wave w moves columns w, w+8, .. (< 36) of every row of a tile; lane l
+  // moves token l.  Tiles past the split gather zero rows into a buffer nobody reads, so
+  // every wave issues the same number of loads per tile and its wait counts are fixed.
+  // Steps jj0 .. jj1-1 (of 5) of tile t's gathers; a wave may issue them in pieces.
+  auto issue = [&](int t, int jj0, int jj1) {
+    const int j = t * kTile + lane;
+    const int slot = j < n_tok ? slot_l[j] : -1;
+    const uint8_t* src = slot >= 0 ? lat_pages + (int64_t)(slot >> 6) * page_stride +
+                                         (int64_t)(slot & (kPage - 1)) * kLatDim
+                                   : g_zero_row;
+    DSA_LDS uint8_t* dst = (DSA_LDS uint8_t*)(&sm.lat[t % kRing][0]);
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int j = t * kTile + 32 * half + 16 * qq + (lane >> 2);
-        const int slot = slot_of(j);
-        const uint8_t* src = slot >= 0 ? lat_pages + (int64_t)(slot >> 6) * page_stride +
-                                             (int64_t)(slot & (kPage - 1)) * kLatDim
-                                       : g_zero_row;
+    for (int jj = 0; jj < 5; ++jj) {
+      const int c = wave + kWaves * jj;
+      if (jj >= jj0 && jj < jj1 && (jj < 4 || c < kCols))  // wave-uniform
+        __builtin_amdgcn_global_load_lds(src + 16 * c, dst + 1024 * c, 16, 0, 0);
+    }
+  };
+
+  // Two roles, so that no wave needs more than 256 registers and every SIMD (waves w and
+  // w + 4) carries the same matrix work per tile (37-38 MFMAs):
+  //  duty waves 0..5   logits of head tile w/2 for token block w%2 (its E4M3 query in
+  //                    registers), and the values of that head tile for dim tiles
+  //                    6 + 5 (w%2) .. +4 (5 accumulators);
+  //  value waves 6, 7  the values of all three head tiles for dim tiles 3 (w-6) .. +2
+  //                    (9 accumulators).
+  auto run = [&](auto role) {
+    constexpr bool DUTY = decltype(role)::value;
+    constexpr int NH = DUTY ? 1 : 3;  // head tiles whose values this wave accumulates
+    constexpr int ND = DUTY ? 5 : 3;  // dim tiles (32 dims each)
+    const int ht_d = wave >> 1, blk = wave & 1;
+    const int ht0 = DUTY ? ht_d : 0;
+    const int dt0 = DUTY ? 6 + 5 * blk : 3 * (wave - kDutyWaves);
+
+    // ---- the query: the row's 96 x 576 E4M3 query goes to a staging area (ring buffer 2 and
+    // the probability exchange, unused until the first barrier of the loop), 4 threads per
+    // head; then every duty wave loads its head tile's codes as the B operand of the logits:
+    // lane (n, g) holds head 32 ht + n, bytes 64 kb + 32 g .. +31 of each 64-byte chunk kb.
+    // A bf16 query is read from LDS before the first two tiles' gathers and quantised after
+    // them.
+    uint8_t* const qstage = &sm.lat[2][0];   // [96][kQStride] codes; scales in bsum
+    float* const qsc = &sm.bsum[0][0][0][0];
+    if (q8_in) {
+      // the prepared codes loaded at the start go to LDS before the gathers are issued, so
+      // that waiting for them waits for nothing else (waves 6, 7 hold heads 0..31 again and
+      // write the same bytes)
+      uint8_t* dst = qstage + qh * kQStride + qpart * 144;
 #pragma unroll
-        for (int c = 0; c < 9; ++c)
-          d[qq][c] = __builtin_nontemporal_load(
-              reinterpret_cast<const v4i*>(src + ((lane & 3) + 4 * c) * 16));
+      for (int i = 0; i < 9; ++i) *reinterpret_cast<v4i*>(dst + 16 * i) = raw[i];
+      if (qpart == 0) qsc[qh] = qs_given;
+    } else {
+      // the staged bf16 query: every wave reads its part before any gather may overwrite it
+      if (qthread) {
+        const uint8_t* src = &sm.lat[0][0] + (qh * kLatDim + qpart * 144) * 2;
+#pragma unroll
+        for (int i = 0; i < 18; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+      }
+      lds_barrier();
+    }
+    issue(0, 0, 5);
+    issue(1, 0, 5);
+    if (!q8_in && qthread) {
+      uint8_t* dst = qstage + qh * kQStride + qpart * 144;
+      // one power-of-two scale per head: the smallest 2^e with absmax <= 448 * 2^e
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < 18; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          am = fmaxf(am, fmaxf(fabsf(bf16_lo((uint32_t)raw[i][j])), fabsf(bf16_hi((uint32_t)raw[i][j]))));
+      am = fmaxf(am, __shfl_xor(am, 1, 64));
+      am = fmaxf(am, __shfl_xor(am, 2, 64));
+      const int e = pow2_scale_exp(am);
+      const float inv = ldexpf(1.0f, -e);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        v4i c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = (uint32_t)raw[2 * i + j / 2][2 * (j % 2)];
+          const uint32_t w1 = (uint32_t)raw[2 * i + j / 2][2 * (j % 2) + 1];
+          c[j] = (int)cvt4_e4m3(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
+                                bf16_hi(w1) * inv);
+        }
+        *reinterpret_cast<v4i*>(dst + 16 * i) = c;
+      }
+      if (qpart == 0) qsc[qh] = ldexpf(1.0f, e);
+    }
+    lds_barrier();  // the staged query is visible (the gathers stay in flight)
+    v8i qb[DUTY ? 8 : 1];  // chunks 0..7; chunk 8 (dims 512..575) stays in LDS (qtail)
+    float mult = 0.f;
+    if constexpr (DUTY) {
+      const int h = 32 * ht_d + n;
+      const uint8_t* qr = qstage + h * kQStride + 32 * g;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const v4i a0 = *reinterpret_cast<const v4i*>(qr + 64 * kb);
+        const v4i a1 = *reinterpret_cast<const v4i*>(qr + 64 * kb + 16);
+        qb[kb] = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      }
+      mult = qsc[h] * lat_scale * sm_scale * kLog2e;
+      // the last chunk goes to its own LDS array (read back at every tile), which keeps the
+      // duty waves within their registers; published by the first barrier of the loop
+      if (blk == 0) {
+        *reinterpret_cast<v4i*>(&sm.qtail[2 * g][h][0]) = *reinterpret_cast<const v4i*>(qr + 512);
+        *reinterpret_cast<v4i*>(&sm.qtail[2 * g + 1][h][0]) =
+            *reinterpret_cast<const v4i*>(qr + 512 + 16);
+      }
+    }
+
+    v16f acc[NH][ND];  // O^T: lane (n, g) holds head 32 (ht0 + hh) + n, dims 32 (dt0 + dd) +
+                       // 8 a + 4 g + c in register 4 a + c
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int dd = 0; dd < ND; ++dd) acc[hh][dd] = v16f{};
+    int m_ref[NH];    // accumulator reference of head 32 ht + n (log2 units), same in every wave
+    float z_run[NH];  // this lane's block-g share of head 32 ht + n's softmax sum
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      m_ref[hh] = kNoMax;
+      z_run[hh] = 0.f;
+    }
+    // V operand of the last tile read: dims 32 dt + n, tokens 16 g .. +15 and 32 + 16 g .. +15
+    // (the K positions of lane (n, g)).  16-lane group vgrp reads the 16 dims of column
+    // 2 dt + vgrp % 2 for 8 tokens at a time; lanes 2r, 2r+1 address the two halves of token
+    // row r
+    v8i vb[ND];
+
+    // ---- values of tile t-1 (PV): O^T += V8^T * P8^T with the blocks' E8M0 scales
+    auto values_of = [&](int tp, int n, int g) {
+      const int pb = tp & 1;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const int ht = ht0 + hh;
+        const int mi = sm.bmax[pb][ht][g][n];
+        const float zb = sm.bsum[pb][ht][g][n];
+        const int mnew = max(mi, __shfl_xor(mi, 32, 64));
+        if (__ballot(mnew > m_ref[hh] + kTau) != 0ull) {
+          // rare: raise the reference and rescale by an exact power of two (every
+          // accumulator register of lane (n, g) belongs to head n)
+          const int mr = max(m_ref[hh], mnew);
+          const float f = exp2f((float)(m_ref[hh] - mr));
+          m_ref[hh] = mr;
+          z_run[hh] *= f;
+#pragma unroll
+          for (int dd = 0; dd < ND; ++dd) acc[hh][dd] *= f;
+        }
+        const int e = max(mi - m_ref[hh], -200);  // <= kTau
+        z_run[hh] += ldexpf(zb, e);
+        const int sc_hi = min(max(127 - 8 + e, 0), 254);
+        const int sc_lo = min(max(127 - 12 + e, 0), 254);
+        // the FP8 operands of v_mfma_scale 32x32x64 hold, in lane (n, g), K positions
+        // 16 g .. +15 in bytes 0..15 and 32 + 16 g .. +15 in bytes 16..31, and the E8M0 scale
+        // of lane (n, j) scales K positions 32 j .. 32 j + 31: so lane (n, g) takes tokens
+        // 16 g .. +15 of block 0 and of block 1, and supplies block g's scale
+        v8i ph, pl;
+        ph.lo = *reinterpret_cast<const v4i*>(&sm.pbuf[pb][ht][0][0][g][n][0]);
+        ph.hi = *reinterpret_cast<const v4i*>(&sm.pbuf[pb][ht][1][0][g][n][0]);
+        pl.lo = *reinterpret_cast<const v4i*>(&sm.pbuf[pb][ht][0][1][g][n][0]);
+        pl.hi = *reinterpret_cast<const v4i*>(&sm.pbuf[pb][ht][1][1][g][n][0]);
+#pragma unroll
+        for (int dd = 0; dd < ND; ++dd) {
+          // O^T[dim][head]: the values are the A operand (unscaled), the probabilities the
+          // B operand with the block's E8M0 scale
+          acc[hh][dd] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[dd], ph, acc[hh][dd], 0,
+                                                                        0, 0, 127, 0, sc_hi);
+          acc[hh][dd] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[dd], pl, acc[hh][dd], 0,
+                                                                        0, 0, 127, 0, sc_lo);
+        }
       }
     };
-    auto store = [&](int t, const TileRegs& d, int buf) {
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int r = 32 * half + 16 * qq + (lane >> 2);
-#pragma unroll
-        for (int c = 0; c < 9; ++c)
-          *reinterpret_cast<v4i*>(&lat[buf][r * kRowStride + ((lane & 3) + 4 * c) * 16]) = d[qq][c];
-      }
-      if (half == 0) {
-        const uint64_t m = __ballot(slot_of(t * kTile + lane) >= 0);
-        if (lane == 0) valid_mask[buf] = m;
-      }
-    };
-    // Every wave executes the same barriers: barrier 1, two per tile (A, B), one after the
-    // last tile and the two of the compute waves' finalize step.  Tile i lives in
-    // ring[i % kRing].  Under load a gather request can wait a long time to issue (every
-    // workgroup of the chip gathers at once), and a loader wave late for a barrier holds
-    // all six compute waves, so the loader requests one tile per step and at most two are
-    // in flight: tile 0 alone first, tile 1 after barrier 1; in the step of tile t it writes
-    // tile t+1 into the other LDS buffer between A and B (every wave has finished tile t-1,
-    // which read that buffer, before A), and requests tile t+kRing after B.  It stops at the
-    // last tile: requests past it (zero rows) are left unread.
-    static_assert(kRing == 3, "the schedule below is written for a ring of three tiles");
-    TileRegs ring[kRing];
-    issue(0, ring[0]);
-    store(0, ring[0], 0);
-    __syncthreads();  // barrier 1: tile 0 and the query are in LDS
-    issue(1, ring[1]);
-    __syncthreads();  // tile 0: A
-    issue(2, ring[2]);
-    store(1, ring[1], 1);
-    __syncthreads();  // B
-    issue(3, ring[0]);
+
 #pragma unroll 1
-    for (int t0 = 1; t0 < n_tiles; t0 += kRing) {
-#pragma unroll
-      for (int u = 0; u < kRing; ++u) {
-        const int t = t0 + u;  // t % kRing == (1 + u) % kRing
-        if (t >= n_tiles) break;  // uniform
-        __syncthreads();  // A
-        store(t + 1, ring[(u + 2) % kRing], (t + 1) & 1);
-        __syncthreads();  // B
-        issue(t + kRing, ring[(u + 1) % kRing]);
-      }
-    }
-    __syncthreads();  // after the last tile
-    __syncthreads();
-    __syncthreads();
-    return;
-  }
+    for (int t = 0; t <= n_tiles; ++t) {
+      // tile t is in LDS once every wave's own gathers of it are done (tile t+1 may still
+      // be in flight); the barrier also publishes tile t-1's probabilities and frees the
+      // buffer tile t-1 used
+      if (wave < kCols - 4 * kWaves) ring_barrier<5>();
+      else ring_barrier<4>();
+      // the lane index as an opaque value of this step: the LDS addresses derived from it are
+      // recomputed here (a few ALU ops) instead of being hoisted out of the loop and spilled
+      int lane_t = lane;
+      asm volatile("" : "+v"(lane_t));
+      const int n = lane_t & 31, g = lane_t >> 5;
+      const int tile_off = __builtin_amdgcn_readfirstlane((t % kRing) * kTileBytes);
+      const uint8_t* tile = &sm.lat[0][0] + tile_off;
 
-  // ------------------------------------------------------------------ compute waves
-  if (q8_in) {
-    // codes and scales prepared by the query quantisation: coalesced copy to LDS
-    const uint8_t* src = q8_in + (int64_t)row * kMlaHeads * kLatDim;
-    for (int i = threadIdx.x; i < kMlaHeads * (kLatDim / 16); i += 384) {
-      const int h = i / (kLatDim / 16), pc = i % (kLatDim / 16);
-      *reinterpret_cast<v4i*>(&q8s[h * kRowStride + pc * 16]) =
-          *reinterpret_cast<const v4i*>(src + (int64_t)i * 16);
-    }
-    if (threadIdx.x < kMlaHeads) qsc[threadIdx.x] = qs_in[(int64_t)row * kMlaHeads + threadIdx.x];
-  } else {
-    // query prep: 4 threads per head, 144 dims each -> E4M3 codes in LDS and the head's
-    // power-of-two scale (smallest 2^e with absmax <= 448 * 2^e)
-    const int h = threadIdx.x >> 2, part = threadIdx.x & 3;
-    const uint16_t* src = q + ((int64_t)row * kMlaHeads + h) * kLatDim + part * 144;
-    v4i raw[18];
+      if constexpr (DUTY) {
+        if (t > 0) values_of(t - 1, n, g);
+        if (t < n_tiles) {
+          issue(t + 2, 0, 2);
+          // ---- logits of head tile ht_d, tokens 32 blk .. +31 of tile t: lane (n, g) gets
+          // head 32 ht + n for tokens 8 (i / 4) + 4 g + i % 4 of the block in register i.  The
+          // accumulator starts at 0 for a visible token and at -inf for a hidden one, so the
+          // softmax below needs no masking.
+          const int pb = t & 1;
+          const int j0 = t * kTile + 32 * blk;
+          const bool vis = j0 + n < n_tok && slot_l[j0 + n] >= 0;
+          const uint32_t vmask = (uint32_t)__ballot(vis);  // lanes 0..31: token n of the block
+          v16f d;
+          if (vmask == 0xFFFFFFFFu) {  // uniform: the whole block is visible
+            d = v16f{};
+          } else {
+            const uint32_t vm_g = vmask >> (4 * g);  // bit 8 a + c: token 8 a + 4 g + c
 #pragma unroll
-    for (int i = 0; i < 18; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 8 * i);
-    float am = 0.f;
+            for (int i = 0; i < 16; ++i) d[i] = ((vm_g >> (8 * (i >> 2) + (i & 3))) & 1u) ? 0.f : -INFINITY;
+          }
+          if (vmask != 0u) {  // uniform
+            const uint8_t* arow = tile + (32 * blk + n) * 16 + 2 * g * 1024;
 #pragma unroll
-    for (int i = 0; i < 18; ++i)
+            for (int kb = 0; kb < 9; ++kb) {
+              v8i A, B;
+              A.lo = *reinterpret_cast<const v4i*>(arow + 4 * kb * 1024);
+              A.hi = *reinterpret_cast<const v4i*>(arow + (4 * kb + 1) * 1024);
+              if (kb < 8) {
+                B = qb[kb < 8 ? kb : 0];
+              } else {
+                B.lo = *reinterpret_cast<const v4i*>(&sm.qtail[2 * g][32 * ht_d + n][0]);
+                B.hi = *reinterpret_cast<const v4i*>(&sm.qtail[2 * g + 1][32 * ht_d + n][0]);
+              }
+              d = mfma_32x32x64_fp8(A, B, d);
+            }
+          }
+          float mx = d[0];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        am = fmaxf(am, fmaxf(fabsf(bf16_lo((uint32_t)raw[i][j])), fabsf(bf16_hi((uint32_t)raw[i][j]))));
-    am = fmaxf(am, __shfl_xor(am, 1, 64));
-    am = fmaxf(am, __shfl_xor(am, 2, 64));
-    const int e = pow2_scale_exp(am);
-    const float inv = ldexpf(1.0f, -e);
-    uint8_t* dst = q8s + h * kRowStride + part * 144;
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, d[i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          // integer block maximum in log2 units (mult > 0; clamped: far-out logits only
+          // saturate it); p * 2^8 = 2^(d * mult + 8 - m_b) in (0, 2^8]
+          const int mi = vmask != 0u ? (int)ceilf(fminf(fmaxf(mx * mult, -1e8f), 1e8f)) : kNoMax;
+          const float off = 8.0f - (float)mi;
+          float zs = 0.f;
+          uint8_t* pw = &sm.pbuf[pb][ht_d][blk][0][0][n][0];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      v4i c;
+          for (int a = 0; a < 4; ++a) {
+            float ph[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w0 = (uint32_t)raw[2 * i + j / 2][2 * (j % 2)];
-        const uint32_t w1 = (uint32_t)raw[2 * i + j / 2][2 * (j % 2) + 1];
-        c[j] = (int)cvt4_e4m3(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
-                              bf16_hi(w1) * inv);
+            for (int c = 0; c < 4; ++c) {
+              ph[c] = __builtin_amdgcn_exp2f(fmaf(d[4 * a + c], mult, off));  // -inf -> 0
+              zs += ph[c];
+            }
+            // two-term E4M3: hi = E4M3(p 2^8), lo = E4M3((p 2^8 - hi) 2^4)
+            const uint32_t hi = cvt4_e4m3(ph[0], ph[1], ph[2], ph[3]);
+            const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+            const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+            const v2s lo01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, ph[0] - d01[0],
+                                                                      ph[1] - d01[1], 0.0625f, false);
+            const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo01, ph[2] - d23[0],
+                                                                    ph[3] - d23[1], 0.0625f, true);
+            // tokens 8 a + 4 g .. +3: half a / 2, byte 8 (a % 2) + 4 g
+            const int off_b = (a >> 1) * 32 * 16 + 8 * (a & 1) + 4 * g;
+            *reinterpret_cast<uint32_t*>(pw + off_b) = hi;
+            *reinterpret_cast<v2s*>(pw + 2 * 32 * 16 + off_b) = lo;
+          }
+          issue(t + 2, 2, 5);
+          zs += __shfl_xor(zs, 32, 64);
+          if (g == 0) {
+            sm.bmax[pb][ht_d][blk][n] = mi;
+            sm.bsum[pb][ht_d][blk][n] = zs * (1.0f / 256.0f);
+          }
+        }
+      } else {
+        if (t < n_tiles) issue(t + 2, 0, 5);
+        if (t > 0) values_of(t - 1, n, g);
       }
-      *reinterpret_cast<v4i*>(dst + 16 * i) = c;
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < n_tiles) {
+        // ---- values of tile t into registers (A operand of the next step's PV)
+        const int vgrp = lane_t >> 4, vli = lane_t & 15;
+        const uint8_t* vbase = tile + (2 * dt0 + (vgrp & 1)) * 1024 +
+                               (16 * (vgrp >> 1) + (vli >> 1)) * 16 + 8 * (vli & 1);
+        read_values<ND>((uint32_t)(uintptr_t)(DSA_LDS const uint8_t*)vbase, vb);
+      }
     }
-    if (part == 0) qsc[h] = ldexpf(1.0f, e);
-  }
-  const int ht = wave >> 1;  // head tile: heads 32*ht .. +31
-  const int hf = wave & 1;   // token half of each tile for the logits, value-dim half for O
-  const uint8_t* qrow = q8s + (32 * ht + n) * kRowStride + 32 * g;
-  v16f acc[8];  // O[32 heads][256 dims] of this wave; acc[dt] covers dims 256*hf + 32*dt .. +31
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = v16f{};
-  float m_run = -INFINITY;  // running max (log2 units) of head n, identical in both waves
-  float z_run = 0.f;        // this lane's share of the running sum of head n
-  bool started = false;
-  __syncthreads();  // barrier 1
-  const float mult = qsc[32 * ht + n] * lat_scale * sm_scale * kLog2e;
+    // the zero-row gathers past the split may still be in flight: every wave waits for its
+    // own, and the barrier below for everyone's, before the ring holds the output
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const int grp = lane >> 4, li = lane & 15;
-  // MFMA row n -> tile token 32*((n>>2)&1) + 16*hf + 4*(n>>3) + (n&3)
-  const int tok = 32 * ((n >> 2) & 1) + 16 * hf + 4 * (n >> 3) + (n & 3);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const uint8_t* tile = lat[buf];
-    const uint64_t vm = valid_mask[buf];
-    // ---- logits of this wave's token half: lane holds head n, tokens 32*g + 16*hf + i
-    float x[16];
-    float mx = -INFINITY;
-    if (vm != 0ull) {
-      const uint8_t* arow = tile + tok * kRowStride + 32 * g;
-      v16f d = {};
-      v4i a0 = *reinterpret_cast<const v4i*>(arow);
-      v4i a1 = *reinterpret_cast<const v4i*>(arow + 16);
-      v4i b0 = *reinterpret_cast<const v4i*>(qrow);
-      v4i b1 = *reinterpret_cast<const v4i*>(qrow + 16);
+    // ---------------------------------------------------------------- finalize
+    // softmax sum of head 32 ht + n: both block shares; values are latent_scale * L8.  Lane
+    // (n, g) owns head n of each accumulator tile, dims 8 a + 4 g .. +3 in registers 4 a ..
+    // 4 a + 3.  The 16-bit outputs (bf16 O, or fp16 O / latent_scale partials) are staged in
+    // the ring as [96 heads][512 dims] (16-byte chunks swizzled within a head's row) and leave
+    // with 16-byte stores; fp32 partials are stored directly.
+    lds_barrier();  // the ring is free: no wave reads it any more and every gather has landed
+    uint8_t* const ostage = &sm.lat[0][0];
+    // one branch on the output mode, outside the unrolled stores
+    auto emit = [&](auto mode_tag) {
+      constexpr int M = decltype(mode_tag)::value;
 #pragma unroll
-      for (int kb = 0; kb < 9; ++kb) {
-        const v8i A = v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        const v8i B = v8i{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        const int nx = kb < 8 ? 64 * (kb + 1) : 64 * kb;
-        a0 = *reinterpret_cast<const v4i*>(arow + nx);
-        a1 = *reinterpret_cast<const v4i*>(arow + nx + 16);
-        b0 = *reinterpret_cast<const v4i*>(qrow + nx);
-        b1 = *reinterpret_cast<const v4i*>(qrow + nx + 16);
-        d = mfma_32x32x64_fp8(A, B, d);
-      }
+      for (int hh = 0; hh < NH; ++hh) {
+        const int h = 32 * (ht0 + hh) + n;
+        const float z = z_run[hh] + __shfl_xor(z_run[hh], 32, 64);
+        const bool empty = !(z > 0.f);
+        const float f = empty ? 0.f : (M == kPartF16 ? 1.0f : lat_scale) / z;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tk = 32 * g + 16 * hf + i;
-        x[i] = ((vm >> tk) & 1ull) ? d[i] * mult : -INFINITY;
-        mx = fmaxf(mx, x[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (g == 0) xmax[ht][hf][n] = mx;
-    }
-    __syncthreads();
-    if (vm != 0ull) {
-      mx = fmaxf(mx, xmax[ht][hf ^ 1][n]);  // the tile max of head n, same in both waves
-      if (!started) {
-        m_run = mx;
-        started = true;
-      } else if (__ballot(mx > m_run + kTau) != 0ull) {
-        const float m_new = fmaxf(m_run, mx);
-        const float f = exp2f(m_run - m_new);
-        m_run = m_new;
-        z_run *= f;
-        if (g == 0) xfer[wave][n] = f;
-        wave_lds_sync();
-        // accumulator register i holds head 8*(i/4) + 4*g + i%4
-        float fr[16];
+        for (int dd = 0; dd < ND; ++dd) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const v4f v = *reinterpret_cast<const v4f*>(&xfer[wave][8 * a + 4 * g]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) fr[4 * a + c] = v[c];
+          for (int a = 0; a < 4; ++a) {
+            const int d = 32 * (dt0 + dd) + 8 * a + 4 * g;
+            const v16f& o = acc[hh][dd];
+            const float v0 = o[4 * a] * f, v1 = o[4 * a + 1] * f, v2 = o[4 * a + 2] * f,
+                        v3 = o[4 * a + 3] * f;
+            if constexpr (M == kPartF32) {
+              float* op = static_cast<float*>(o_part) + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
+              *reinterpret_cast<v4f*>(op + (int64_t)h * kVDim + d) = v4f{v0, v1, v2, v3};
+            } else {
+              v2i w;
+              w[0] = (int)(M == kDirect ? pack_bf16(v0, v1) : pack_f16(v0, v1));
+              w[1] = (int)(M == kDirect ? pack_bf16(v2, v3) : pack_f16(v2, v3));
+              // 16-byte chunk (d / 8) of head h's 1 KB row sits at chunk (d / 8) ^ (h % 32):
+              // the 32 heads of one store then fall on distinct banks
+              *reinterpret_cast<v2i*>(ostage + h * (2 * kVDim) + 16 * ((d >> 3) ^ n) + 8 * g) = w;
+            }
+          }
         }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[dt][i] *= fr[i];
-        wave_lds_sync();
-      }
-      // ---- probabilities of this half -> two E4M3 terms (hi = E4M3(p), lo = E4M3(p - hi)),
-      // stored as bytes 32*g + 16*hf + i of head n's row
-      v4i phi, plo;
-      float zsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float p4[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float p = exp2f(x[4 * j + c] - m_run);  // x = -inf -> 0
-          zsum += p;
-          p4[c] = p * kPScale;
+        if (DUTY && blk == 0 && g == 0) {  // one wave per head tile writes the LSE
+          const float lse_h = empty ? -INFINITY : ((float)m_ref[hh] + log2f(z)) * kLn2;
+          if constexpr (M == kDirect) lse_out[(int64_t)row * kMlaHeads + h] = lse_h;
+          else lse_part[((int64_t)s * n_q + row) * kMlaHeads + h] = lse_h;
         }
-        const uint32_t hi = cvt4_e4m3(p4[0], p4[1], p4[2], p4[3]);
-        const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-        const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-        phi[j] = (int)hi;
-        plo[j] = (int)cvt4_e4m3(p4[0] - d01[0], p4[1] - d01[1], p4[2] - d23[0], p4[3] - d23[1]);
       }
-      z_run += zsum;
-      *reinterpret_cast<v4i*>(&pbuf[ht][0][n][32 * g + 16 * hf]) = phi;
-      *reinterpret_cast<v4i*>(&pbuf[ht][1][n][32 * g + 16 * hf]) = plo;
-    }
-    __syncthreads();
-    if (vm != 0ull) {
-      // ---- A operands: head n, tokens 32*g .. +31 of the tile (both halves)
-      const v4i h0 = *reinterpret_cast<const v4i*>(&pbuf[ht][0][n][32 * g]);
-      const v4i h1 = *reinterpret_cast<const v4i*>(&pbuf[ht][0][n][32 * g + 16]);
-      const v4i l0 = *reinterpret_cast<const v4i*>(&pbuf[ht][1][n][32 * g]);
-      const v4i l1 = *reinterpret_cast<const v4i*>(&pbuf[ht][1][n][32 * g + 16]);
-      const v8i pa = v8i{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-      const v8i pl = v8i{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      // ---- O += P8 * V8: B operand via LDS transpose reads.  In each 16-lane group,
-      // lanes 2r, 2r+1 address the two 8-byte halves of token row r (8 rows), and lane i
-      // then receives dim (group base + i) of those 8 tokens.
-      const uint8_t* vb = tile + (32 * (grp >> 1) + (li >> 1)) * kRowStride + 256 * hf +
-                          16 * (grp & 1) + 8 * (li & 1);
+      if constexpr (M != kPartF32) {
+        lds_barrier();
+        uint8_t* dst = reinterpret_cast<uint8_t*>(
+            M == kDirect ? out_bf16 + (int64_t)row * kMlaHeads * kVDim
+                         : static_cast<uint16_t*>(o_part) + ((int64_t)s * n_q + row) * kMlaHeads * kVDim);
+        constexpr int kPieces = kMlaHeads * kVDim * 2 / 16;  // 6,144 16-byte pieces
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        v8i B;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (DSA_LDS v2i*)(vb + 8 * jj * kRowStride + 32 * dt));
-          B[2 * jj] = r2[0];
-          B[2 * jj + 1] = r2[1];
+        for (int i = 0; i < kPieces / kThreads; ++i) {
+          const int c = i * kThreads + (int)threadIdx.x;
+          const int hc = c >> 6, ch = c & 63;  // head, 16-byte chunk of its row
+          *reinterpret_cast<v4i*>(dst + 16 * c) =
+              *reinterpret_cast<const v4i*>(ostage + hc * (2 * kVDim) + 16 * (ch ^ (hc & 31)));
         }
-        acc[dt] = mfma_32x32x64_fp8(pa, B, acc[dt]);
-        acc[dt] = mfma_32x32x64_fp8(pl, B, acc[dt]);
       }
-    }
-    // (no barrier here: the next tile's maxima and probabilities are written only after
-    // its barrier A, which every wave reaches after this tile's values product)
-  }
-  __syncthreads();  // after the last tile
-
-  // ------------------------------------------------------------------ finalize
-  // each wave summed the probabilities of its own token halves: add the partner's
-  const float zl = z_run + __shfl_xor(z_run, 32, 64);
-  if (g == 0) xfer[wave][n] = zl;
-  __syncthreads();
-  const float z = zl + xfer[wave ^ 1][n];
-  const bool empty = !(z > 0.f);
-  const float lse = empty ? -INFINITY : (m_run + log2f(z)) * kLn2;
-  // values are latent_scale * L8; probabilities entered the product scaled by 2^4
-  const float invz = empty ? 0.f : lat_scale / (z * kPScale);
-  __syncthreads();
-  if (g == 0) xfer[wave][n] = invz;
-  wave_lds_sync();
-  float fr[16];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const v4f v = *reinterpret_cast<const v4f*>(&xfer[wave][8 * a + 4 * g]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) fr[4 * a + c] = v[c];
-  }
-  const int head0 = 32 * ht;
-  const int dim0 = 256 * hf + n;
-  if (mode == kDirect) {
-    uint16_t* ob = out_bf16 + (int64_t)row * kMlaHeads * kVDim;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = head0 + 8 * (i / 4) + 4 * g + (i % 4);
-        uint32_t u = __float_as_uint(acc[dt][i] * fr[i]);  // round to nearest even bf16
-        u += 0x7FFFu + ((u >> 16) & 1u);
-        ob[(int64_t)h * kVDim + dim0 + 32 * dt] = (uint16_t)(u >> 16);
-      }
-    if (g == 0 && hf == 0) lse_out[(int64_t)row * kMlaHeads + head0 + n] = lse;
-  } else if (mode == kPartF32) {
-    float* op = static_cast<float*>(o_part) + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = head0 + 8 * (i / 4) + 4 * g + (i % 4);
-        op[(int64_t)h * kVDim + dim0 + 32 * dt] = acc[dt][i] * fr[i];
-      }
-    if (g == 0 && hf == 0) lse_part[((int64_t)s * n_q + row) * kMlaHeads + head0 + n] = lse;
-  } else {
-    _Float16* op = static_cast<_Float16*>(o_part) + ((int64_t)s * n_q + row) * kMlaHeads * kVDim;
-    const float unscale = 1.0f / lat_scale;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = head0 + 8 * (i / 4) + 4 * g + (i % 4);
-        op[(int64_t)h * kVDim + dim0 + 32 * dt] = (_Float16)(acc[dt][i] * (fr[i] * unscale));
-      }
-    if (g == 0 && hf == 0) lse_part[((int64_t)s * n_q + row) * kMlaHeads + head0 + n] = lse;
-  }
+    };
+    if (mode == kDirect)
+      emit(std::integral_constant<int, kDirect>{});
+    else if (mode == kPartF16)
+      emit(std::integral_constant<int, kPartF16>{});
+    else
+      emit(std::integral_constant<int, kPartF32>{});
+  };
+  if (wave < kDutyWaves)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 }  // namespace
