@@ -249,6 +249,10 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="run stage 2 as both top-k passes instead of taking the indexer's "
                          "per-chunk candidates")
+    ap.add_argument("--query-prep", choices=("fused", "inline", "first", "side"), default=None,
+                    help="where the MLA query is quantised: inside the attention kernel "
+                         "(default), by the indexer's launch, by its own launch ahead of stage 1, "
+                         "or on a side stream during stages 1-2")
     ap.add_argument("--query-side-stream", action="store_true",
                     help="quantise the MLA query on a side stream during stages 1-2 instead of "
                          "inside the attention kernel")
@@ -279,6 +283,7 @@ def main():
     batch = synth.make_batch(wl, "cuda")
     step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
                           query_on_side_stream=args.query_side_stream,
+                          query_prep=args.query_prep,
                           select_in_attention=not (args.separate_topk or args.unfused),
                           store_scores=True if (args.store_scores or args.unfused) else None,
                           key_format=wl.key_format,
@@ -299,13 +304,15 @@ def main():
         # step starts at evs[0] on the main stream, which the side stream waits for
         if evs:
             evs[0].record(stream)
+        if step.query_prep == "first":
+            step.prepare_query(batch.q_mla, stream=stream)
         if step.query_on_side_stream:
             step._ev_start.record(stream)
             step.side.wait_event(step._ev_start)
             step.prepare_query(batch.q_mla, stream=step.side)
             step._ev_query.record(step.side)
         step.index(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
-                   batch.block_table, max(wl.q_per_seq), stream)
+                   batch.block_table, max(wl.q_per_seq), stream, q_mla=batch.q_mla)
         if evs:
             evs[1].record(stream)
         if not step.select_in_attention:
@@ -415,6 +422,7 @@ def main():
                    "indexer_emits_topk_candidates": not args.unfused,
                    "scores_stored": step.store_scores,
                    "topk_final_in_attention": step.select_in_attention,
+                   "mla_query_prep": step.query_prep,
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),
         "us_per_layer_median": round(med, 2),

@@ -8,6 +8,7 @@
  *
  *   dsa_index_score       stage 1  indexer scores           ("What changed in Kimi K3.1 Pro")
  *   dsa_index_score_mxfp4 stage 1 on MXFP4 index keys        ("Native MXFP4 indexer")
+ *   dsa_index_score_quantize_q  stage 1 plus stage 3's query quantisation in one launch
  *   dsa_topk              stage 2  exact top-k select       ("Exact top-k merge with ~10x less traffic")
  *                         Stage 1 can also emit each 256-token group's top-k candidates while
  *                         its scores are on chip; stage 2 then only runs its final pass (the
@@ -144,6 +145,30 @@ dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_
                                  const int32_t* block_table, int32_t bt_stride, float* scores,
                                  int64_t score_stride, int32_t cand_k, void* cand_workspace,
                                  size_t cand_workspace_bytes, void* stream);
+
+/*
+ * Stage 1 with the MLA query's quantisation in the same launch: exactly
+ * dsa_index_score (key_format 0) or dsa_index_score_mxfp4 (key_format 1) with the same
+ * arguments, plus dsa_quantize_q(n_q, 96, 576, q_mla_bf16, q8_mla, q_mla_scale) -- the
+ * E4M3 codes and per-(row, head) power-of-two scales that stage 3 applies to the query
+ * ("Sparse attention cuts long-context decode bandwidth": the 576-dim FP8 product over the
+ * selected latents), bitwise identical to that call.  One more workgroup per request and
+ * row group does it while the keys stream, so a decode step needs no launch of its own
+ * for it; stage 3 then takes q8_mla / q_mla_scale as a prepared query.
+ *   q_mla_bf16: bf16 [n_q][96][576], 16-byte aligned (read only).
+ *   q8_mla: uint8 [n_q][96][576], 16-byte aligned; q_mla_scale: fp32 [n_q][96] (written).
+ * Errors: those of dsa_index_score; DSA_ERR_UNSUPPORTED for another key_format;
+ * DSA_ERR_INVALID_ARG for a null or misaligned query buffer.
+ */
+dsa_status dsa_index_score_quantize_q(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                                      int32_t max_q_per_seq, const int32_t* cu_q,
+                                      const int32_t* seq_lens, const void* q_bf16,
+                                      const float* head_w, const void* key_pages,
+                                      int64_t key_page_stride, int32_t key_format,
+                                      const int32_t* block_table, int32_t bt_stride, float* scores,
+                                      int64_t score_stride, int32_t cand_k, void* cand_workspace,
+                                      size_t cand_workspace_bytes, const void* q_mla_bf16,
+                                      uint8_t* q8_mla, float* q_mla_scale, void* stream);
 
 /*
  * Stage 2 — exact top-k over each row's visible scores (tokens 0..position).

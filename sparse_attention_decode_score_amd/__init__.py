@@ -49,6 +49,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_index_score.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32,
                                       _P, _I64, _I32, _P, _SZ, _P]
         L.dsa_index_score_mxfp4.argtypes = L.dsa_index_score.argtypes
+        L.dsa_index_score_quantize_q.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64,
+                                                 _I32, _P, _I32, _P, _I64, _I32, _P, _SZ, _P, _P,
+                                                 _P, _P]
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
@@ -69,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_validate_slots.argtypes = [_I32, _P, _I64]
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
-        for f in ("dsa_index_score", "dsa_index_score_mxfp4", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
+        for f in ("dsa_index_score", "dsa_index_score_mxfp4", "dsa_index_score_quantize_q", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
                   "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append", "dsa_validate_batch",
                   "dsa_validate_slots", "dsa_sparse_mla_decode_noalloc"):
             getattr(L, f).restype = ctypes.c_int
@@ -156,13 +159,14 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
                     scores: Optional[torch.Tensor], *, max_seq_len: int, max_q_per_seq: int,
                     key_page_stride: Optional[int] = None, cand_k: int = 0,
                     cand_workspace: Optional[torch.Tensor] = None, key_format: str = "e4m3",
-                    stream=None) -> None:
+                    mla_query: Optional[tuple] = None, stream=None) -> None:
     """Indexer scores into scores [n_q, score_stride] (fp32); with cand_workspace, also the
     per-chunk top-k candidates for a top-k of cand_k (consumed by dsa_topk with
     from_candidates=True).  scores=None with cand_workspace: candidates only (no scores
     stored; pass rescore=(q_idx, head_w, key_pages) and the same key_format to the final
     top-k pass).  key_format "mxfp4": the key cache holds MXFP4 keys
-    (dsa_index_score_mxfp4)."""
+    (dsa_index_score_mxfp4).  mla_query=(q_mla, codes, scales): the same launch also
+    writes dsa_quantize_q(q_mla, codes, scales) (dsa_index_score_quantize_q)."""
     if key_format not in ("e4m3", "mxfp4"):
         raise ValueError(f"key_format must be 'e4m3' or 'mxfp4' (got {key_format!r})")
     num_seqs = seq_lens.shape[0]
@@ -179,6 +183,19 @@ def dsa_index_score(cu_q: torch.Tensor, seq_lens: torch.Tensor, q_idx: torch.Ten
     stride = key_page_stride if key_page_stride is not None else key_pages.stride(0) * key_pages.element_size()
     if cand_workspace is not None:
         _expect(cand_workspace, "cand_workspace", torch.uint8)
+    if mla_query is not None:
+        q_mla, codes, scales = mla_query
+        _expect(q_mla, "q_mla", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+        _expect(codes, "codes", torch.uint8, (n_q, MLA_HEADS, LATENT_DIM))
+        _expect(scales, "scales", torch.float32, (n_q, MLA_HEADS))
+        _check(lib().dsa_index_score_quantize_q(
+            num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q), _ptr(seq_lens),
+            _ptr(q_idx), _ptr(head_w), _ptr(key_pages), int(stride), _KEY_FORMATS[key_format],
+            _ptr(block_table), block_table.shape[1], _ptr(scores),
+            scores.shape[1] if scores is not None else 0, int(cand_k), _ptr(cand_workspace),
+            cand_workspace.numel() if cand_workspace is not None else 0, _ptr(q_mla),
+            _ptr(codes), _ptr(scales), _stream(stream)))
+        return
     fn = lib().dsa_index_score_mxfp4 if key_format == "mxfp4" else lib().dsa_index_score
     _check(fn(num_seqs, n_q, int(max_seq_len), int(max_q_per_seq), _ptr(cu_q),
                                  _ptr(seq_lens), _ptr(q_idx), _ptr(head_w), _ptr(key_pages),
@@ -413,14 +430,18 @@ class DecodeStep:
     indexer also emits the top-k candidates (fused) and stores no scores (store_scores=False:
     the final pass recomputes the few groups it must re-read), and the final top-k pass runs
     inside the attention kernel (select_in_attention: two launches, plus the split merge);
-    otherwise stage 2 is its own call.  With query_on_side_stream the MLA query is quantised on a side
-    stream while stages 1 and 2 run.
+    otherwise stage 2 is its own call.  The MLA query is quantised inside the attention call
+    (query_prep="inline", the default: the kernel stages the bf16 query in LDS while its
+    selection runs), by the indexer's launch ("fused": one more workgroup per request there),
+    by its own launch ahead of stage 1 ("first"), or on a side stream while stages 1 and 2
+    run ("side"; query_on_side_stream=True means the same).
     """
 
     def __init__(self, n_q: int, max_seq_len: int, k: int, num_splits: int, device="cuda",
                  fused: bool = True, query_on_side_stream: bool = False,
                  select_in_attention: Optional[bool] = None, write_selection: bool = True,
-                 store_scores: Optional[bool] = None, key_format: str = "e4m3"):
+                 store_scores: Optional[bool] = None, key_format: str = "e4m3",
+                 query_prep: Optional[str] = None):
         if key_format not in _KEY_FORMATS:
             raise ValueError(f"key_format must be 'e4m3' or 'mxfp4' (got {key_format!r})")
         self.key_format = key_format
@@ -441,7 +462,14 @@ class DecodeStep:
         self.n_q, self.max_seq_len, self.k, self.num_splits = n_q, max_seq_len, k, num_splits
         self.fused = fused
         self.select_in_attention = select_in_attention
-        self.query_on_side_stream = query_on_side_stream
+        if query_prep is None:
+            query_prep = "side" if query_on_side_stream else "inline"
+        if query_prep not in ("fused", "inline", "first", "side"):
+            raise ValueError("query_prep must be 'fused', 'inline', 'first' or 'side' "
+                             f"(got {query_prep!r})")
+        self.query_prep = query_prep
+        self.query_on_side_stream = query_prep == "side"
+        self.query_prepared = query_prep != "inline"
         dev = torch.device(device)
         self.scores = torch.empty((n_q, max_seq_len), dtype=torch.float32, device=dev)
         self.topk_idx = torch.empty((n_q, k), dtype=torch.int32, device=dev)
@@ -457,14 +485,20 @@ class DecodeStep:
         self._ev_query = torch.cuda.Event()
 
     def index(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq,
-              stream=None):
-        """Stage 1 (with the fused first top-k pass when self.fused)."""
+              stream=None, q_mla=None):
+        """Stage 1 (with the fused first top-k pass when self.fused); with query_prep
+        "fused", also the MLA query's quantisation (q_mla is then required)."""
         self._rescore = None if self.store_scores else (q_idx, head_w, key_pages)
+        mla_query = None
+        if self.query_prep == "fused":
+            if q_mla is None:
+                raise ValueError("query_prep='fused' quantises the MLA query in stage 1: pass q_mla")
+            mla_query = (q_mla, self.q8, self.q_scale)
         dsa_index_score(cu_q, seq_lens, q_idx, head_w, key_pages, block_table,
                         self.scores if self.store_scores else None,
                         max_seq_len=self.max_seq_len, max_q_per_seq=max_q_per_seq,
                         cand_k=self.k, cand_workspace=self.workspace if self.fused else None,
-                        key_format=self.key_format, stream=stream)
+                        key_format=self.key_format, mla_query=mla_query, stream=stream)
 
     def select(self, cu_q, seq_lens, block_table, stream=None):
         """Stage 2."""
@@ -478,8 +512,8 @@ class DecodeStep:
 
     def attend(self, q_mla, latent_pages, latent_scale, softmax_scale, stream=None):
         """Stages 3 and 4: on the query prepared by prepare_query when the step quantises it
-        on the side stream, else on q_mla (quantised inside the call)."""
-        if self.query_on_side_stream:
+        beforehand, else on q_mla (quantised inside the call)."""
+        if self.query_prepared:
             dsa_sparse_mla_decode(None, latent_pages, latent_scale, self.topk_slot, softmax_scale,
                                   self.num_splits, out=self.out, lse=self.lse, q8=self.q8,
                                   q_scale=self.q_scale, workspace=self.mla_workspace,
@@ -493,7 +527,7 @@ class DecodeStep:
     def select_attend(self, cu_q, seq_lens, block_table, q_mla, latent_pages, latent_scale,
                       softmax_scale, stream=None):
         """Stages 2-4 in one launch (the final top-k pass inside the attention kernel)."""
-        prepared = self.query_on_side_stream
+        prepared = self.query_prepared
         dsa_topk_sparse_mla(cu_q, seq_lens, self.scores, self.k, block_table, self.workspace,
                             None if prepared else q_mla, latent_pages, latent_scale,
                             softmax_scale, self.num_splits, max_seq_len=self.max_seq_len,
@@ -509,12 +543,15 @@ class DecodeStep:
     def run(self, cu_q, seq_lens, q_idx, head_w, key_pages, block_table, q_mla, latent_pages,
             latent_scale, softmax_scale, max_q_per_seq, stream=None):
         main = torch.cuda.current_stream() if stream is None else stream
+        if self.query_prep == "first":
+            self.prepare_query(q_mla, stream=main)
         if self.query_on_side_stream:
             self._ev_start.record(main)
             self.side.wait_event(self._ev_start)
             self.prepare_query(q_mla, stream=self.side)
             self._ev_query.record(self.side)
-        self.index(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq, main)
+        self.index(cu_q, seq_lens, q_idx, head_w, key_pages, block_table, max_q_per_seq, main,
+                   q_mla=q_mla)
         if self.select_in_attention:
             if self.query_on_side_stream:
                 main.wait_event(self._ev_query)

@@ -141,7 +141,9 @@ dsa_status index_score_checked(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                                const void* key_pages, int64_t key_page_stride,
                                const int32_t* block_table, int32_t bt_stride, float* scores,
                                int64_t score_stride, int32_t cand_k, void* cand_workspace,
-                               size_t cand_workspace_bytes, bool mxfp4, void* stream) {
+                               size_t cand_workspace_bytes, bool mxfp4, void* stream,
+                               const char* name,
+                               dsa::MlaQueryPrep prep = dsa::MlaQueryPrep{nullptr, nullptr, nullptr}) {
   dsa_status st = check_batch(num_seqs, n_q, max_seq_len, cu_q, seq_lens);
   if (st != DSA_OK) return st;
   DSA_REQUIRE(max_q_per_seq >= 1 && max_q_per_seq <= n_q,
@@ -180,8 +182,9 @@ dsa_status index_score_checked(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                                           static_cast<const uint16_t*>(q_bf16), head_w,
                                           static_cast<const uint8_t*>(key_pages), key_page_stride,
                                           block_table, bt_stride, scores, score_stride, cand_k,
-                                          cand_workspace, mxfp4, static_cast<hipStream_t>(stream)),
-                  mxfp4 ? "dsa_index_score_mxfp4" : "dsa_index_score");
+                                          cand_workspace, mxfp4, static_cast<hipStream_t>(stream),
+                                          prep),
+                  name);
 }
 
 }  // namespace
@@ -195,7 +198,7 @@ dsa_status dsa_index_score(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
   return index_score_checked(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens, q_bf16,
                              head_w, key_pages, key_page_stride, block_table, bt_stride, scores,
                              score_stride, cand_k, cand_workspace, cand_workspace_bytes, false,
-                             stream);
+                             stream, "dsa_index_score");
 }
 
 dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
@@ -208,7 +211,30 @@ dsa_status dsa_index_score_mxfp4(int32_t num_seqs, int32_t n_q, int32_t max_seq_
   return index_score_checked(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens, q_bf16,
                              head_w, key_pages, key_page_stride, block_table, bt_stride, scores,
                              score_stride, cand_k, cand_workspace, cand_workspace_bytes, true,
-                             stream);
+                             stream, "dsa_index_score_mxfp4");
+}
+
+dsa_status dsa_index_score_quantize_q(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,
+                                      int32_t max_q_per_seq, const int32_t* cu_q,
+                                      const int32_t* seq_lens, const void* q_bf16,
+                                      const float* head_w, const void* key_pages,
+                                      int64_t key_page_stride, int32_t key_format,
+                                      const int32_t* block_table, int32_t bt_stride, float* scores,
+                                      int64_t score_stride, int32_t cand_k, void* cand_workspace,
+                                      size_t cand_workspace_bytes, const void* q_mla_bf16,
+                                      uint8_t* q8_mla, float* q_mla_scale, void* stream) {
+  if (key_format != 0 && key_format != 1)
+    return fail(DSA_ERR_UNSUPPORTED, "key_format must be 0 (E4M3) or 1 (MXFP4) (got %d)", key_format);
+  DSA_REQUIRE(q_mla_bf16 && q8_mla && q_mla_scale,
+              "q_mla_bf16, q8_mla and q_mla_scale must be non-null");
+  DSA_REQUIRE(aligned(q_mla_bf16, 16) && aligned(q8_mla, 16),
+              "q_mla_bf16 and q8_mla must be 16-byte aligned");
+  return index_score_checked(num_seqs, n_q, max_seq_len, max_q_per_seq, cu_q, seq_lens, q_bf16,
+                             head_w, key_pages, key_page_stride, block_table, bt_stride, scores,
+                             score_stride, cand_k, cand_workspace, cand_workspace_bytes,
+                             key_format == 1, stream, "dsa_index_score_quantize_q",
+                             dsa::MlaQueryPrep{static_cast<const uint16_t*>(q_mla_bf16), q8_mla,
+                                               q_mla_scale});
 }
 
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k) {

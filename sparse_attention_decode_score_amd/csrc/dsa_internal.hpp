@@ -45,15 +45,24 @@ hipError_t launch_topk_final(int num_seqs, int n_q, const int32_t* cu_q, const i
 hipError_t launch_quantize_q(int rows, int heads, int dim, const uint16_t* q, uint8_t* codes,
                              float* scales, hipStream_t st);
 
+// The MLA query's E4M3 quantisation carried by an indexer launch: codes [n_q][96][576] and
+// scales [n_q][96], bitwise what launch_quantize_q(n_q, 96, 576, q, ...) writes.
+struct MlaQueryPrep {
+  const uint16_t* q;  // bf16 [n_q][96][576]; nullptr: no preparation
+  uint8_t* codes;
+  float* scales;
+};
+
 // topk_ws == nullptr: scores only.  Otherwise the kernel also writes every 256-token group's
 // top-k candidates for a top-k of k into topk_ws (see topk_buffers).  mxfp4: the key cache
-// holds MXFP4 keys (4,352-byte pages) instead of E4M3 keys with an fp32 scale.
+// holds MXFP4 keys (4,352-byte pages) instead of E4M3 keys with an fp32 scale.  prep.q set:
+// one more workgroup per request and row group quantises those rows' MLA query.
 hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_per_seq,
                               const int32_t* cu_q, const int32_t* seq_lens, const uint16_t* q,
                               const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
                               const int32_t* block_table, int bt_stride, float* scores,
                               int64_t score_stride, int k, void* topk_ws, bool mxfp4,
-                              hipStream_t st);
+                              hipStream_t st, MlaQueryPrep prep = MlaQueryPrep{nullptr, nullptr, nullptr});
 
 hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu_q,
                        const int32_t* seq_lens, const float* scores, int64_t score_stride, int k,

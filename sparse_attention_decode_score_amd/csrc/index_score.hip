@@ -59,6 +59,63 @@ struct CandOut {
   int k;
 };
 
+// E4M3 codes and power-of-two scale of one (row, head) of dim = 64 * PPL values: 8
+// consecutive lanes hold the head, lane i of the 8 converting dims PPL*8*i .. +PPL*8-1 from
+// raw (16-byte bf16 loads); the head's absmax is reduced across its 8 lanes.  live = false:
+// the lanes take part in the reduction only.
+template <int PPL>
+__device__ __forceinline__ void quantize_head(const v4i (&raw)[PPL], uint8_t* codes, float* scales,
+                                              int64_t rh, bool live) {
+  constexpr int dim = PPL * 64;
+  const int lane8 = threadIdx.x & 7;
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < PPL; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      am = fmaxf(am, fmaxf(fabsf(bf16_lo((uint32_t)raw[i][j])), fabsf(bf16_hi((uint32_t)raw[i][j]))));
+  am = fmaxf(am, __shfl_xor(am, 1, 64));
+  am = fmaxf(am, __shfl_xor(am, 2, 64));
+  am = fmaxf(am, __shfl_xor(am, 4, 64));
+  const int e = pow2_scale_exp(am);
+  const float inv = ldexpf(1.0f, -e);
+  if (!live) return;
+  const int64_t base = rh * dim + lane8 * (PPL * 8);
+#pragma unroll
+  for (int i = 0; i < PPL; ++i) {
+    v2i c;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w0 = (uint32_t)raw[i][2 * j], w1 = (uint32_t)raw[i][2 * j + 1];
+      c[j] = (int)cvt4_e4m3(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
+                            bf16_hi(w1) * inv);
+    }
+    *reinterpret_cast<v2i*>(codes + base + 8 * i) = c;
+  }
+  if (lane8 == 0) scales[rh] = ldexpf(1.0f, e);
+}
+
+// The MLA query rows r0 .. r0+nr-1 (96 heads x 576 dims each) quantised by one 256-thread
+// workgroup, one row (three passes of 32 heads, all loads first) at a time.
+__device__ __forceinline__ void quantize_mla_rows(const MlaQueryPrep& pp, int r0, int nr) {
+  constexpr int PPL = kLatDim / 64;  // 9
+  const int hs = threadIdx.x >> 3, lane8 = threadIdx.x & 7;
+#pragma unroll 1
+  for (int r = r0; r < r0 + nr; ++r) {
+    v4i raw[3][PPL];
+#pragma unroll
+    for (int ps = 0; ps < 3; ++ps) {
+      const int64_t rh = (int64_t)r * kMlaHeads + 32 * ps + hs;
+      const uint16_t* src = pp.q + rh * kLatDim + lane8 * (PPL * 8);
+#pragma unroll
+      for (int i = 0; i < PPL; ++i) raw[ps][i] = *reinterpret_cast<const v4i*>(src + 8 * i);
+    }
+#pragma unroll
+    for (int ps = 0; ps < 3; ++ps)
+      quantize_head<PPL>(raw[ps], pp.codes, pp.scales, (int64_t)r * kMlaHeads + 32 * ps + hs, true);
+  }
+}
+
 // Why the structure below: the key loads of a wave's ring are issued unconditionally
 // (page indices past the segment are clamped to a visible page, and the last group issues
 // no loads past itself), and nothing is stored to global memory until every load has
@@ -72,7 +129,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ head_w,
     const uint8_t* __restrict__ key_pages, int64_t page_stride,
     const int32_t* __restrict__ block_table, int bt_stride, float* __restrict__ scores,
-    int64_t score_stride, int groups_per_wave, CandOut cand) {
+    int64_t score_stride, int groups_per_wave, CandOut cand, MlaQueryPrep prep) {
   using Cfg = IdxCfg<R>;
   constexpr int NF = Cfg::kInFlight;
   constexpr bool STAGE = Cfg::kStage;
@@ -90,6 +147,10 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   const int r0 = q0 + (int)blockIdx.z * R;
   if (r0 >= q1) return;
   const int nr = min(R, q1 - r0);
+  if (prep.q != nullptr && blockIdx.x == gridDim.x - 1) {  // the extra x slice
+    quantize_mla_rows(prep, r0, nr);
+    return;
+  }
   const int L = seq_lens[b];
   const int n_pages = (L + kPage - 1) / kPage;
   const int p0 = (int)blockIdx.x * kWaves * kGroupPages * G;
@@ -268,30 +329,7 @@ __global__ __launch_bounds__(64) void quantize_q_kernel(const uint16_t* __restri
   v4i raw[PPL];
 #pragma unroll
   for (int i = 0; i < PPL; ++i) raw[i] = *reinterpret_cast<const v4i*>(q + base + 8 * i);
-  float am = 0.f;
-#pragma unroll
-  for (int i = 0; i < PPL; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      am = fmaxf(am, fmaxf(fabsf(bf16_lo((uint32_t)raw[i][j])), fabsf(bf16_hi((uint32_t)raw[i][j]))));
-  am = fmaxf(am, __shfl_xor(am, 1, 64));
-  am = fmaxf(am, __shfl_xor(am, 2, 64));
-  am = fmaxf(am, __shfl_xor(am, 4, 64));
-  const int e = pow2_scale_exp(am);
-  const float inv = ldexpf(1.0f, -e);
-  if (!live) return;
-#pragma unroll
-  for (int i = 0; i < PPL; ++i) {
-    v2i c;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t w0 = (uint32_t)raw[i][2 * j], w1 = (uint32_t)raw[i][2 * j + 1];
-      c[j] = (int)cvt4_e4m3(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv,
-                            bf16_hi(w1) * inv);
-    }
-    *reinterpret_cast<v2i*>(codes + base + 8 * i) = c;
-  }
-  if ((lane & 7) == 0) scales[rh] = ldexpf(1.0f, e);
+  quantize_head<PPL>(raw, codes, scales, rh, live);
 }
 
 }  // namespace
@@ -315,7 +353,7 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
                               const float* head_w, const uint8_t* key_pages, int64_t key_page_stride,
                               const int32_t* block_table, int bt_stride, float* scores,
                               int64_t score_stride, int k, void* topk_ws, bool mxfp4,
-                              hipStream_t st) {
+                              hipStream_t st, MlaQueryPrep prep) {
   const int max_pages = (max_seq_len + kPage - 1) / kPage;
   int R = 8;
   if (max_q_per_seq <= 1) R = 1;
@@ -336,7 +374,9 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
   G = std::min(DSA_INDEX_GROUPS_PER_WAVE, (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1));
 #endif
   const unsigned gx = (unsigned)((max_pages + kWaves * kGroupPages * G - 1) / (kWaves * kGroupPages * G));
-  const dim3 grid(gx, (unsigned)num_seqs, gz), block(256);
+  // with a query preparation, one more x slice of workgroups: the MLA query rows of each
+  // (request, row group)
+  const dim3 grid(gx + (prep.q ? 1u : 0u), (unsigned)num_seqs, gz), block(256);
   CandOut cand{nullptr, nullptr, nullptr, 0, 0, k};
   if (topk_ws) {
     const TopkBuffers t = topk_buffers(topk_ws, n_q, max_seq_len, k);
@@ -347,11 +387,11 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
     if (mxfp4)                                                                                   \
       hipLaunchKernelGGL((index_score_kernel<RR, CC, true>), grid, block, 0, st, cu_q, seq_lens, \
                          q, head_w, key_pages, key_page_stride, block_table, bt_stride, scores,  \
-                         score_stride, G, cand);                                                  \
+                         score_stride, G, cand, prep);                                            \
     else                                                                                         \
       hipLaunchKernelGGL((index_score_kernel<RR, CC, false>), grid, block, 0, st, cu_q,          \
                          seq_lens, q, head_w, key_pages, key_page_stride, block_table, bt_stride, \
-                         scores, score_stride, G, cand);                                          \
+                         scores, score_stride, G, cand, prep);                                    \
   } while (0)
 #define DSA_LAUNCH_R(CC)                 \
   switch (R) {                           \

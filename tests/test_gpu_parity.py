@@ -359,11 +359,12 @@ def test_lse_combine_matches_oracle_with_empty_splits():
 
 
 # ------------------------------------------------------------------------ whole path
-def _end_to_end(wl, rows, num_splits=None):
+def _end_to_end(wl, rows, num_splits=None, query_prep=None):
     S = num_splits or wl.num_splits
-    say("e2e", wl.name, "rows", rows, "S", S)
+    say("e2e", wl.name, "rows", rows, "S", S, "query", query_prep or "default")
     batch = synth.make_batch(wl, DEV)
-    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, key_format=wl.key_format)
+    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, key_format=wl.key_format,
+                          query_prep=query_prep)
     out, lse = step.run(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
                         batch.block_table, batch.q_mla, batch.latent_pool, batch.latent_scale,
                         batch.softmax_scale, max(wl.q_per_seq))
@@ -414,6 +415,15 @@ def test_end_to_end_degenerate_contexts(num_splits):
     wl = synth.custom([1, 2, 63, 64, 65, 2049], [1, 2, 1, 1, 1, 1], topk=2048,
                       num_splits=num_splits, seed=71, name="degenerate")
     _end_to_end(wl, rows=list(range(wl.n_q)))
+
+
+@pytest.mark.parametrize("query_prep", ["fused", "first", "side"])
+def test_end_to_end_with_a_prepared_query(query_prep):
+    # the MLA query quantised by the indexer's launch, by its own launch, or on a side
+    # stream: the attention kernel then reads the prepared codes
+    wl = synth.custom([20000, 9000, 2049], [5, 1, 3], topk=2048, num_splits=4, seed=88,
+                      name="e2e-prepared")
+    _end_to_end(wl, rows=[0, 4, 5, 8], query_prep=query_prep)
 
 
 def test_end_to_end_spec_full_size():
@@ -508,6 +518,48 @@ def test_fused_index_topk_is_bitwise_the_stage_by_stage_path(wl):
     for row, (b, pos) in enumerate(wl.row_positions()):
         assert torch.equal(s1[row, : pos + 1], s2[row, : pos + 1]), row
     assert torch.equal(i1, i2) and torch.equal(t1, t2)
+
+
+@pytest.mark.parametrize("wl", [
+    SMALL[0], SMALL[3], FUSED[4], FUSED[5],
+    synth.custom([5000, 4097], [4, 5], topk=2048, seed=87, name="mx-prep", key_format="mxfp4"),
+], ids=lambda w: w.name)
+def test_index_with_query_prep_is_bitwise_both_calls(wl):
+    """dsa_index_score_quantize_q = dsa_index_score (scores and candidates, bit for bit) +
+    dsa_quantize_q of the MLA query (codes and scales, bit for bit), for row groups of 1, 2,
+    4 and 8 rows per request and both key formats."""
+    say("index+query prep", wl.name)
+    batch = synth.make_batch(wl, DEV)
+    k = wl.topk
+    ws1 = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k))
+    ws2 = dsa.workspace(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, k))
+    s1 = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    s2 = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+    q8_ref = torch.empty((wl.n_q, 96, 576), dtype=torch.uint8, device=DEV)
+    qs_ref = torch.empty((wl.n_q, 96), device=DEV)
+    q8 = torch.full((wl.n_q, 96, 576), 0x5A, dtype=torch.uint8, device=DEV)
+    qs = torch.full((wl.n_q, 96), float("nan"), device=DEV)
+    common = dict(max_seq_len=wl.max_seq_len, max_q_per_seq=max(wl.q_per_seq), cand_k=k,
+                  key_format=wl.key_format)
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, s1, cand_workspace=ws1, **common)
+    dsa.dsa_quantize_q(batch.q_mla, q8_ref, qs_ref)
+    dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                        batch.block_table, s2, cand_workspace=ws2,
+                        mla_query=(batch.q_mla, q8, qs), **common)
+    torch.cuda.synchronize()
+    assert torch.equal(q8, q8_ref) and torch.equal(qs, qs_ref)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        assert torch.equal(s1[row, : pos + 1], s2[row, : pos + 1]), row
+    # the candidates: the final pass over each workspace selects bitwise the same
+    idx1 = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    idx2 = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(batch.cu_q, batch.seq_lens, s1, k, None, idx1, None, ws1,
+                 max_seq_len=wl.max_seq_len, from_candidates=True)
+    dsa.dsa_topk(batch.cu_q, batch.seq_lens, s2, k, None, idx2, None, ws2,
+                 max_seq_len=wl.max_seq_len, from_candidates=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
 
 
 def test_fused_topk_resends_groups_that_hold_the_winners():
