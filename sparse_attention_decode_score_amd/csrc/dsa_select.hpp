@@ -17,10 +17,9 @@ constexpr int kGroupTok = 256;      // tokens per first-pass group (one wave, 4 
 constexpr int kFinalThreads = DSA_FINAL_THREADS;  // threads of the final pass
 constexpr int kFinalWaves = kFinalThreads / 64;
 constexpr int kFinalPerThread = 32;  // at most, in registers
-#ifndef DSA_BUCKET_MAX
-#define DSA_BUCKET_MAX 512
-#endif
-constexpr int kBucketMax = DSA_BUCKET_MAX;  // keys of the last search bucket, finished from LDS
+constexpr int kRadixBits = 8;                  // key bits one pass of the final selection settles
+constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kHistWords = 3 * kRadixBins;     // LDS counters of the final selection
 constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds on chip
 
 // Per-group record of the first selection pass.
@@ -305,25 +304,24 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* red, int&
   return before + x - v;
 }
 
-// Bits of the key a step of the bucket search resolves: every wave but the first counts the
-// bucket against one of the 2^bits - 1 thresholds of the step.
-constexpr int kStepBits = kFinalWaves >= 16 ? 4 : kFinalWaves >= 8 ? 3 : kFinalWaves >= 4 ? 2 : 1;
-
 // Exact top-k (1 <= k <= number of real keys) of up to kFinalThreads * E keys held in
 // registers: thread t holds elements t*E .. t*E+E-1 (keys kv, values vv; elements past the
 // end hold the sentinel key).  Writes the values of the chosen elements, in element order,
 // to out[0..k) (LDS) and returns the k-th element's key and value.
 //
-// K, the k-th largest key, is the largest T with #{keys >= T} >= k.  All real keys share the
-// bits of their maximum and minimum above the highest bit where those differ, so the search
-// starts below it with the bracket [K, K_hi) around every key.  While many keys are in play
-// the whole workgroup settles one bit per exchange; the counts give the number of keys left
-// in [K, K_hi) (#{>= K} - #{>= K_hi}), and once at most kBucketMax remain they are compacted
-// to LDS and every wave loads them: a step then tries 2^kStepBits - 1 thresholds at once
-// (one per wave, #{>= T} = #{>= K_hi} + #{bucket keys >= T}) and settles kStepBits bits per
-// exchange, ending early when one key is left in the bracket (it is the k-th).  Every T
-// tried is >= 1, so sentinels never count.
-// red: 4 * kFinalWaves ints of LDS (16-byte aligned); note: 1 int; bucket: kBucketMax.
+// K, the k-th largest key, is found digit by digit (a radix select).  All real keys share
+// the bits of their maximum and minimum above the highest bit where those differ; below it,
+// each pass histograms the next 8 bits (fewer in the last pass) of the keys that still
+// match the digits found so far (LDS atomics), and after one barrier every wave reads the
+// 256 counts and takes the largest digit whose suffix count still reaches the number of
+// keys wanted from the bracket.  The keys of larger digits are all selected; the wanted
+// count drops by them.  The search ends after the last bit, or as soon as the bracket holds
+// exactly the keys still wanted (K is then its smallest key, one more exchange).  The keys
+// equal to K that are taken are the first k - #{> K} in element order.  Sentinels never
+// count.
+// Three histograms rotate, so one barrier per pass suffices: the one a pass clears was last
+// read two passes before, which every wave finished before the previous barrier.
+// red: 4 * kFinalWaves ints of LDS (16-byte aligned); note: 1 int; hist: kHistWords.
 struct KthKey {
   uint32_t key;
   int idx;
@@ -331,147 +329,78 @@ struct KthKey {
 
 template <int E>
 __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int k, int* out,
-                                  int* red, int* note, uint32_t* bucket) {
+                                  int* red, int* note, uint32_t* hist) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int parity = 0;
-  // this wave's #{keys > T} (strict) or #{keys >= T}, wave-uniform (vector counts in four
-  // accumulators, then one DPP reduction)
-  auto count = [&](uint32_t T, bool strict) {
-    int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
-#pragma unroll
-    for (int j = 0; j < E; j += 4) {
-      c0 += (strict ? kv[j] > T : kv[j] >= T) ? 1 : 0;
-      c1 += (strict ? kv[j + 1] > T : kv[j + 1] >= T) ? 1 : 0;
-      c2 += (strict ? kv[j + 2] > T : kv[j + 2] >= T) ? 1 : 0;
-      c3 += (strict ? kv[j + 3] > T : kv[j + 3] >= T) ? 1 : 0;
-    }
-    return wave_sum((c0 + c1) + (c2 + c3));
-  };
+  for (int i = tid; i < 2 * kRadixBins; i += kFinalThreads) hist[i] = 0u;
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     mx = max(mx, kv[j]);
     mn = min(mn, kv[j] == kSentinel ? 0xFFFFFFFFu : kv[j]);
   }
-  block_max_min(mx, mn, red, parity);
-  uint32_t K = mx, K_hi = 0u;
-  bool has_hi = false;
-  int c_K = kFinalThreads * E, c_hi = 0;  // #{>= K} (an upper bound until K moves), #{>= K_hi}
-  int bit = -1;                           // mx == mn: every real key is the k-th
+  block_max_min(mx, mn, red, parity);  // its barrier also publishes the cleared histograms
+  uint32_t K = mx;
   if (mx != mn) {
-    bit = 31 - __builtin_clz(mx ^ mn);
-    if (bit < 31) {
-      const uint32_t span = 2u << bit;
-      K = mx & ~(span - 1u);
-      K_hi = K + span;
-      has_hi = K_hi != 0u;  // (every key is below K_hi: c_hi = 0)
-    } else {
-      K = 0u;
-    }
-  }
+    int need = k;                              // keys wanted from the current bracket
+    int lo_bit = 32 - __builtin_clz(mx ^ mn);  // bits lo_bit .. 31 are those of mx
+    uint32_t prefix = lo_bit >= 32 ? 0u : (mx >> lo_bit) << lo_bit;
+    bool open = true;  // the bracket still holds more keys than are wanted from it
 #pragma unroll 1
-  for (; bit >= 0; --bit) {
-    const uint32_t T = K | (1u << bit);
-    const int c = block_sum_waves(count(T, false), red, parity);
-    if (c >= k) {
-      K = T;
-      c_K = c;
-    } else {
-      K_hi = T;
-      has_hi = true;
-      c_hi = c;
-    }
-    if (c_K - c_hi <= kBucketMax) {  // uniform
-      --bit;
-      break;
-    }
-  }
-  int r;  // equal keys taken (>= 1)
-  if (bit >= 0) {
-    const uint32_t lo = K > 1u ? K : 1u;
-    auto in_bucket = [&](uint32_t x) { return x >= lo && (!has_hi || x < K_hi); };
-    int na = 0;
+    for (int pass = 0; lo_bit > 0; ++pass) {  // uniform
+      const int width = lo_bit < kRadixBits ? lo_bit : kRadixBits;
+      const int sh = lo_bit - width;
+      uint32_t* h = hist + kRadixBins * (pass % 3);
+      if (pass > 0) {
+        uint32_t* h2 = hist + kRadixBins * ((pass + 1) % 3);
+        for (int i = tid; i < kRadixBins; i += kFinalThreads) h2[i] = 0u;
+      }
+      const uint64_t want = (uint64_t)prefix >> lo_bit;  // the bits found so far
 #pragma unroll
-    for (int j = 0; j < E; ++j) na += in_bucket(kv[j]) ? 1 : 0;
-    int n_bucket;
-    int at = block_excl_scan(na, &n_bucket, red, parity);
-#pragma unroll
-    for (int j = 0; j < E; ++j)
-      if (in_bucket(kv[j])) bucket[at++] = kv[j];
-    __syncthreads();
-    constexpr int BE = kBucketMax / 64;
-    uint32_t bk[BE];
-#pragma unroll
-    for (int j = 0; j < BE; ++j) {
-      const int e = 64 * j + lane;
-      bk[j] = e < n_bucket ? bucket[e] : kSentinel;
-    }
-    const int c_hi0 = c_hi;
-    auto bcount = [&](uint32_t T, bool strict) {
-      int c = c_hi0;
-#pragma unroll
-      for (int j = 0; j < BE; ++j) c += __popcll(__ballot(strict ? bk[j] > T : bk[j] >= T));
-      return c;
-    };
-#pragma unroll 1
-    while (bit >= 0) {  // uniform
-      if (c_K - c_hi == 1) {
-        // one key in [K, K_hi) (c_K, even as a bound, is then exact): it is the k-th
-        const uint32_t lo2 = K > 1u ? K : 1u;
-        uint32_t x = K;
-#pragma unroll
-        for (int j = 0; j < BE; ++j) {
-          const uint64_t m = __ballot(bk[j] >= lo2 && (!has_hi || bk[j] < K_hi));
-          if (m) x = (uint32_t)__builtin_amdgcn_readlane((int)bk[j], (int)__builtin_ctzll(m));
-        }
-        K = x;
+      for (int j = 0; j < E; ++j)
+        if (kv[j] != kSentinel && ((uint64_t)kv[j] >> lo_bit) == want)
+          atomicAdd(&h[__builtin_amdgcn_ubfe(kv[j], sh, width)], 1u);
+      __syncthreads();
+      // lane l holds the counts of digits 4l .. 4l+3; suffix sums over the digits, from the
+      // lane's own four and the totals of the lanes above it
+      const v4i c4 = *reinterpret_cast<const v4i*>(&h[4 * lane]);
+      const int s3 = c4[3], s2 = s3 + c4[2], s1 = s2 + c4[1], s0 = s1 + c4[0];
+      const int incl = wave_incl_scan(s0);
+      const int above_lane = __builtin_amdgcn_readlane(incl, 63) - incl;
+      const int S0 = above_lane + s0, S1 = above_lane + s1, S2 = above_lane + s2,
+                S3 = above_lane + s3;
+      // the digit D: largest with S(D) >= need (S falls as the digit grows)
+      const uint64_t ok = __ballot(S0 >= need);  // lane 0 always (S(0) = all in bracket)
+      const int L = 63 - __builtin_clzll(ok);
+      const int i_l = S3 >= need ? 3 : S2 >= need ? 2 : S1 >= need ? 1 : 0;
+      const int s_next = i_l == 3 ? above_lane : i_l == 2 ? S3 : i_l == 1 ? S2 : S1;
+      const int s_at = i_l == 3 ? S3 : i_l == 2 ? S2 : i_l == 1 ? S1 : S0;
+      const int D = 4 * L + __builtin_amdgcn_readlane(i_l, L);
+      const int taken = __builtin_amdgcn_readlane(s_next, L);   // keys of larger digits
+      const int in_d = __builtin_amdgcn_readlane(s_at, L) - taken;  // keys of digit D
+      need -= taken;
+      prefix |= (uint32_t)D << sh;
+      lo_bit = sh;
+      if (in_d == need) {  // uniform: every key left in the bracket is taken
+        open = false;
         break;
       }
-      const int d = bit + 1 < kStepBits ? bit + 1 : kStepBits;
-      const int sh = bit + 1 - d;
-      const int n_t = (1 << d) - 1;
-      int* buf = red_buf(red, parity);
-      if (w >= 1 && w <= n_t) {
-        const int c = bcount(K | ((uint32_t)w << sh), false);
-        if (lane == 0) buf[w] = c;
-      }
-      __syncthreads();
-      // all counts in vector reads (no read waits on another); unused slots count as -1 < k
-      int cs[kFinalWaves];
-#pragma unroll
-      for (int j = 0; j < kFinalWaves; j += 4) {
-        const v4i c4 = *reinterpret_cast<const v4i*>(buf + j);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cs[j + q] = (j + q >= 1 && j + q <= n_t) ? c4[q] : -1;
-      }
-      int digit = 0, c_dig = c_K, c_next = c_hi;
-#pragma unroll
-      for (int j = 1; j < kFinalWaves; ++j) {
-        if (cs[j] >= k) {  // counts fall as j grows
-          digit = j;
-          c_dig = cs[j];
-        }
-      }
-#pragma unroll
-      for (int j = 1; j < kFinalWaves; ++j)
-        if (j == digit + 1 && j <= n_t) c_next = cs[j];
-      if (digit + 1 <= n_t) {
-        K_hi = K | ((uint32_t)(digit + 1) << sh);
-        has_hi = true;
-        c_hi = c_next;
-      }
-      K |= (uint32_t)digit << sh;
-      c_K = c_dig;
-      bit -= d;
     }
-    r = k - bcount(K, true);
-  } else {
-    r = k - block_sum_waves(count(K, true), red, parity);
+    K = prefix;
+    if (!open && lo_bit > 0) {
+      // the k-th key is the smallest of the bracket
+      const uint64_t want = (uint64_t)prefix >> lo_bit;
+      uint32_t bmin = 0xFFFFFFFFu, dummy = 0u;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (kv[j] != kSentinel && ((uint64_t)kv[j] >> lo_bit) == want) bmin = min(bmin, kv[j]);
+      block_max_min(dummy, bmin, red, parity);
+      K = bmin;
+    }
   }
   // one scan of (#{> K}, #{== K}) per thread (each field stays below 2^16): equal keys are
-  // taken in element order until r of them are, so the output position is the keys above K
-  // before this thread plus min(equal keys before it, r)
+  // taken in element order until r = k - #{> K} of them are, so the output position is the
+  // keys above K before this thread plus min(equal keys before it, r)
   int n_eq = 0, n_gt = 0;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
@@ -480,6 +409,7 @@ __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], i
   }
   int tot;
   const int before = block_excl_scan(n_gt | (n_eq << 16), &tot, red, parity);
+  const int r = k - (tot & 0xFFFF);  // equal keys taken (>= 1)
   const int eq_before = before >> 16;
   int pos = (before & 0xFFFF) + min(eq_before, r);
   int e_rank = eq_before;
@@ -509,7 +439,7 @@ __host__ __device__ __forceinline__ int final_per_thread(int n) {
 // exact fallbacks of the final pass come here).
 template <int E, class Get, class Val>
 __device__ KthKey block_topk_e(Get get, Val val, int n, int k, int* out, int* red, int* note,
-                               uint32_t* bucket) {
+                               uint32_t* hist) {
   const int tid = threadIdx.x;
   uint32_t kv[E];
   int vv[E];
@@ -519,19 +449,19 @@ __device__ KthKey block_topk_e(Get get, Val val, int n, int k, int* out, int* re
     kv[j] = e < n ? get(e) : kSentinel;
     vv[j] = e < n ? val(e) : 0;
   }
-  return block_topk_regs<E>(kv, vv, k, out, red, note, bucket);
+  return block_topk_regs<E>(kv, vv, k, out, red, note, hist);
 }
 
 // (get / val are taken by value: they hold a pointer or two, and the slow path is a call.)
 template <class Get, class Val>
 __device__ KthKey block_topk(Get get, Val val, int n, int k, int* out, int* red, int* note,
-                             uint32_t* bucket) {
+                             uint32_t* hist) {
   const int tid = threadIdx.x;
   if (n <= kFinalTile) {
     switch (final_per_thread(n)) {
-      case 8: return block_topk_e<8>(get, val, n, k, out, red, note, bucket);
-      case 16: return block_topk_e<16>(get, val, n, k, out, red, note, bucket);
-      default: return block_topk_e<32>(get, val, n, k, out, red, note, bucket);
+      case 8: return block_topk_e<8>(get, val, n, k, out, red, note, hist);
+      case 16: return block_topk_e<16>(get, val, n, k, out, red, note, hist);
+      default: return block_topk_e<32>(get, val, n, k, out, red, note, hist);
     }
   }
   constexpr int E = 16;  // tile of the re-read path

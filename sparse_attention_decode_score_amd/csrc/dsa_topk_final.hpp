@@ -130,13 +130,13 @@ __device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n
 }
 
 // LDS the final pass needs besides its output: the on-chip candidate tile (keys, token
-// indices), the reduction scratch and the last search bucket.
+// indices), the reduction scratch and the radix histograms of the selection.
 struct FinalScratch {
   uint32_t* lkey;   // kFinalTile
   int32_t* lidx;    // kFinalTile
   int* red;         // 4 * kFinalWaves, 16-byte aligned
   int* note;        // 1
-  uint32_t* bucket; // kBucketMax
+  uint32_t* hist;   // kHistWords
 };
 
 // The exact top k (token order) of row `row` (request position pos, n_vis = pos + 1 visible
@@ -164,7 +164,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
   int32_t* lidx = sc.lidx;
   int* red = sc.red;
   int* note_p = sc.note;
-  uint32_t* bucket = sc.bucket;
+  uint32_t* hist = sc.hist;
   float* const row_scores = scores + (int64_t)row * score_stride;
   const float* src = row_scores;
   // LDS of a recomputation (the candidate tile is free until the resend rebuilds it)
@@ -217,7 +217,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
             vv[4 * q + j] = c[q][j];
           }
         }
-        kth = block_topk_regs<E>(kv, vv, k, out, red, note_p, bucket);
+        kth = block_topk_regs<E>(kv, vv, k, out, red, note_p, hist);
       };
       switch (final_per_thread(n_cand)) {
         case 8: run(std::integral_constant<int, 8>()); break;
@@ -226,7 +226,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
       }
     } else {
       kth = block_topk([ck](int i) { return ck[i]; }, [ci](int i) { return ci[i]; }, n_cand, k,
-                       out, red, note_p, bucket);
+                       out, red, note_p, hist);
     }
     const uint32_t K = kth.key;
     const int I = kth.idx;
@@ -304,7 +304,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
         }
         __syncthreads();
         block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, total, k,
-                   out, red, note_p, bucket);
+                   out, red, note_p, hist);
       } else {
         // Too many to hold.  Every winner ranks at or above the candidates' k-th (K, I) (the
         // k-th of a subset is a lower bound of the true k-th), so only those elements of the
@@ -314,7 +314,7 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
         if (n_groups <= kMaxTopk) kept = gather_kept(resend_at, total, ranked, lkey, lidx, red, parity);
         if (kept <= kFinalTile) {
           block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
-                     k, out, red, note_p, bucket);
+                     k, out, red, note_p, hist);
         } else {
           // no stored scores: the rest of the row is recomputed first
           if (rs.q) {
@@ -333,9 +333,9 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
           kept = gather_kept(score_at, n_vis, at_least, lkey, lidx, red, parity);
           if (kept <= kFinalTile) {
             block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
-                       k, out, red, note_p, bucket);
+                       k, out, red, note_p, hist);
           } else {
-            block_topk(score_get, ident, n_vis, k, out, red, note_p, bucket);
+            block_topk(score_get, ident, n_vis, k, out, red, note_p, hist);
           }
         }
       }

@@ -169,7 +169,7 @@ struct SelectSmem {
   int32_t lidx[kFinalTile];
   alignas(16) int red[4 * kFinalWaves];
   int note;
-  uint32_t bucket[kBucketMax];
+  alignas(16) uint32_t hist[kHistWords];
 };
 static_assert(sizeof(SelectSmem) <= offsetof(MlaSmem, slot_l), "selection scratch overlaps slot_l");
 static_assert(kFinalThreads == kThreads, "the fused kernel runs the final pass on its own threads");
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     SelectSmem& ss = *reinterpret_cast<SelectSmem*>(&sm);
     int b, pos;
     row_of(sel.cu_q, sel.seq_lens, sel.num_seqs, row, b, pos);
-    const FinalScratch sc{ss.lkey, ss.lidx, ss.red, &ss.note, ss.bucket};
+    const FinalScratch sc{ss.lkey, ss.lidx, ss.red, &ss.note, ss.hist};
     const int32_t* bt = sel.block_table + (int64_t)b * sel.bt_stride;
     // a resend overwrites the staged query: its gathers must have landed first
     auto before_resend = [&]() {

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   __shared__ int out[kMaxTopk];
   __shared__ __attribute__((aligned(16))) int red[4 * kFinalWaves];
   __shared__ int note;
-  __shared__ uint32_t bucket[kBucketMax];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHistWords];
   const int row = blockIdx.x, tid = threadIdx.x;
   int b, pos;
   row_of(cu_q, seq_lens, num_seqs, row, b, pos);
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   int32_t* oi = topk_idx + (int64_t)row * k;
   int32_t* os = topk_slot ? topk_slot + (int64_t)row * k : nullptr;
   const int32_t* bt = block_table ? block_table + (int64_t)b * bt_stride : nullptr;
-  FinalScratch sc{lkey, lidx, red, &note, bucket};
+  FinalScratch sc{lkey, lidx, red, &note, hist};
   const int n_out = final_select_row(row, n_vis, scores, score_stride, k, num_groups, row_cap,
                                      cand_key, cand_idx, info, rs, bt, out, sc);
 #pragma unroll 8
