@@ -104,9 +104,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // One wave's top-m of a group: lane l holds element 64*j + l in keys[j] (element i is token
 // t0 + i; elements i >= n are not visible).  Writes the min(n, m) chosen keys and token
 // indices in token order to ck / ci, sentinels (key 0, index INT_MAX) after them, and the
-// group's record.  Wave-uniform control flow only; no LDS.
+// group's record.  Wave-uniform control flow only.  wave_hist: 256 counters of LDS (16-byte
+// aligned) that only this wave uses.
 __device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, int m, int t0,
-                                             uint32_t* ck, int32_t* ci, ChunkInfo* inf) {
+                                             uint32_t* ck, int32_t* ci, ChunkInfo* inf,
+                                             uint32_t* wave_hist) {
   const int lane = lane_id();
   uint32_t kv[4];
 #pragma unroll
@@ -123,11 +125,13 @@ __device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, i
     if (lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
     return;
   }
-  // K = the m-th largest key: the largest T with #{keys >= T} >= m, two bits at a time.  The
+  // K = the m-th largest key, found 8 bits at a time (a radix select within the wave).  The
   // visible keys (>= 1) share the bits of their maximum and minimum above the highest bit
-  // where those differ, so the search starts below it with the bracket [K, K_hi) around
-  // every key; it ends early when one key is left in the bracket (that key is the m-th).
-  // Every T tried is >= 1, so the sentinel of an invisible element never counts.
+  // where those differ; below it, each step histograms the next 8 bits of the keys that still
+  // match the digits found so far (LDS atomics on this wave's counters, which LDS applies in
+  // the wave's order, so no wait is needed before reading them back) and takes the largest
+  // digit whose suffix count reaches the number of keys still wanted.  The search stops when
+  // the bracket holds exactly the keys still wanted; K is then its smallest key.
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -136,81 +140,55 @@ __device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, i
   }
   mx = wave_max_u32(mx);
   mn = wave_min_u32(mn);
-  uint32_t K = mx, K_hi = 0u;
-  bool has_hi = false;
-  int c_K = n, c_hi = 0;  // #{>= K} (an upper bound until K moves), #{>= K_hi}
-  int bit = -1;           // mx == mn: every visible key is the m-th
+  uint32_t K = mx;
+  DSA_LDS uint32_t* const hist = (DSA_LDS uint32_t*)wave_hist;
   if (mx != mn) {
-    bit = 31 - __builtin_clz(mx ^ mn);
-    if (bit < 31) {
-      const uint32_t span = 2u << bit;
-      K = mx & ~(span - 1u);
-      K_hi = K + span;
-      has_hi = K_hi != 0u;
-    } else {
-      K = 0u;
-    }
-  }
+    int need = m;
+    int lo_bit = 32 - __builtin_clz(mx ^ mn);  // bits lo_bit .. 31 are those of mx
+    uint32_t prefix = lo_bit >= 32 ? 0u : (mx >> lo_bit) << lo_bit;
+    bool exact = true;
 #pragma unroll 1
-  for (; bit >= 0; --bit) {
-    if (c_K - c_hi == 1) {
-      const uint32_t lo = K > 1u ? K : 1u;
-      uint32_t x = K;
+    while (lo_bit > 0) {  // uniform
+      const int width = lo_bit < 8 ? lo_bit : 8;
+      const int sh = lo_bit - width;
+      *reinterpret_cast<DSA_LDS v4i*>(hist + 4 * lane) = v4i{0, 0, 0, 0};
+      const uint64_t want = (uint64_t)prefix >> lo_bit;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint64_t b = __ballot(kv[j] >= lo && (!has_hi || kv[j] < K_hi));
-        if (b) x = (uint32_t)__builtin_amdgcn_readlane((int)kv[j], (int)__builtin_ctzll(b));
+      for (int j = 0; j < 4; ++j)
+        if (kv[j] != kSentinel && ((uint64_t)kv[j] >> lo_bit) == want)
+          __hip_atomic_fetch_add(hist + __builtin_amdgcn_ubfe(kv[j], sh, width), 1u,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+      const v4i c4 = *reinterpret_cast<const DSA_LDS v4i*>(hist + 4 * lane);
+      const int s3 = c4[3], s2 = s3 + c4[2], s1 = s2 + c4[1], s0 = s1 + c4[0];
+      const int incl = wave_incl_scan(s0);
+      const int above_lane = __builtin_amdgcn_readlane(incl, 63) - incl;
+      const int S0 = above_lane + s0, S1 = above_lane + s1, S2 = above_lane + s2,
+                S3 = above_lane + s3;
+      const uint64_t ok = __ballot(S0 >= need);  // lane 0 always
+      const int L = 63 - __builtin_clzll(ok);
+      const int i_l = S3 >= need ? 3 : S2 >= need ? 2 : S1 >= need ? 1 : 0;
+      const int s_next = i_l == 3 ? above_lane : i_l == 2 ? S3 : i_l == 1 ? S2 : S1;
+      const int s_at = i_l == 3 ? S3 : i_l == 2 ? S2 : i_l == 1 ? S1 : S0;
+      const int D = 4 * L + __builtin_amdgcn_readlane(i_l, L);
+      const int taken = __builtin_amdgcn_readlane(s_next, L);
+      const int in_d = __builtin_amdgcn_readlane(s_at, L) - taken;
+      need -= taken;
+      prefix |= (uint32_t)D << sh;
+      lo_bit = sh;
+      if (in_d == need) {  // every key left in the bracket is taken
+        exact = lo_bit == 0;
+        break;
       }
-      K = x;
-      break;
     }
-    if (bit == 0) {  // the last bit alone
-      const uint32_t T = K | 1u;
-      int c = 0;
+    K = prefix;
+    if (!exact) {
+      const uint64_t want = (uint64_t)prefix >> lo_bit;
+      uint32_t bmin = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c += __popcll(__ballot(kv[j] >= T));
-      if (c >= m) {
-        K = T;
-        c_K = c;
-      } else {
-        K_hi = T;
-        has_hi = true;
-        c_hi = c;
-      }
-      break;
+      for (int j = 0; j < 4; ++j)
+        if (kv[j] != kSentinel && ((uint64_t)kv[j] >> lo_bit) == want) bmin = min(bmin, kv[j]);
+      K = wave_min_u32(bmin);
     }
-    // two bits per step: the counts against the three thresholds of the next two bits are
-    // independent (their ballots overlap); they fall as the threshold rises
-    const int sh = bit - 1;
-    const uint32_t T1 = K | (1u << sh), T2 = K | (2u << sh), T3 = K | (3u << sh);
-    int c1 = 0, c2 = 0, c3 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c1 += __popcll(__ballot(kv[j] >= T1));
-      c2 += __popcll(__ballot(kv[j] >= T2));
-      c3 += __popcll(__ballot(kv[j] >= T3));
-    }
-    if (c3 >= m) {
-      K = T3;
-      c_K = c3;
-    } else if (c2 >= m) {
-      K = T2;
-      c_K = c2;
-      K_hi = T3;
-      has_hi = true;
-      c_hi = c3;
-    } else if (c1 >= m) {
-      K = T1;
-      c_K = c1;
-      K_hi = T2;
-      has_hi = true;
-      c_hi = c2;
-    } else {
-      K_hi = T1;
-      has_hi = true;
-      c_hi = c1;
-    }
-    --bit;  // with the loop's decrement: two bits settled
   }
   int gt = 0;
 #pragma unroll

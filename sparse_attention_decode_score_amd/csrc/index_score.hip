@@ -140,6 +140,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t cbuf_key[CSTAGE ? R : 1][CSTAGE ? Cfg::kCandSlots : 1];
   __shared__ __attribute__((aligned(16))) int32_t cbuf_idx[CSTAGE ? R : 1][CSTAGE ? Cfg::kCandSlots : 1];
   __shared__ __attribute__((aligned(16))) ChunkInfo cbuf_info[CSTAGE ? R : 1][CSTAGE ? kWaves * Cfg::kMaxGroups : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t ghist[CAND ? kWaves : 1][256];  // per wave
 
   const int G = groups_per_wave;  // <= Cfg::kMaxGroups (host-checked)
   const int b = blockIdx.y;
@@ -243,11 +244,12 @@ __global__ __launch_bounds__(256) void index_score_kernel(
           const int gl = kWaves * gi + wave;  // group index in the workgroup
           if constexpr (CSTAGE) {
             group_select(keys[r], min(kGroupTok, n_vis - t0), m, t0, &cbuf_key[r][gl * m],
-                         &cbuf_idx[r][gl * m], &cbuf_info[r][gl]);
+                         &cbuf_idx[r][gl * m], &cbuf_info[r][gl], &ghist[wave][0]);
           } else {
             const int64_t base = (int64_t)row * cand.row_cap + (int64_t)grp * m;
             group_select(keys[r], min(kGroupTok, n_vis - t0), m, t0, cand.key + base,
-                         cand.idx + base, cand.info + (int64_t)row * cand.num_groups + grp);
+                         cand.idx + base, cand.info + (int64_t)row * cand.num_groups + grp,
+                         &ghist[wave][0]);
           }
         }
       }

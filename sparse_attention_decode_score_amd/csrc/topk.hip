@@ -37,6 +37,7 @@ __global__ __launch_bounds__(256) void topk_group_kernel(
     const float* __restrict__ scores, int64_t score_stride, int k, int num_groups,
     int64_t row_cap, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx,
     ChunkInfo* __restrict__ info) {
+  __shared__ __attribute__((aligned(16))) uint32_t ghist[4][256];  // per wave
   const int row = blockIdx.y;
   int b, pos;
   row_of(cu_q, seq_lens, num_seqs, row, b, pos);
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void topk_group_kernel(
   const int m = group_cand_count(n_vis, k);
   const int64_t base = (int64_t)row * row_cap + (int64_t)g * m;
   group_select(keys, n, m, t0, cand_key + base, cand_idx + base,
-               info + (int64_t)row * num_groups + g);
+               info + (int64_t)row * num_groups + g, &ghist[threadIdx.x >> 6][0]);
 }
 
 // ---------------------------------------------------------------- pass 2
