@@ -216,8 +216,8 @@ dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const in
  *
  *   Query: q8 (uint8 E4M3 codes [n_q][96][576]) and q_scale (fp32 [n_q][96]) as
  *   dsa_quantize_q(n_q, 96, 576, ...) writes them, when both are given (the caller can
- *   prepare them on another stream while stages 1 and 2 run); otherwise q_bf16
- *   [n_q][96][576] bf16, quantised inside the call.
+ *   prepare them on another stream while stages 1 and 2 run; both 16-byte aligned);
+ *   otherwise q_bf16 [n_q][96][576] bf16 (16-byte aligned), quantised inside the call.
  *   topk_slot int32 [n_q][k]; -1 entries are skipped.
  *   num_splits S in 1..64, S <= k: split s of a row covers entries [s*k/S, (s+1)*k/S)
  *   of its slot list (splits add workgroups for small batches).

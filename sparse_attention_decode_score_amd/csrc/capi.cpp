@@ -68,7 +68,8 @@ dsa_status check_mla_inputs(int32_t n_q, const void* q_bf16, const void* q8,
   DSA_REQUIRE((q8 == nullptr) == (q_scale == nullptr), "q8 and q_scale must both be given or both be NULL");
   DSA_REQUIRE(prepared || q_bf16, "the query is missing: give q_bf16 or q8 and q_scale");
   DSA_REQUIRE(latent_pages, "latent_pages must be non-null");
-  DSA_REQUIRE(prepared ? aligned(q8, 16) : aligned(q_bf16, 16), "the query must be 16-byte aligned");
+  DSA_REQUIRE(prepared ? aligned(q8, 16) && aligned(q_scale, 16) : aligned(q_bf16, 16),
+              "the query (codes and scales) must be 16-byte aligned");
   DSA_REQUIRE(aligned(latent_pages, 16), "latent_pages must be 16-byte aligned");
   DSA_REQUIRE(latent_page_stride >= DSA_LATENT_PAGE_BYTES && latent_page_stride % 16 == 0,
               "latent_page_stride must be >= 36864 and a multiple of 16 (got %lld)",

@@ -16,11 +16,13 @@ constexpr int kGroupTok = 256;      // tokens per first-pass group (one wave, 4 
 #endif
 constexpr int kFinalThreads = DSA_FINAL_THREADS;  // threads of the final pass
 constexpr int kFinalWaves = kFinalThreads / 64;
-constexpr int kFinalPerThread = 32;  // at most, in registers
+constexpr int kFinalPerThread = 32;     // keys per thread of the on-chip candidate list (LDS)
+constexpr int kFinalRegPerThread = 64;  // keys per thread the selection holds in registers
 constexpr int kRadixBits = 8;                  // key bits one pass of the final selection settles
 constexpr int kRadixBins = 1 << kRadixBits;
 constexpr int kHistWords = 3 * kRadixBins;     // LDS counters of the final selection
-constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds on chip
+constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds in LDS
+constexpr int kFinalRegTile = kFinalThreads * kFinalRegPerThread;  // ... and in registers
 
 // Per-group record of the first selection pass.
 struct ChunkInfo {
@@ -36,17 +38,21 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return k == 0u ? 1u : k;
 }
 
-// Candidates a first-pass group keeps: four times the winners a full group holds on
-// average (k * 256 / n_vis; the on-chip form of the 1.5 x 2048 / W per-shard rule of the
-// exact top-k merge, with more slack because a group is small), rounded up to 4, at least
-// 4 and at most the group.  At 131,072 visible tokens and k = 2,048: 16 of 256 (a group
-// holds 4 winners on average; more than 16 happens about once in 10^6 groups for
-// independent scores, and is then caught and resent).
+// Candidates a first-pass group keeps, m.  A full group holds lambda = k * 256 / n_vis of the
+// winners on average (the on-chip form of the per-shard rule of the exact top-k merge, with
+// slack because a group is small): m = 4 lambda where lambda >= 4, else 4 lambda + 4 and at
+// least 8, rounded up to 4 and at most the group.  A group holding m or more winners is
+// resent (read again in full) by the final pass; for independent scores that is about one
+// group in 10^5 rows at lambda = 4 (131,072 visible tokens, k = 2,048: m = 16) and rarer at
+// smaller lambda (1,048,576 tokens: lambda = 1/2, m = 8, 32,768 candidates).
 __host__ __device__ __forceinline__ int group_cand_count(int n_vis, int k) {
-  const int64_t num = 4 * (int64_t)k * kGroupTok;
-  int64_t m = (num + n_vis - 1) / n_vis;
+  const int64_t num = 4 * (int64_t)k * kGroupTok;  // 4 lambda n_vis
+  int64_t m = (num + n_vis - 1) / n_vis;           // ceil(4 lambda)
+  if (num < 16 * (int64_t)n_vis) {                 // lambda < 4
+    m += 4;
+    if (m < 8) m = 8;
+  }
   m = (m + 3) / 4 * 4;
-  if (m < 4) m = 4;
   if (m > kGroupTok) m = kGroupTok;
   return (int)m;
 }
@@ -305,9 +311,9 @@ struct KthKey {
   int idx;
 };
 
-template <int E>
-__device__ KthKey block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], int k, int* out,
-                                  int* red, int* note, uint32_t* hist) {
+template <int E, class Val>
+__device__ KthKey block_topk_regs(const uint32_t (&kv)[E], Val val, int k, int* out, int* red,
+                                  int* note, uint32_t* hist) {
   const int tid = threadIdx.x, lane = tid & 63;
   int parity = 0;
   for (int i = tid; i < 2 * kRadixBins; i += kFinalThreads) hist[i] = 0u;
@@ -391,25 +397,29 @@ __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], const int (&vv)[E], i
   const int eq_before = before >> 16;
   int pos = (before & 0xFFFF) + min(eq_before, r);
   int e_rank = eq_before;
+  // element indices first (no loads in this loop), then every thread turns k / 512 of them
+  // into values with independent loads
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     bool take = kv[j] > K;
     if (kv[j] == K) {
       take = e_rank < r;
-      if (e_rank == r - 1) *note = vv[j];
+      if (e_rank == r - 1) *note = tid * E + j;
       ++e_rank;
     }
-    if (take) out[pos++] = vv[j];
+    if (take) out[pos++] = tid * E + j;
   }
   __syncthreads();
-  const int I = *note;
+  const int I = val(*note);
+#pragma unroll 4
+  for (int i = tid; i < k; i += kFinalThreads) out[i] = val(out[i]);
   __syncthreads();
   return KthKey{K, I};
 }
 
-// Smallest per-thread count E in {8, 16, 32} with kFinalThreads * E >= n.
+// Smallest per-thread count E in {8, 16, 32, 64} with kFinalThreads * E >= n.
 __host__ __device__ __forceinline__ int final_per_thread(int n) {
-  return n <= 8 * kFinalThreads ? 8 : n <= 16 * kFinalThreads ? 16 : 32;
+  return n <= 8 * kFinalThreads ? 8 : n <= 16 * kFinalThreads ? 16 : n <= 32 * kFinalThreads ? 32 : 64;
 }
 
 // The same selection over get(0 .. n-1) / val(0 .. n-1) (1 <= k <= real keys, any n): up to
@@ -420,14 +430,12 @@ __device__ KthKey block_topk_e(Get get, Val val, int n, int k, int* out, int* re
                                uint32_t* hist) {
   const int tid = threadIdx.x;
   uint32_t kv[E];
-  int vv[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const int e = tid * E + j;
     kv[j] = e < n ? get(e) : kSentinel;
-    vv[j] = e < n ? val(e) : 0;
   }
-  return block_topk_regs<E>(kv, vv, k, out, red, note, hist);
+  return block_topk_regs<E>(kv, val, k, out, red, note, hist);
 }
 
 // (get / val are taken by value: they hold a pointer or two, and the slow path is a call.)

@@ -81,7 +81,7 @@ __device__ int gather_kept(const Get& get, int n, const Keep& keep, uint32_t* lk
 // (32 * kQRowStride bytes, 16-byte aligned) and folded head weights (32 floats, 16-byte
 // aligned).  Starts and ends with a barrier; every thread of the workgroup calls it.
 template <class Need>
-__device__ void rescore_groups(const IndexRescore& rs, int row, int n_vis, int n_groups,
+__device__ void rescore_groups(const IndexRescore rs, int row, int n_vis, int n_groups,
                                const int32_t* bt_row, float* row_scores, Need need, uint8_t* q8,
                                float* w) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -139,6 +139,259 @@ struct FinalScratch {
   uint32_t* hist;   // kHistWords
 };
 
+// The resend of the final pass (see final_select_row).  Everything is passed by value: a
+// pointer into the kernel's argument block would make the compiler copy that block to
+// scratch memory at the kernel's start.
+struct ResendArgs {
+  int row, n_vis, k, n_groups, m, parity;
+  uint32_t K;
+  int I;
+  const uint32_t* ck;
+  const int32_t* ci;
+  const ChunkInfo* inf;
+  IndexRescore rs;
+  const int32_t* bt_row;
+  float* row_scores;
+  int* out;
+  uint32_t* lkey;
+  int32_t* lidx;
+  int* red;
+  int* note_p;
+  uint32_t* hist;
+  uint8_t* rq8;
+  float* rw;
+};
+
+__device__ __forceinline__ void final_resend(const ResendArgs a) {
+  const int tid = threadIdx.x;
+  const int row = a.row, n_vis = a.n_vis, k = a.k, n_groups = a.n_groups, m = a.m;
+  int parity = a.parity;
+  const uint32_t K = a.K;
+  const int I = a.I;
+  const uint32_t* __restrict__ ck = a.ck;
+  const int32_t* __restrict__ ci = a.ci;
+  const ChunkInfo* __restrict__ inf = a.inf;
+  const IndexRescore rs = a.rs;
+  const int32_t* bt_row = a.bt_row;
+  float* const row_scores = a.row_scores;
+  const float* src = row_scores;
+  int* out = a.out;
+  uint32_t* lkey = a.lkey;
+  int32_t* lidx = a.lidx;
+  int* red = a.red;
+  int* note_p = a.note_p;
+  uint32_t* hist = a.hist;
+  uint8_t* const rq8 = a.rq8;
+  float* const rw = a.rw;
+  auto score_get = [src](int i) { return score_key(src[i]); };
+  auto ident = [](int i) { return i; };
+  auto flag_of = [&](const ChunkInfo& ic) {
+    return ic.saturated && (ic.key > K || (ic.key == K && ic.idx < I));
+  };
+  auto flagged = [&](int g) { return flag_of(inf[g]); };
+    // Rebuild the candidate list in token order, flagged groups in full and the others as
+    // sent: thread t owns groups GPT t .. GPT t + GPT-1, and one scan of their lengths gives
+    // every thread the list position of its elements.  out[g] (free until the next
+    // selection) = start of group g | kFlagBit if g is flagged, for the recomputation.
+    constexpr uint32_t kFlagBit = 0x80000000u, kStartMask = 0x7FFFFFFFu;
+    uint32_t* const starts = reinterpret_cast<uint32_t*>(out);
+    int total = 0;
+    constexpr int GPT = kMaxTopk / kFinalThreads;  // groups per thread: GPT tid .. +GPT-1
+    int len[GPT];   // elements of each of them in the resend list
+    uint32_t fl = 0;  // which of them are flagged
+    int at0 = 0;      // the resend-list position of this thread's first element
+    if (n_groups <= kMaxTopk) {
+      int sum = 0;
+#pragma unroll
+      for (int q = 0; q < GPT; ++q) {
+        const int g = GPT * tid + q;
+        const bool f = g < n_groups && flagged(g);
+        fl |= f ? 1u << q : 0u;
+        len[q] = g >= n_groups ? 0 : (f ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
+        sum += len[q];
+      }
+      int at = block_excl_scan(sum, &total, red, parity);
+      at0 = at;
+#pragma unroll
+      for (int q = 0; q < GPT; ++q) {
+        const int g = GPT * tid + q;  // every group has >= 1 element: starts increase
+        starts[g] = g < n_groups ? ((uint32_t)at | (((fl >> q) & 1u) ? kFlagBit : 0u)) : kStartMask;
+        at += len[q];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < GPT; ++q) len[q] = 0;
+      total = kFinalTile + 1;
+    }
+    __syncthreads();
+    auto flagged_lds = [starts](int g) { return (starts[g] & kFlagBit) != 0u; };
+    // no stored scores: the flagged groups, which the resend reads in full, are recomputed
+    if (rs.q && n_groups <= kMaxTopk)
+      rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores, flagged_lds, rq8, rw);
+    // The list is written group by group in token order.  A thread copies the candidates of
+    // its own unflagged groups; the flagged groups (256 recomputed scores each) are copied by
+    // the wave of the thread that owns them, 4 elements per lane.  keep(key, token) filters
+    // the elements; off[q] is the position of group q's kept elements after this thread's
+    // first.
+    const int lane = tid & 63;
+    // fn(q, key, token) for every candidate of this thread's unflagged groups, in token
+    // order within each group: 4 candidates of every group per step, all of a step's loads
+    // issued together (a group's m slots are a multiple of 4 and 16-byte aligned)
+    int max_len = 0;
+#pragma unroll
+    for (int q = 0; q < GPT; ++q) max_len = ((fl >> q) & 1u) ? max_len : max(max_len, len[q]);
+    auto each_candidate = [&](auto fn) {
+#pragma unroll 1
+      for (int i4 = 0; i4 < max_len; i4 += 4) {
+        v4i kk[GPT], ii[GPT];
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) {
+          const bool on = !((fl >> q) & 1u) && i4 < len[q];
+          const int64_t o = on ? (int64_t)(GPT * tid + q) * m + i4 : 0;
+          kk[q] = *reinterpret_cast<const v4i*>(ck + o);
+          ii[q] = *reinterpret_cast<const v4i*>(ci + o);
+        }
+#pragma unroll
+        for (int q = 0; q < GPT; ++q)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (!((fl >> q) & 1u) && i4 + c < len[q]) fn(q, (uint32_t)kk[q][c], ii[q][c]);
+      }
+    };
+    // kept elements of every group of this thread (flagged ones counted by the wave)
+    auto count_kept = [&](auto keep, int (&cnt)[GPT]) {
+#pragma unroll
+      for (int q = 0; q < GPT; ++q) cnt[q] = 0;
+      each_candidate([&](int q, uint32_t key, int t) {
+#pragma unroll
+        for (int qq = 0; qq < GPT; ++qq) cnt[qq] += (qq == q && keep(key, t)) ? 1 : 0;
+      });
+      for (uint64_t owners = __ballot(fl != 0u); owners; owners &= owners - 1) {  // uniform
+        const int ol = (int)__builtin_ctzll(owners);
+        const uint32_t ofl = (uint32_t)__builtin_amdgcn_readlane((int)fl, ol);
+        for (uint32_t qs = ofl; qs; qs &= qs - 1) {
+          const int q = (int)__builtin_ctz(qs);
+          const int g = GPT * (tid - lane + ol) + q;
+          int c = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 64 * j + lane;
+            const int t = g * kGroupTok + i;
+            const bool in = i < kGroupTok && t < n_vis && keep(score_key(src[t]), t);
+            c += __popcll(__ballot(in));
+          }
+#pragma unroll
+          for (int qq = 0; qq < GPT; ++qq)
+            if (qq == q && lane == ol) cnt[qq] = c;
+        }
+      }
+    };
+    // writes the kept elements, this thread's first at position base
+    auto write_kept = [&](auto keep, int base, const int (&cnt)[GPT]) {
+      int off[GPT];
+      int run = base;
+#pragma unroll
+      for (int q = 0; q < GPT; ++q) {
+        off[q] = run;
+        run += cnt[q];
+      }
+      {
+        int wpos[GPT];
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) wpos[q] = off[q];
+        each_candidate([&](int q, uint32_t key, int t) {
+          if (keep(key, t)) {
+            int pos = 0;
+#pragma unroll
+            for (int qq = 0; qq < GPT; ++qq) pos = qq == q ? wpos[qq] : pos;
+            lkey[pos] = key;
+            lidx[pos] = t;
+#pragma unroll
+            for (int qq = 0; qq < GPT; ++qq) wpos[qq] += qq == q ? 1 : 0;
+          }
+        });
+      }
+      for (uint64_t owners = __ballot(fl != 0u); owners; owners &= owners - 1) {  // uniform
+        const int ol = (int)__builtin_ctzll(owners);
+        const uint32_t ofl = (uint32_t)__builtin_amdgcn_readlane((int)fl, ol);
+        for (uint32_t qs = ofl; qs; qs &= qs - 1) {
+          const int q = (int)__builtin_ctz(qs);
+          const int g = GPT * (tid - lane + ol) + q;
+          int o = 0;
+#pragma unroll
+          for (int qq = 0; qq < GPT; ++qq) o = qq == q ? off[qq] : o;
+          int pos = __builtin_amdgcn_readlane(o, ol);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 64 * j + lane;
+            const int t = g * kGroupTok + i;
+            const uint32_t key = (i < kGroupTok && t < n_vis) ? score_key(src[t]) : kSentinel;
+            const bool in = i < kGroupTok && t < n_vis && keep(key, t);
+            const uint64_t b = __ballot(in);
+            if (in) {
+              lkey[pos + lanes_below(b)] = key;
+              lidx[pos + lanes_below(b)] = t;
+            }
+            pos += __popcll(b);
+          }
+        }
+      }
+    };
+    if (total <= kFinalTile) {
+      auto all = [](uint32_t, int) { return true; };
+      int cnt[GPT];
+#pragma unroll
+      for (int q = 0; q < GPT; ++q) cnt[q] = len[q];
+      write_kept(all, at0, cnt);
+      __syncthreads();
+      block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, total, k,
+                 out, red, note_p, hist);
+    } else {
+      // Too many to hold.  Every winner ranks at or above the candidates' k-th (K, I) (the
+      // k-th of a subset is a lower bound of the true k-th), so only those elements of the
+      // resend list are kept (counted, then written in list order); if even they do not
+      // fit, the whole row is filtered by K.
+      auto ranked = [K, I](uint32_t key, int t) { return key > K || (key == K && t <= I); };
+      int kept = kFinalTile + 1;
+      if (n_groups <= kMaxTopk) {
+        int cnt[GPT];
+        count_kept(ranked, cnt);
+        int mine = 0;
+#pragma unroll
+        for (int q = 0; q < GPT; ++q) mine += cnt[q];
+        const int pos = block_excl_scan(mine, &kept, red, parity);
+        if (kept <= kFinalTile) write_kept(ranked, pos, cnt);
+        __syncthreads();
+      }
+      if (kept <= kFinalTile) {
+        block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
+                   k, out, red, note_p, hist);
+      } else {
+        // no stored scores: the rest of the row is recomputed first
+        if (rs.q) {
+          if (n_groups <= kMaxTopk)
+            rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
+                           [&](int g) { return !flagged_lds(g); }, rq8, rw);
+          else
+            rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
+                           [](int) { return true; }, rq8, rw);
+        }
+        auto score_at = [src](int e, uint32_t& key, int& t) {
+          key = score_key(src[e]);
+          t = e;
+        };
+        auto at_least = [K](uint32_t key, int) { return key >= K; };
+        kept = gather_kept(score_at, n_vis, at_least, lkey, lidx, red, parity);
+        if (kept <= kFinalTile) {
+          block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
+                     k, out, red, note_p, hist);
+        } else {
+          block_topk(score_get, ident, n_vis, k, out, red, note_p, hist);
+        }
+      }
+    }
+  }
+
 // The exact top k (token order) of row `row` (request position pos, n_vis = pos + 1 visible
 // tokens) from its group candidates, resending flagged groups from the scores.  Writes the
 // selected token indices to out[0 .. n_out) (LDS, kMaxTopk entries) and returns n_out =
@@ -187,17 +440,15 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
     // selection does not wait for it
     const ChunkInfo info0 = inf[min(tid, n_groups - 1)];
     KthKey kth;
-    if (n_cand <= kFinalTile) {
+    if (n_cand <= kFinalRegTile) {
       // this thread's E consecutive candidates straight into registers (n_cand and the
       // row's slots are multiples of 4 and 16-byte aligned)
       auto run = [&](auto e_tag) {
         constexpr int E = decltype(e_tag)::value;
         uint32_t kv[E];
-        int vv[E];
-        // keys first, then the token indices: the search waits for the keys only, and the
-        // index loads are still in flight until the compaction needs them
+        // the keys only: a chosen element's token index is read when it is written out
         // (a quad past the end reads element 0 and is masked below)
-        v4i a[E / 4], c[E / 4];
+        v4i a[E / 4];
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
           const int e = tid * E + 4 * q;
@@ -205,24 +456,17 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
         }
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
-          const int e = tid * E + 4 * q;
-          c[q] = *reinterpret_cast<const v4i*>(ci + (e < n_cand ? e : 0));
-        }
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
           const bool in = tid * E + 4 * q < n_cand;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            kv[4 * q + j] = in ? (uint32_t)a[q][j] : kSentinel;
-            vv[4 * q + j] = c[q][j];
-          }
+          for (int j = 0; j < 4; ++j) kv[4 * q + j] = in ? (uint32_t)a[q][j] : kSentinel;
         }
-        kth = block_topk_regs<E>(kv, vv, k, out, red, note_p, hist);
+        kth = block_topk_regs<E>(kv, [ci](int e) { return ci[e]; }, k, out, red, note_p, hist);
       };
       switch (final_per_thread(n_cand)) {
         case 8: run(std::integral_constant<int, 8>()); break;
         case 16: run(std::integral_constant<int, 16>()); break;
-        default: run(std::integral_constant<int, 32>()); break;
+        case 32: run(std::integral_constant<int, 32>()); break;
+        default: run(std::integral_constant<int, 64>()); break;
       }
     } else {
       kth = block_topk([ck](int i) { return ck[i]; }, [ci](int i) { return ci[i]; }, n_cand, k,
@@ -241,104 +485,8 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
     int parity = 0;
     if (block_sum(any, red, parity) > 0) {
       before_scratch();
-      // Rebuild the candidate list in token order, flagged groups in full and the others as
-      // sent: group starts go to LDS (`out` is free until the next selection), then every
-      // thread fills its own elements, locating each one's group by a fixed-depth search.
-      // out[g] = start of group g in the resend list | kFlagBit if g is flagged; the
-      // entries past the last group hold kStartMask, so a fixed-depth search needs no bound
-      constexpr uint32_t kFlagBit = 0x80000000u, kStartMask = 0x7FFFFFFFu;
-      uint32_t* const starts = reinterpret_cast<uint32_t*>(out);
-      int total = 0;
-      if (n_groups <= kMaxTopk) {
-        constexpr int GPT = kMaxTopk / kFinalThreads;  // groups per thread
-        int len[GPT], sum = 0;
-        uint32_t fl = 0;
-#pragma unroll
-        for (int q = 0; q < GPT; ++q) {
-          const int g = GPT * tid + q;
-          const bool f = g < n_groups && flagged(g);
-          fl |= f ? 1u << q : 0u;
-          len[q] = g >= n_groups ? 0 : (f ? min(kGroupTok, n_vis - g * kGroupTok) : inf[g].count);
-          sum += len[q];
-        }
-        int at = block_excl_scan(sum, &total, red, parity);
-#pragma unroll
-        for (int q = 0; q < GPT; ++q) {
-          const int g = GPT * tid + q;  // every group has >= 1 element: starts increase
-          starts[g] = g < n_groups ? ((uint32_t)at | (((fl >> q) & 1u) ? kFlagBit : 0u)) : kStartMask;
-          at += len[q];
-        }
-      } else {
-        total = kFinalTile + 1;
-      }
-      __syncthreads();
-      auto flagged_lds = [starts](int g) { return (starts[g] & kFlagBit) != 0u; };
-      // no stored scores: the flagged groups, which the resend reads in full, are recomputed
-      if (rs.q && n_groups <= kMaxTopk)
-        rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores, flagged_lds, rq8, rw);
-      // element e of the resend list (flagged groups in full, the others' candidates): its
-      // group by a fixed-depth search over the starts
-      auto resend_at = [&](int e, uint32_t& key, int& t) {
-        int lo = 0;  // the last group starting at or before e
-#pragma unroll
-        for (int step = kMaxTopk / 2; step >= 1; step >>= 1)
-          lo += (int)(starts[lo + step] & kStartMask) <= e ? step : 0;
-        const uint32_t st = starts[lo];
-        const int i = e - (int)(st & kStartMask);
-        if (st & kFlagBit) {
-          t = lo * kGroupTok + i;
-          key = score_key(src[t]);
-        } else {
-          key = ck[(int64_t)lo * m + i];
-          t = ci[(int64_t)lo * m + i];
-        }
-      };
-      if (total <= kFinalTile) {
-#pragma unroll 8
-        for (int e = tid; e < total; e += kFinalThreads) {
-          uint32_t key;
-          int t;
-          resend_at(e, key, t);
-          lkey[e] = key;
-          lidx[e] = t;
-        }
-        __syncthreads();
-        block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, total, k,
-                   out, red, note_p, hist);
-      } else {
-        // Too many to hold.  Every winner ranks at or above the candidates' k-th (K, I) (the
-        // k-th of a subset is a lower bound of the true k-th), so only those elements of the
-        // resend list are kept; if even they do not fit, the whole row is filtered by K.
-        auto ranked = [K, I](uint32_t key, int t) { return key > K || (key == K && t <= I); };
-        int kept = kFinalTile + 1;
-        if (n_groups <= kMaxTopk) kept = gather_kept(resend_at, total, ranked, lkey, lidx, red, parity);
-        if (kept <= kFinalTile) {
-          block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
-                     k, out, red, note_p, hist);
-        } else {
-          // no stored scores: the rest of the row is recomputed first
-          if (rs.q) {
-            if (n_groups <= kMaxTopk)
-              rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
-                             [&](int g) { return !flagged_lds(g); }, rq8, rw);
-            else
-              rescore_groups(rs, row, n_vis, n_groups, bt_row, row_scores,
-                             [](int) { return true; }, rq8, rw);
-          }
-          auto score_at = [src](int e, uint32_t& key, int& t) {
-            key = score_key(src[e]);
-            t = e;
-          };
-          auto at_least = [K](uint32_t key, int) { return key >= K; };
-          kept = gather_kept(score_at, n_vis, at_least, lkey, lidx, red, parity);
-          if (kept <= kFinalTile) {
-            block_topk([lkey](int i) { return lkey[i]; }, [lidx](int i) { return lidx[i]; }, kept,
-                       k, out, red, note_p, hist);
-          } else {
-            block_topk(score_get, ident, n_vis, k, out, red, note_p, hist);
-          }
-        }
-      }
+      final_resend(ResendArgs{row, n_vis, k, n_groups, m, parity, K, I, ck, ci, inf, rs, bt_row,
+                              row_scores, out, lkey, lidx, red, note_p, hist, rq8, rw});
     }
     n_out = k;
   }

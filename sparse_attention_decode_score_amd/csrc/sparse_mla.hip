@@ -228,33 +228,32 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int lane = threadIdx.x & 63;
   const int n = lane & 31, g = lane >> 5;
 
-  // The row's query goes out first, so that its latency hides behind the selection or the
-  // slot-list load.  Prepared E4M3 codes go to registers (4 threads per head, 144 dims
-  // each; waves 6, 7 load a copy of heads 0..31 that nobody uses, which keeps the loads
-  // outside any divergent branch).  A bf16 query goes to LDS by direct gathers: its 110,592
-  // bytes fill the three latent buffers exactly, which the selection leaves alone unless it
-  // resends groups (it then waits for the gathers first, and the query is staged again
-  // after it).
-  const bool qthread = threadIdx.x < 4 * kMlaHeads;
-  const int qh = (threadIdx.x >> 2) % kMlaHeads, qpart = threadIdx.x & 3;
-  v4i raw[18];
-  float qs_given = 0.f;
-  if (q8_in) {
-    const uint8_t* src = q8_in + ((int64_t)row * kMlaHeads + qh) * kLatDim + qpart * 144;
-#pragma unroll
-    for (int i = 0; i < 9; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
-    qs_given = qs_in[(int64_t)row * kMlaHeads + qh];
-  }
+  // The row's query goes to LDS first, by direct gathers, so that its latency hides behind
+  // the selection or the slot-list load: bf16 values (110,592 bytes: the three latent
+  // buffers exactly) or prepared E4M3 codes (55,296 bytes) and their 96 scales just after
+  // them.  The selection leaves that LDS alone unless it resends groups; it then waits for
+  // the gathers first, and the query is staged again after it.
+  constexpr int kQ8Bytes = kMlaHeads * kLatDim;  // 55,296
   auto stage_query = [&]() {
-    constexpr int kQChunks = kMlaHeads * kLatDim * 2 / 1024;  // 108 chunks of 1 KB
-    static_assert(kQChunks * 1024 == kRing * kTileBytes, "the bf16 query fills the ring");
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t)row * kMlaHeads * kLatDim);
     DSA_LDS uint8_t* dst = (DSA_LDS uint8_t*)(&sm.lat[0][0]);
-    for (int c = wave; c < kQChunks; c += kWaves)  // wave-uniform
-      __builtin_amdgcn_global_load_lds(qrow + 1024 * c + 16 * lane, dst + 1024 * c, 16, 0, 0);
+    if (q8_in) {
+      const uint8_t* qrow = q8_in + (int64_t)row * kQ8Bytes;
+      for (int c = wave; c < kQ8Bytes / 1024; c += kWaves)  // wave-uniform
+        __builtin_amdgcn_global_load_lds(qrow + 1024 * c + 16 * lane, dst + 1024 * c, 16, 0, 0);
+      if (wave == 0 && lane < kMlaHeads / 4)  // the scales: 384 bytes
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(qs_in + (int64_t)row * kMlaHeads) + 16 * lane,
+                                         dst + kQ8Bytes, 16, 0, 0);
+    } else {
+      constexpr int kQChunks = kMlaHeads * kLatDim * 2 / 1024;  // 108 chunks of 1 KB
+      static_assert(kQChunks * 1024 == kRing * kTileBytes, "the bf16 query fills the ring");
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q + (int64_t)row * kMlaHeads * kLatDim);
+      for (int c = wave; c < kQChunks; c += kWaves)  // wave-uniform
+        __builtin_amdgcn_global_load_lds(qrow + 1024 * c + 16 * lane, dst + 1024 * c, 16, 0, 0);
+    }
   };
-  if (!q8_in) stage_query();
-  bool q_in_lds = q8_in == nullptr;
+  static_assert(kQ8Bytes + 4 * kMlaHeads <= kRing * kTileBytes, "the prepared query fits the ring");
+  stage_query();
+  bool q_in_lds = true;
 
   if constexpr (SELECT) {
     // stage 2 for this row (every split of the row runs it: it is latency-bound), then the
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   }
   // slot_l holds the split's slots, the selection scratch is dead, and every query gather
   // has landed (a resend overwrote the staged query: it is staged again)
-  if (!q8_in && !q_in_lds) stage_query();
+  if (!q_in_lds) stage_query();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
@@ -347,25 +346,33 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     // them.
     uint8_t* const qstage = &sm.lat[2][0];   // [96][kQStride] codes; scales in bsum
     float* const qsc = &sm.bsum[0][0][0][0];
-    if (q8_in) {
-      // the prepared codes loaded at the start go to LDS before the gathers are issued, so
-      // that waiting for them waits for nothing else (waves 6, 7 hold heads 0..31 again and
-      // write the same bytes)
-      uint8_t* dst = qstage + qh * kQStride + qpart * 144;
+    // every wave reads its part of the staged query (4 threads per head, 144 dims each)
+    // before any gather may overwrite it
+    const bool qthread = threadIdx.x < 4 * kMlaHeads;
+    const int qh = threadIdx.x >> 2, qpart = threadIdx.x & 3;
+    v4i raw[18];
+    float qs_given = 0.f;
+    if (qthread) {
+      if (q8_in) {
+        const uint8_t* src = &sm.lat[0][0] + qh * kLatDim + qpart * 144;
 #pragma unroll
-      for (int i = 0; i < 9; ++i) *reinterpret_cast<v4i*>(dst + 16 * i) = raw[i];
-      if (qpart == 0) qsc[qh] = qs_given;
-    } else {
-      // the staged bf16 query: every wave reads its part before any gather may overwrite it
-      if (qthread) {
+        for (int i = 0; i < 9; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
+        qs_given = reinterpret_cast<const float*>(&sm.lat[0][0] + kQ8Bytes)[qh];
+      } else {
         const uint8_t* src = &sm.lat[0][0] + (qh * kLatDim + qpart * 144) * 2;
 #pragma unroll
         for (int i = 0; i < 18; ++i) raw[i] = *reinterpret_cast<const v4i*>(src + 16 * i);
       }
-      lds_barrier();
     }
+    lds_barrier();
     issue(0, 0, 5);
     issue(1, 0, 5);
+    if (q8_in && qthread) {
+      uint8_t* dst = qstage + qh * kQStride + qpart * 144;
+#pragma unroll
+      for (int i = 0; i < 9; ++i) *reinterpret_cast<v4i*>(dst + 16 * i) = raw[i];
+      if (qpart == 0) qsc[qh] = qs_given;
+    }
     if (!q8_in && qthread) {
       uint8_t* dst = qstage + qh * kQStride + qpart * 144;
       // one power-of-two scale per head: the smallest 2^e with absmax <= 448 * 2^e
