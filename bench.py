@@ -196,7 +196,9 @@ def cpu_baseline(batch, rows, budget_s=12.0, max_passes=64):
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(byts / t_total / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "cores_note": "one Python process; cores = the BLAS threads numpy may use in the "
+                          "oracle's matrix products (the rest of it runs on one core)",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "stage_s": {"index_score": round(stage_s[0], 3), "topk": round(stage_s[1], 3),
                         "sparse_mla": round(stage_s[2], 3), "lse_combine": round(stage_s[3], 3)},
             "sample": f"{done} query-row passes over the {len(rows)} rows of the {wl.name} "
@@ -216,6 +218,50 @@ def _probe_lib():
     L.dsa_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return L
+
+
+def page_read_ceiling(torch, batch):
+    """Rate at which this GPU reads the workload's own index-key pages through its block
+    table with the indexer's load pattern and no arithmetic (our probe kernel): the ceiling
+    of the indexer's key stream.  E4M3 pages only (None for MXFP4 keys)."""
+    wl = batch.wl
+    if wl.key_format != "e4m3":
+        return None
+    L = _probe_lib()
+    pages = torch.cat([batch.block_table[b, : (wl.seq_lens[b] + PAGE - 1) // PAGE]
+                       for b in range(wl.num_seqs)]).contiguous()
+    n = pages.numel()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    stride = batch.key_pool.stride(0)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        L.dsa_probe_page_read(batch.key_pool.data_ptr(), stride, pages.data_ptr(), n,
+                              sink.data_ptr(), st)
+    ts = []
+    for _ in range(5):
+        L.dsa_probe_stream_read(flush.data_ptr(), flush.numel(), sink.data_ptr(), 8192, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.dsa_probe_page_read(batch.key_pool.data_ptr(), stride, pages.data_ptr(), n,
+                              sink.data_ptr(), st)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del flush
+    ts.sort()
+    return n * (PAGE * IDX_BYTES_PER_TOKEN) / ts[len(ts) // 2] / 1e9
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def stream_read_ceiling(torch, n_bytes=4 << 30):
@@ -262,6 +308,9 @@ def main():
     ap.add_argument("--separate-topk", action="store_true",
                     help="run stage 2's final pass as its own kernel instead of inside the "
                          "attention kernel")
+    ap.add_argument("--also-splits", type=int, nargs="*", default=None,
+                    help="also time the step at these split counts (default: 16 for the long "
+                         "workload, the split count of the pages' 16-chunk reading)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -281,13 +330,16 @@ def main():
     S = args.splits or wl.num_splits
     torch.cuda.set_device(0)
     batch = synth.make_batch(wl, "cuda")
-    step = dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, S, fused=not args.unfused,
-                          query_on_side_stream=args.query_side_stream,
-                          query_prep=args.query_prep,
-                          select_in_attention=not (args.separate_topk or args.unfused),
-                          store_scores=True if (args.store_scores or args.unfused) else None,
-                          key_format=wl.key_format,
-                          write_selection=False)
+    def make_step(n_splits):
+        return dsa.DecodeStep(wl.n_q, wl.max_seq_len, wl.topk, n_splits, fused=not args.unfused,
+                              query_on_side_stream=args.query_side_stream,
+                              query_prep=args.query_prep,
+                              select_in_attention=not (args.separate_topk or args.unfused),
+                              store_scores=True if (args.store_scores or args.unfused) else None,
+                              key_format=wl.key_format,
+                              write_selection=False)
+
+    step = make_step(S)
     stream = torch.cuda.current_stream()
     probe = _probe_lib()
     flush_buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -299,7 +351,7 @@ def main():
         probe.dsa_probe_stream_read(flush_buf.data_ptr(), flush_buf.numel(), flush_sink.data_ptr(),
                                     8192, stream.cuda_stream)
 
-    def one_step(evs=None):
+    def one_step(evs=None, step=step):
         # stage 3's query quantisation runs on a side stream while stages 1 and 2 run; the
         # step starts at evs[0] on the main stream, which the side stream waits for
         if evs:
@@ -336,17 +388,17 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
-    def timed_steps(with_stages):
+    def timed_steps(with_stages, stp=step):
         per = []
         for _ in range(args.steps):
             if not args.no_flush:
                 flush()                     # outside the events
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             if with_stages:
-                one_step(evs)
+                one_step(evs, stp)
             else:
                 evs[0].record(stream)
-                one_step()
+                one_step(None, stp)
                 evs[3].record(stream)
             per.append(evs)
         torch.cuda.synchronize()
@@ -364,6 +416,19 @@ def main():
     for evs in timed_steps(True):
         for i in range(3):
             stage[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)   # us
+    also = args.also_splits if args.also_splits is not None else ([16] if wl.name == "long" else [])
+    also_us = {}
+    for s2 in also:
+        if s2 == S:
+            continue
+        st2 = make_step(s2)
+        for _ in range(args.warmup):
+            if not args.no_flush:
+                flush()
+            one_step(None, st2)
+        per2 = timed_steps(False, st2)
+        also_us[str(s2)] = round(sum(e[0].elapsed_time(e[3]) * 1e3 for e in per2) / len(per2), 2)
+        del st2
     step_us_sorted = sorted(step_us)
     med = step_us_sorted[len(step_us_sorted) // 2]
     p10 = step_us_sorted[int(0.1 * (len(step_us_sorted) - 1))]
@@ -382,6 +447,7 @@ def main():
     mfma_bound = idx_flops / idx_bytes > FP8_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     traffic = _traffic_from_profile() if wl.name == "long" else None  # counted on `long`
     ceiling = stream_read_ceiling(torch)
+    page_ceiling = page_read_ceiling(torch, batch)
     if args.copy_calibration:
         src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -425,6 +491,7 @@ def main():
                    "mla_query_prep": step.query_prep,
                    "flush_llc_between_steps": not args.no_flush},
         "us_per_layer": round(mean_us, 2),
+        "us_per_layer_at_other_splits": also_us or None,
         "us_per_layer_median": round(med, 2),
         "us_per_layer_p10_p90": [round(p10, 2), round(p90, 2)],
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
@@ -447,6 +514,9 @@ def main():
         "algorithmic_tflop": {"index_score": round(idx_flops / 1e12, 4),
                               "sparse_mla": round(sparse_mla_flops(wl) / 1e12, 4)},
         "stream_read_ceiling_GBps": round(ceiling, 1),
+        "index_page_read_ceiling_GBps": round(page_ceiling, 1) if page_ceiling else None,
+        "index_score_frac_of_page_ceiling": (round(idx_gbps / page_ceiling, 4)
+                                             if page_ceiling and not mfma_bound else None),
         "wall_s_timed_loop": round(t_wall, 4),
         "cpu_baseline": cpu,
         "cache_append": append,

@@ -1,6 +1,7 @@
 // Measurement kernels for the benchmark (not part of the DSA path): the achievable
 // streaming-read rate of this GPU, and the rate of reading whole index-key pages through a
-// block table with the indexer's exact per-lane load pattern but no arithmetic.
+// block table with the indexer's exact per-lane load pattern (non-temporal loads, as the
+// indexer issues them) but no arithmetic: the ceiling the indexer's key stream can reach.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,7 +21,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const v4i* __restrict_
 }
 
 // one wave per page: lane l reads 16-byte pieces 4*(l/32) + j of tokens l%32 and 32 + l%32,
-// then its token's fp32 scale, as the indexer does
+// then its token's fp32 scale, as the indexer does (non-temporal loads)
 __global__ __launch_bounds__(256) void page_read_kernel(const uint8_t* __restrict__ pool,
                                                         int64_t page_stride,
                                                         const int32_t* __restrict__ pages,
@@ -34,8 +35,9 @@ __global__ __launch_bounds__(256) void page_read_kernel(const uint8_t* __restric
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc ^= *reinterpret_cast<const v4i*>(base + (4 * g + j) * 1024 + (32 * hf + n) * 16);
-  acc[0] ^= *reinterpret_cast<const int*>(base + 8192 + 4 * lane);
+      acc ^= __builtin_nontemporal_load(
+          reinterpret_cast<const v4i*>(base + (4 * g + j) * 1024 + (32 * hf + n) * 16));
+  acc[0] ^= __builtin_nontemporal_load(reinterpret_cast<const int*>(base + 8192 + 4 * lane));
   if (acc[0] == 0x7A5C3E1F && acc[1] == 0x1 && acc[2] == 0x2 && acc[3] == 0x3) out[0] = 1;
 }
 

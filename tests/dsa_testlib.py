@@ -10,10 +10,12 @@ import oracle as O
 
 # Tolerances.  Indexer score: |g - o| <= 1e-3 * max(|o|, A) where A is the same head sum with
 # |w| (guards cancellation near zero).  Attention: |g - o| <= 2e-2 + 1e-2 |o| for O (bf16 out),
-# 1e-4 absolute for the LSE.
+# 1e-4 + 1e-5 |lse| for the LSE: its logits are accumulated in fp32 from 576 FP8 products,
+# so their absolute rounding grows with their magnitude (a large common offset, as with
+# latents that share a large mean, moves every logit by the same large amount).
 SCORE_RTOL = 1e-3
 O_ATOL, O_RTOL = 2e-2, 1e-2
-LSE_ATOL = 1e-4
+LSE_ATOL, LSE_RTOL = 1e-4, 1e-5
 
 
 def host(batch):
@@ -78,7 +80,8 @@ def check_attention(o_got, lse_got, o_ref, lse_ref, where=""):
     assert np.array_equal(np.isfinite(lse_got), fin), f"{where}: LSE finiteness differs"
     if fin.any():
         dl = np.abs(lse_got[fin] - lse_ref[fin])
-        assert dl.max() <= LSE_ATOL, f"{where}: LSE max err {dl.max()}"
+        lim = LSE_ATOL + LSE_RTOL * np.abs(lse_ref[fin])
+        assert (dl <= lim).all(), f"{where}: LSE max err {dl.max()} (|lse| up to {np.abs(lse_ref[fin]).max():.1f})"
     return float(d.max()), float(np.abs(lse_got[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
 
 

@@ -3,7 +3,7 @@
 Small ragged batches span several tiles and group tails; the named workloads run at full
 size with sampled rows.  Top-k is compared bit for bit on identical fp32 scores (scores the
 oracle computed, uploaded to both sides); the indexer within 1e-3 relative; attention
-outputs within 2e-2 abs + 1e-2 rel and the LSE within 1e-4.
+outputs within 2e-2 abs + 1e-2 rel and the LSE within 1e-4 + 1e-5 |lse|.
 """
 import math
 import sys
@@ -325,6 +325,56 @@ def test_sparse_mla_merged_in_call(num_splits, prepared):
         assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def _adversarial_mla_case(case):
+    """Latents with a large common mean (every E4M3 latent shifted by +2 and re-encoded) and,
+    for row 0, a query aligned with one selected token's latent so that this token carries
+    almost all the softmax weight (a second one close behind for "two_dominant")."""
+    wl = synth.custom([4096, 3000], [2, 1], topk=2048, seed=95)
+    batch = synth.make_batch(wl, DEV)
+    pool = batch.latent_pool
+    vals = pool.view(torch.float8_e4m3fn).float()
+    batch.latent_pool.copy_((vals + 2.0).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8))
+    rng = np.random.default_rng(96)
+    bt = batch.block_table.cpu().numpy()
+    slots = np.full((wl.n_q, 2048), -1, np.int32)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        n = min(2048, pos + 1)
+        t = np.sort(rng.choice(pos + 1, size=n, replace=False))
+        slots[row, :n] = O.physical_slot(bt[b], t)
+    if case != "large_mean":
+        lat = latent_rows(batch, slots[0]).view(np.uint8)
+        lv = torch.from_numpy(lat.copy()).view(torch.float8_e4m3fn).double().numpy()  # [2048, 576]
+        star = 1234
+        q = lv[star] - lv.mean(axis=0)          # aligned with the chosen token's latent
+        # scale so that the chosen token's logit leads the next one by about 25 nats
+        lg = (lv @ q) * batch.latent_scale * batch.softmax_scale
+        gap = lg[star] - np.max(np.delete(lg, star))
+        q = q * (25.0 / max(gap, 1e-6))
+        qm = np.repeat(q[None], 96, axis=0)
+        if case == "two_dominant":
+            second = 77
+            q2 = lv[second] - lv.mean(axis=0)
+            qm[::2] = 0.5 * qm[::2] + q2 * (25.0 / max(gap, 1e-6)) * 0.5
+        batch.q_mla[0].copy_(torch.from_numpy(qm).to(torch.bfloat16))
+    return wl, batch, slots
+
+
+@pytest.mark.parametrize("case", ["dominant", "two_dominant", "large_mean"])
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_sparse_mla_adversarial_softmax(case, num_splits):
+    # probabilities spanning many orders of magnitude within and across 32-token blocks,
+    # and values with a large common mean: the two-term E4M3 probabilities stay within the
+    # parity tolerance (the oracle takes the exact softmax of the same quantised inputs)
+    say("mla adversarial", case, num_splits)
+    wl, batch, slots = _adversarial_mla_case(case)
+    slots_d = torch.from_numpy(slots).to(DEV)
+    out, lse = run_mla_merged(batch, slots_d, num_splits)
+    o_np, l_np = out.float().cpu().numpy(), lse.cpu().numpy()
+    for row in range(wl.n_q):
+        o_ref, l_ref = O.lse_combine(_oracle_attention(batch, row, slots[row], num_splits))
+        check_attention(o_np[row], l_np[row], o_ref, l_ref, f"{case} row {row} S={num_splits}")
+
+
 def test_sparse_mla_topk_equal_to_context_is_dense_mla():
     wl = synth.custom([2048], [1], topk=2048, seed=42)
     batch = synth.make_batch(wl, DEV)
@@ -434,6 +484,13 @@ def test_end_to_end_spec_full_size():
 def test_end_to_end_long_full_size():
     wl = synth.workload("long")
     _end_to_end(wl, rows=[0, 13, 31])
+
+
+def test_end_to_end_long_full_size_16_splits():
+    # the 16 contiguous chunks of the pages' reading of the long decode: each split
+    # attends 128 of the row's 2,048 selected tokens
+    wl = synth.workload("long")
+    _end_to_end(wl, rows=[0, 31], num_splits=16)
 
 
 @pytest.mark.slow
