@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   //  value waves 6, 7  the values of all three head tiles for dim tiles 3 (w-6) .. +2
   //                    (9 accumulators).
   auto run = [&](auto role) {
-    constexpr bool DUTY = decltype(role)::value;
+    constexpr int ROLE = decltype(role)::value;  // 0: duty, PV first; 1: duty, PV last; 2: value
+    constexpr bool DUTY = ROLE < 2;
+    constexpr bool PV_FIRST = ROLE != 1;
     constexpr int NH = DUTY ? 1 : 3;  // head tiles whose values this wave accumulates
     constexpr int ND = DUTY ? 5 : 3;  // dim tiles (32 dims each)
     const int ht_d = wave >> 1, blk = wave & 1;
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       const uint8_t* tile = &sm.lat[0][0] + tile_off;
 
       if constexpr (DUTY) {
-        if (t > 0) values_of(t - 1, n, g);
+        if (PV_FIRST && t > 0) values_of(t - 1, n, g);
         if (t < n_tiles) {
           issue(t + 2, 0, 2);
           // ---- logits of head tile ht_d, tokens 32 blk .. +31 of tile t: lane (n, g) gets
@@ -574,6 +576,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
             sm.bsum[pb][ht_d][blk][n] = zs * (1.0f / 256.0f);
           }
         }
+        // the second duty wave of a SIMD takes the values product last: its softmax then
+        // runs while the other duty wave's matrix products do
+        if (!PV_FIRST && t > 0) values_of(t - 1, n, g);
       } else {
         if (t < n_tiles) issue(t + 2, 0, 5);
         if (t > 0) values_of(t - 1, n, g);
@@ -657,10 +662,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     else
       emit(std::integral_constant<int, kPartF32>{});
   };
-  if (wave < kDutyWaves)
-    run(std::true_type{});
+  // waves w and w + 4 share a SIMD: waves 0..3 and 6, 7 run their products first, the
+  // duty waves 4, 5 (on the SIMDs of duty waves 0, 1) last
+  if (wave < 4)
+    run(std::integral_constant<int, 0>{});
+  else if (wave < kDutyWaves)
+    run(std::integral_constant<int, 1>{});
   else
-    run(std::false_type{});
+    run(std::integral_constant<int, 2>{});
 }
 
 }  // namespace
