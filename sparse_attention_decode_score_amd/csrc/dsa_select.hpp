@@ -1,6 +1,7 @@
 // Exact selection primitives of the top-k stage: order-preserving keys, the per-group
-// candidate rule, one wave's top-m of a 256-token group (ballots only, keys in registers)
-// and one 512-thread workgroup's top-k of up to 16,384 keys (bitwise threshold search).
+// candidate rule, one wave's top-m of a 256-token group (a radix select on the wave's own LDS
+// counters, keys in registers) and one 512-thread workgroup's top-k of up to 32,768 keys held
+// in registers (a radix select with 8-bit digits), with slower paths for more.
 //
 // Total order everywhere: larger key first, equal keys by lower element index (token order).
 #pragma once
