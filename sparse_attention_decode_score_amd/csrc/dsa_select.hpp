@@ -21,7 +21,14 @@ constexpr int kFinalPerThread = 32;     // keys per thread of the on-chip candid
 constexpr int kFinalRegPerThread = 64;  // keys per thread the selection holds in registers
 constexpr int kRadixBits = 8;                  // key bits one pass of the final selection settles
 constexpr int kRadixBins = 1 << kRadixBits;
-constexpr int kHistWords = 3 * kRadixBins;     // LDS counters of the final selection
+// The final selection's histogram of a pass is kept in four copies (lane % 4 picks one), so
+// that lanes of one instruction adding to a crowded digit hit four addresses instead of one
+// (LDS serialises atomics on one address); a copy is 260 words, so one digit's four copies
+// sit on four different banks and each lane's four digits stay 16-byte aligned.
+constexpr int kHistCopies = 4;
+constexpr int kHistStride = kRadixBins + 4;
+constexpr int kHistSet = kHistCopies * kHistStride;  // one pass's counters
+constexpr int kHistWords = 3 * kHistSet;             // three in rotation
 constexpr int kFinalTile = kFinalThreads * kFinalPerThread;  // keys the final pass holds in LDS
 constexpr int kFinalRegTile = kFinalThreads * kFinalRegPerThread;  // ... and in registers
 
@@ -317,7 +324,7 @@ __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], Val val, int k, int* 
                                   int* note, uint32_t* hist) {
   const int tid = threadIdx.x, lane = tid & 63;
   int parity = 0;
-  for (int i = tid; i < 2 * kRadixBins; i += kFinalThreads) hist[i] = 0u;
+  for (int i = tid; i < 2 * kHistSet; i += kFinalThreads) hist[i] = 0u;
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
@@ -335,20 +342,23 @@ __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], Val val, int k, int* 
     for (int pass = 0; lo_bit > 0; ++pass) {  // uniform
       const int width = lo_bit < kRadixBits ? lo_bit : kRadixBits;
       const int sh = lo_bit - width;
-      uint32_t* h = hist + kRadixBins * (pass % 3);
+      uint32_t* h = hist + kHistSet * (pass % 3);
       if (pass > 0) {
-        uint32_t* h2 = hist + kRadixBins * ((pass + 1) % 3);
-        for (int i = tid; i < kRadixBins; i += kFinalThreads) h2[i] = 0u;
+        uint32_t* h2 = hist + kHistSet * ((pass + 1) % 3);
+        for (int i = tid; i < kHistSet; i += kFinalThreads) h2[i] = 0u;
       }
       const uint64_t want = (uint64_t)prefix >> lo_bit;  // the bits found so far
+      uint32_t* const hc = h + kHistStride * (lane & (kHistCopies - 1));
 #pragma unroll
       for (int j = 0; j < E; ++j)
         if (kv[j] != kSentinel && ((uint64_t)kv[j] >> lo_bit) == want)
-          atomicAdd(&h[__builtin_amdgcn_ubfe(kv[j], sh, width)], 1u);
+          atomicAdd(&hc[__builtin_amdgcn_ubfe(kv[j], sh, width)], 1u);
       __syncthreads();
-      // lane l holds the counts of digits 4l .. 4l+3; suffix sums over the digits, from the
-      // lane's own four and the totals of the lanes above it
-      const v4i c4 = *reinterpret_cast<const v4i*>(&h[4 * lane]);
+      // lane l holds the counts of digits 4l .. 4l+3 (summed over the copies); suffix sums
+      // over the digits, from the lane's own four and the totals of the lanes above it
+      v4i c4 = *reinterpret_cast<const v4i*>(&h[4 * lane]);
+#pragma unroll
+      for (int c = 1; c < kHistCopies; ++c) c4 += *reinterpret_cast<const v4i*>(&h[kHistStride * c + 4 * lane]);
       const int s3 = c4[3], s2 = s3 + c4[2], s1 = s2 + c4[1], s0 = s1 + c4[0];
       const int incl = wave_incl_scan(s0);
       const int above_lane = __builtin_amdgcn_readlane(incl, 63) - incl;
