@@ -53,7 +53,16 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // resent (read again in full) by the final pass; for independent scores that is about one
 // group in 10^5 rows at lambda = 4 (131,072 visible tokens, k = 2,048: m = 16) and rarer at
 // smaller lambda (1,048,576 tokens: lambda = 1/2, m = 8, 32,768 candidates).
+#ifndef DSA_FULL_ROW_MAX
+#define DSA_FULL_ROW_MAX (kFinalThreads * kFinalRegPerThread)
+#endif
+// Rows of at most this many visible tokens keep every token (m = 256, "full" rows): the final
+// pass then selects from the whole row in registers, which costs less than a first-pass
+// selection that would keep a large share of each group anyway (m >= 64 below 32,768 tokens).
+constexpr int kFullRowMax = DSA_FULL_ROW_MAX;
+static_assert(kFullRowMax <= kFinalThreads * kFinalRegPerThread, "full rows fit the registers");
 __host__ __device__ __forceinline__ int group_cand_count(int n_vis, int k) {
+  if (n_vis <= kFullRowMax) return kGroupTok;
   const int64_t num = 4 * (int64_t)k * kGroupTok;  // 4 lambda n_vis
   int64_t m = (num + n_vis - 1) / n_vis;           // ceil(4 lambda)
   if (num < 16 * (int64_t)n_vis) {                 // lambda < 4
@@ -128,15 +137,18 @@ __device__ __forceinline__ void group_select(const uint32_t (&keys)[4], int n, i
 #pragma unroll
   for (int j = 0; j < 4; ++j) kv[j] = (64 * j + lane < n) ? keys[j] : kSentinel;
   if (n <= m) {
+    // with m = 256 (a full row) the slots hold the row's tokens in order: the final pass
+    // takes a slot's token from its position and reads no group record, so neither is written
+    const bool full = m == kGroupTok;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = 64 * j + lane;
       if (i < m) {
         ck[i] = kv[j];
-        ci[i] = i < n ? t0 + i : 0x7FFFFFFF;
+        if (!full) ci[i] = i < n ? t0 + i : 0x7FFFFFFF;
       }
     }
-    if (lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
+    if (!full && lane == 0) *inf = ChunkInfo{n, 0, 0u, -1};
     return;
   }
   // K = the m-th largest key, found 8 bits at a time (a radix select within the wave).  The

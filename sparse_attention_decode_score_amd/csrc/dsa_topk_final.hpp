@@ -436,9 +436,12 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
     const uint32_t* ck = cand_key + (int64_t)row * row_cap;
     const int32_t* ci = cand_idx + (int64_t)row * row_cap;
     const ChunkInfo* inf = info + (int64_t)row * num_groups;
+    // a full row (m = 256): its candidate slots are the row's tokens in order, no group
+    // record was written and none can hide a winner
+    const bool full = m == kGroupTok;
     // this thread's first group record, loaded now so that the flag check after the
     // selection does not wait for it
-    const ChunkInfo info0 = inf[min(tid, n_groups - 1)];
+    const ChunkInfo info0 = full ? ChunkInfo{0, 0, 0u, 0} : inf[min(tid, n_groups - 1)];
     KthKey kth;
     if (n_cand <= kFinalRegTile) {
       // this thread's E consecutive candidates straight into registers (n_cand and the
@@ -460,7 +463,8 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
 #pragma unroll
           for (int j = 0; j < 4; ++j) kv[4 * q + j] = in ? (uint32_t)a[q][j] : kSentinel;
         }
-        kth = block_topk_regs<E>(kv, [ci](int e) { return ci[e]; }, k, out, red, note_p, hist);
+        kth = block_topk_regs<E>(kv, [ci, full](int e) { return full ? e : ci[e]; }, k, out,
+                                 red, note_p, hist);
       };
       switch (final_per_thread(n_cand)) {
         case 8: run(std::integral_constant<int, 8>()); break;
@@ -479,11 +483,12 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
       return ic.saturated && (ic.key > K || (ic.key == K && ic.idx < I));
     };
     auto flagged = [&](int g) { return flag_of(inf[g]); };
-    int any = tid < n_groups && flag_of(info0) ? 1 : 0;
+    int any = !full && tid < n_groups && flag_of(info0) ? 1 : 0;
 #pragma unroll 4
-    for (int g = tid + kFinalThreads; g < n_groups; g += kFinalThreads) any |= flagged(g) ? 1 : 0;
+    for (int g = tid + kFinalThreads; !full && g < n_groups; g += kFinalThreads)
+      any |= flagged(g) ? 1 : 0;
     int parity = 0;
-    if (block_sum(any, red, parity) > 0) {
+    if (!full && block_sum(any, red, parity) > 0) {
       before_scratch();
       final_resend(ResendArgs{row, n_vis, k, n_groups, m, parity, K, I, ck, ci, inf, rs, bt_row,
                               row_scores, out, lkey, lidx, red, note_p, hist, rq8, rw});

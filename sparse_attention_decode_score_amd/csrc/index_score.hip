@@ -303,12 +303,13 @@ __global__ __launch_bounds__(256) void index_score_kernel(
         const int n_grp = min(g_lo + seg_groups, (n_vis + kGroupTok - 1) / kGroupTok) - g_lo;
         if (n_grp <= 0) continue;
         const int m = group_cand_count(n_vis, cand.k);
+        const bool full = m == kGroupTok;  // keys only (group_select wrote nothing else)
         const int64_t base = (int64_t)row * cand.row_cap + (int64_t)g_lo * m;
         for (int i = tid; i < n_grp * m; i += 256) {
           cand.key[base + i] = cbuf_key[r][i];
-          cand.idx[base + i] = cbuf_idx[r][i];
+          if (!full) cand.idx[base + i] = cbuf_idx[r][i];
         }
-        for (int i = tid; i < n_grp; i += 256)
+        for (int i = tid; !full && i < n_grp; i += 256)
           cand.info[(int64_t)row * cand.num_groups + g_lo + i] = cbuf_info[r][i];
       }
     }
