@@ -123,8 +123,12 @@ __device__ __forceinline__ void quantize_mla_rows(const MlaQueryPrep& pp, int r0
 // loads and stores in one counter that may complete out of order, so a store in flight,
 // or loads under data-dependent branches, would force a full drain of the ring at every
 // wait instead of a wait for the oldest page only.
+// Eight-row groups are held to three workgroups per CU (168 VGPRs, three waves per SIMD: the
+// LDS of three fits): their rows' products and selections are latency-bound, and the third
+// wave hides more of it than the registers it costs (a few spills; speculative decode
+// indexer 44 -> 35 us).
 template <int R, bool CAND, bool MX>
-__global__ __launch_bounds__(256) void index_score_kernel(
+__global__ __launch_bounds__(256, (R == 8 ? 3 : 1)) void index_score_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ head_w,
     const uint8_t* __restrict__ key_pages, int64_t page_stride,
