@@ -198,6 +198,20 @@ dsa_status dsa_index_score_quantize_q(int32_t num_seqs, int32_t n_q, int32_t max
  *   [n_q][score_stride] fp32 whose contents need no initialisation.
  */
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k);
+
+/*
+ * The top-k workspace's layout record.  Its first 256 bytes hold (magic, k, max_seq_len, n_q,
+ * status), written by the call that writes the candidates (dsa_index_score* with a workspace,
+ * or dsa_topk's own first pass).  A final pass (dsa_topk with from_candidates = 1, or
+ * dsa_topk_sparse_mla) whose (k, max_seq_len, n_q) differ from the record's reads the
+ * candidates of another layout: it selects nothing (every row's topk_idx / topk_slot -1, and
+ * in dsa_topk_sparse_mla O = 0, LSE = -inf) and sets status to 1.  This call reads the
+ * record (it waits for `stream`: a diagnostic, not for the hot path) and returns DSA_OK, or
+ * DSA_ERR_WORKSPACE when no record was written or a final pass found a mismatch (the message
+ * names the record's values).  workspace_bytes >= 256.
+ */
+dsa_status dsa_topk_workspace_status(const void* workspace, size_t workspace_bytes, void* stream);
+
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
                     const int32_t* seq_lens, float* scores, int64_t score_stride, int32_t k,
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,

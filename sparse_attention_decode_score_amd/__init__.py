@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_index_score_quantize_q.argtypes = [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I64,
                                                  _I32, _P, _I32, _P, _I64, _I32, _P, _SZ, _P, _P,
                                                  _P, _P]
+        L.dsa_topk_workspace_status.argtypes = [_P, _SZ, _P]
         L.dsa_topk_workspace_size.argtypes = [_I32, _I32, _I32]
         L.dsa_topk_workspace_size.restype = _SZ
         L.dsa_topk.argtypes = [_I32, _I32, _I32, _P, _P, _P, _I64, _I32, _P, _I32, _P, _P, _P, _SZ,
@@ -227,6 +228,14 @@ def _rescore_args(rescore, key_format):
 
 def dsa_topk_workspace_size(n_q: int, max_seq_len: int, k: int) -> int:
     return int(lib().dsa_topk_workspace_size(int(n_q), int(max_seq_len), int(k)))
+
+
+def dsa_topk_workspace_status(workspace: torch.Tensor, stream=None) -> None:
+    """Reads the top-k workspace's layout record (waits for the stream): raises DsaError if no
+    call wrote candidates into it, or if a final pass found them written for another
+    (k, max_seq_len, n_q) and therefore selected nothing."""
+    _check(lib().dsa_topk_workspace_status(_ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                                           _stream(stream)))
 
 
 def dsa_topk(cu_q: torch.Tensor, seq_lens: torch.Tensor, scores: torch.Tensor, k: int,

@@ -243,6 +243,27 @@ size_t dsa_topk_workspace_size(int32_t n_q, int32_t max_seq_len, int32_t k) {
   return dsa::topk_workspace_bytes(n_q, max_seq_len, k);
 }
 
+dsa_status dsa_topk_workspace_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  DSA_REQUIRE(workspace != nullptr, "workspace must be non-null");
+  DSA_REQUIRE(workspace_bytes >= dsa::kWsHeaderBytes, "workspace_bytes (%zu) must be >= %zu",
+              workspace_bytes, dsa::kWsHeaderBytes);
+  int32_t h[5] = {0, 0, 0, 0, 0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(h, workspace, sizeof h, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess)
+    return fail(DSA_ERR_LAUNCH, "reading the workspace's layout record: %s", hipGetErrorString(e));
+  if (h[0] != dsa::kWsMagic)
+    return fail(DSA_ERR_WORKSPACE, "the workspace holds no layout record: no call wrote "
+                                   "candidates into it");
+  if (h[4] != 0)
+    return fail(DSA_ERR_WORKSPACE,
+                "a final top-k pass found candidates written for k = %d, max_seq_len = %d, "
+                "n_q = %d, which differ from its own arguments, and selected nothing",
+                h[1], h[2], h[3]);
+  return ok();
+}
+
 dsa_status dsa_topk(int32_t num_seqs, int32_t n_q, int32_t max_seq_len, const int32_t* cu_q,
                     const int32_t* seq_lens, float* scores, int64_t score_stride, int32_t k,
                     const int32_t* block_table, int32_t bt_stride, int32_t* topk_idx,

@@ -24,11 +24,23 @@ struct IndexRescore {
   int mxfp4;               // key cache format: 0 E4M3 + fp32 scale, 1 MXFP4
 };
 
+// The first 256 bytes of a top-k workspace hold a layout record: the pass that writes the
+// candidates (the indexer, or the first pass of dsa_topk) stores (magic, k, max_seq_len, n_q,
+// status = 0); the final pass compares it with its own arguments, and on a mismatch (the two
+// calls disagree about where the candidates lie) selects nothing (-1) and sets status to 1.
+constexpr int32_t kWsMagic = 0x44534131;  // "DSA1"
+constexpr size_t kWsHeaderBytes = 256;
+struct WsLayout {
+  int32_t* header;  // the workspace's first bytes
+  int k, max_seq_len, n_q;
+};
+
 struct TopkBuffers {
   TopkPlan plan;
   uint32_t* cand_key;
   int32_t* cand_idx;
   ChunkInfo* info;
+  WsLayout layout;
 };
 
 TopkPlan topk_plan(int max_seq_len, int k);

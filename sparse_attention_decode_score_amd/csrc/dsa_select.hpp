@@ -7,6 +7,7 @@
 #pragma once
 
 #include "dsa_device.hpp"
+#include "dsa_internal.hpp"
 
 namespace dsa {
 
@@ -39,6 +40,22 @@ struct ChunkInfo {
   uint32_t key;   // its m-th element (when saturated): key and token index
   int idx;
 };
+
+// The top-k workspace's layout record (see WsLayout): written once per launch by the pass
+// that fills the candidates, checked by the final pass.
+__device__ __forceinline__ void write_ws_layout(const WsLayout& l) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+    *reinterpret_cast<v4i*>(l.header) = v4i{kWsMagic, l.k, l.max_seq_len, l.n_q};
+    l.header[4] = 0;
+  }
+}
+__device__ __forceinline__ bool ws_layout_ok(const WsLayout& l) {
+  const v4i h = *reinterpret_cast<const v4i*>(l.header);
+  return h[0] == kWsMagic && h[1] == l.k && h[2] == l.max_seq_len && h[3] == l.n_q;
+}
+__device__ __forceinline__ void flag_ws_layout(const WsLayout& l) {
+  if (threadIdx.x == 0) l.header[4] = 1;
+}
 
 // Score -> key: larger score = larger key, -0.0 == +0.0, NaN just above the sentinel.
 __device__ __forceinline__ uint32_t score_key(float f) {

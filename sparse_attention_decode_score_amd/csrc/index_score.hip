@@ -57,6 +57,7 @@ struct CandOut {
   int64_t row_cap;
   int num_groups;
   int k;
+  WsLayout layout;  // the workspace's layout record, written by one thread of the launch
 };
 
 // E4M3 codes and power-of-two scale of one (row, head) of dim = 64 * PPL values: 8
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(256, (R == 8 ? 3 : 1)) void index_score_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t ghist[CAND ? kWaves : 1][256];  // per wave
 
   const int G = groups_per_wave;  // <= Cfg::kMaxGroups (host-checked)
+  if constexpr (CAND) write_ws_layout(cand.layout);
   const int b = blockIdx.y;
   const int q0 = cu_q[b], q1 = cu_q[b + 1];
   const int r0 = q0 + (int)blockIdx.z * R;
@@ -384,10 +386,11 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
   // with a query preparation, one more x slice of workgroups: the MLA query rows of each
   // (request, row group)
   const dim3 grid(gx + (prep.q ? 1u : 0u), (unsigned)num_seqs, gz), block(256);
-  CandOut cand{nullptr, nullptr, nullptr, 0, 0, k};
+  CandOut cand{nullptr, nullptr, nullptr, 0, 0, k, WsLayout{nullptr, 0, 0, 0}};
   if (topk_ws) {
     const TopkBuffers t = topk_buffers(topk_ws, n_q, max_seq_len, k);
-    cand = CandOut{t.cand_key, t.cand_idx, t.info, (int64_t)t.plan.row_cap, t.plan.num_groups, k};
+    cand = CandOut{t.cand_key, t.cand_idx, t.info, (int64_t)t.plan.row_cap, t.plan.num_groups, k,
+                   t.layout};
   }
 #define DSA_LAUNCH_IDX(RR, CC)                                                                    \
   do {                                                                                           \

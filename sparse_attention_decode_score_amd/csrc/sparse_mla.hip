@@ -195,6 +195,7 @@ struct SelectArgs {
   int bt_stride;
   int32_t* topk_idx;   // optional outputs, written by split 0 of each row
   int32_t* topk_slot;
+  WsLayout layout;     // the candidate workspace's layout record
 };
 
 template <bool SELECT>
@@ -269,9 +270,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       __syncthreads();
       q_in_lds = false;
     };
-    const int n_out = final_select_row(row, pos + 1, sel.scores, sel.score_stride, k,
-                                       sel.num_groups, sel.row_cap, sel.cand_key, sel.cand_idx,
-                                       sel.info, sel.rs, bt, slot_l, sc, before_resend);
+    // candidates written for another layout: nothing is selected (see WsLayout)
+    const bool layout_ok = ws_layout_ok(sel.layout);
+    if (!layout_ok && s == 0) flag_ws_layout(sel.layout);
+    const int n_out = layout_ok ? final_select_row(row, pos + 1, sel.scores, sel.score_stride, k,
+                                                   sel.num_groups, sel.row_cap, sel.cand_key,
+                                                   sel.cand_idx, sel.info, sel.rs, bt, slot_l, sc,
+                                                   before_resend)
+                                : 0;
     auto to_slot = [&](int t) { return t < 0 ? -1 : bt[t >> 6] * kPage + (t & (kPage - 1)); };
     if (s == 0 && (sel.topk_idx || sel.topk_slot)) {
       for (int i = threadIdx.x; i < k; i += kThreads) {
@@ -787,7 +793,7 @@ hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
                                   float* lse, void* workspace, hipStream_t st) {
   const SelectArgs sel{cu_q, seq_lens, num_seqs, scores, score_stride, t.plan.num_groups,
                        (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info, rs, block_table,
-                       bt_stride, topk_idx, topk_slot};
+                       bt_stride, topk_idx, topk_slot, t.layout};
   return launch_mla_common(&sel, n_q, q, q8, q_scale, latent_pages, latent_page_stride,
                            latent_scale, nullptr, k, softmax_scale, num_splits, nullptr, nullptr,
                            out_bf16, lse, workspace, st);

@@ -36,8 +36,9 @@ __global__ __launch_bounds__(256) void topk_group_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int num_seqs,
     const float* __restrict__ scores, int64_t score_stride, int k, int num_groups,
     int64_t row_cap, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx,
-    ChunkInfo* __restrict__ info) {
+    ChunkInfo* __restrict__ info, WsLayout layout) {
   __shared__ __attribute__((aligned(16))) uint32_t ghist[4][256];  // per wave
+  write_ws_layout(layout);
   const int row = blockIdx.y;
   int b, pos;
   row_of(cu_q, seq_lens, num_seqs, row, b, pos);
@@ -63,7 +64,8 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
     float* scores, int64_t score_stride, int k, int num_groups, int64_t row_cap,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
     const ChunkInfo* __restrict__ info, IndexRescore rs, const int32_t* __restrict__ block_table,
-    int bt_stride, int32_t* __restrict__ topk_idx, int32_t* __restrict__ topk_slot) {
+    int bt_stride, int32_t* __restrict__ topk_idx, int32_t* __restrict__ topk_slot,
+    WsLayout layout) {
   __shared__ __attribute__((aligned(16))) uint32_t lkey[kFinalTile];
   __shared__ __attribute__((aligned(16))) int32_t lidx[kFinalTile];
   __shared__ int out[kMaxTopk];
@@ -78,8 +80,12 @@ __global__ __launch_bounds__(kFinalThreads) void topk_final_kernel(
   int32_t* os = topk_slot ? topk_slot + (int64_t)row * k : nullptr;
   const int32_t* bt = block_table ? block_table + (int64_t)b * bt_stride : nullptr;
   FinalScratch sc{lkey, lidx, red, &note, hist};
-  const int n_out = final_select_row(row, n_vis, scores, score_stride, k, num_groups, row_cap,
-                                     cand_key, cand_idx, info, rs, bt, out, sc);
+  // candidates written for another layout: nothing is selected (see WsLayout)
+  const bool layout_ok = ws_layout_ok(layout);
+  if (!layout_ok) flag_ws_layout(layout);
+  const int n_out = layout_ok ? final_select_row(row, n_vis, scores, score_stride, k, num_groups,
+                                                 row_cap, cand_key, cand_idx, info, rs, bt, out, sc)
+                              : 0;
 #pragma unroll 8
   for (int i = tid; i < k; i += kFinalThreads) {
     const int t = i < n_out ? out[i] : -1;
@@ -113,7 +119,8 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t topk_workspace_bytes(int n_q, int max_seq_len, int k) {
   const TopkPlan p = topk_plan(max_seq_len, k);
   const size_t nc = (size_t)n_q * p.row_cap;
-  return align256(nc * 4) * 2 + align256((size_t)n_q * p.num_groups * sizeof(ChunkInfo));
+  return kWsHeaderBytes + align256(nc * 4) * 2 +
+         align256((size_t)n_q * p.num_groups * sizeof(ChunkInfo));
 }
 
 TopkBuffers topk_buffers(void* workspace, int n_q, int max_seq_len, int k) {
@@ -121,6 +128,8 @@ TopkBuffers topk_buffers(void* workspace, int n_q, int max_seq_len, int k) {
   const size_t nc = (size_t)n_q * p.row_cap;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   TopkBuffers t;
+  t.layout = WsLayout{reinterpret_cast<int32_t*>(ws), k, max_seq_len, n_q};
+  ws += kWsHeaderBytes;
   t.plan = p;
   t.cand_key = reinterpret_cast<uint32_t*>(ws);
   t.cand_idx = reinterpret_cast<int32_t*>(ws + align256(nc * 4));
@@ -137,7 +146,7 @@ hipError_t launch_topk_final(int num_seqs, int n_q, const int32_t* cu_q, const i
   hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)n_q), dim3(kFinalThreads), 0, st, cu_q,
                      seq_lens, num_seqs, const_cast<float*>(scores), score_stride, k,
                      t.plan.num_groups, (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info,
-                     rs, block_table, bt_stride, topk_idx, topk_slot);
+                     rs, block_table, bt_stride, topk_idx, topk_slot, t.layout);
   return hipGetLastError();
 }
 
@@ -148,7 +157,8 @@ hipError_t launch_topk(int num_seqs, int n_q, int max_seq_len, const int32_t* cu
   const TopkBuffers t = topk_buffers(workspace, n_q, max_seq_len, k);
   hipLaunchKernelGGL(topk_group_kernel, dim3((unsigned)((t.plan.num_groups + 3) / 4), (unsigned)n_q),
                      dim3(256), 0, st, cu_q, seq_lens, num_seqs, scores, score_stride, k,
-                     t.plan.num_groups, (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info);
+                     t.plan.num_groups, (int64_t)t.plan.row_cap, t.cand_key, t.cand_idx, t.info,
+                     t.layout);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_final(num_seqs, n_q, cu_q, seq_lens, scores, score_stride, k, t,

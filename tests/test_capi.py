@@ -275,6 +275,15 @@ def test_validate_batch_accepts_a_valid_batch_and_names_each_violation(L):
     assert "bt_stride" in _err()
 
 
+def test_topk_workspace_status_rejects_bad_host_args(L):
+    # argument checks run before any device access, so they need no GPU
+    L.dsa_topk_workspace_status.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert L.dsa_topk_workspace_status(None, 4096, None) == 1
+    assert b"non-null" in L.dsa_last_error()
+    assert L.dsa_topk_workspace_status(ctypes.c_void_p(256), 64, None) == 1
+    assert b">= 256" in L.dsa_last_error()
+
+
 def test_validate_slots(L):
     import numpy as np
     dsa.dsa_validate_slots(np.array([0, 5, -1, 64 * 9 + 63], np.int32), 10)

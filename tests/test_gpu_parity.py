@@ -577,6 +577,76 @@ def test_fused_index_topk_is_bitwise_the_stage_by_stage_path(wl):
     assert torch.equal(i1, i2) and torch.equal(t1, t2)
 
 
+def test_final_pass_selects_nothing_from_candidates_of_another_layout():
+    # the indexer writes candidates for a top-2,048; a final pass asked for a top-1,024 would
+    # read them with another row and group layout: it selects nothing, and the workspace
+    # record reports it; calls that agree select the exact top-k and leave the record clean
+    say("workspace layout record")
+    wl = synth.custom([5000, 3000], [2, 1], topk=2048, seed=71, name="layout")
+    batch = synth.make_batch(wl, DEV)
+    k_idx = 2048
+    ws = dsa.workspace(max(dsa.dsa_topk_workspace_size(wl.n_q, wl.max_seq_len, kk)
+                           for kk in (1024, 2048)))
+    scores = torch.full((wl.n_q, wl.max_seq_len), float("nan"), device=DEV)
+
+    def index():
+        dsa.dsa_index_score(batch.cu_q, batch.seq_lens, batch.q_idx, batch.head_w, batch.key_pool,
+                            batch.block_table, scores, max_seq_len=wl.max_seq_len,
+                            max_q_per_seq=max(wl.q_per_seq), cand_k=k_idx, cand_workspace=ws)
+
+    def final(k):
+        idx = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+        slot = torch.full((wl.n_q, k), -7, dtype=torch.int32, device=DEV)
+        dsa.dsa_topk(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, idx, slot, ws,
+                     max_seq_len=wl.max_seq_len, from_candidates=True)
+        torch.cuda.synchronize()
+        return idx, slot
+
+    def attend(k):
+        out = torch.full((wl.n_q, 96, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((wl.n_q, 96), float("nan"), dtype=torch.float32, device=DEV)
+        dsa.dsa_topk_sparse_mla(batch.cu_q, batch.seq_lens, scores, k, batch.block_table, ws,
+                                batch.q_mla, batch.latent_pool, batch.latent_scale,
+                                batch.softmax_scale, 2, max_seq_len=wl.max_seq_len, out=out,
+                                lse=lse)
+        torch.cuda.synchronize()
+        return out, lse
+
+    index()
+    idx, slot = final(1024)
+    assert bool((idx == -1).all()) and bool((slot == -1).all())
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_topk_workspace_status(ws)
+    index()
+    out, lse = attend(1024)
+    assert bool((out.float() == 0).all()) and bool(torch.isneginf(lse).all())
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_topk_workspace_status(ws)
+    index()
+    idx, slot = final(k_idx)
+    dsa.dsa_topk_workspace_status(ws)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        n = min(k_idx, pos + 1)
+        ref = np.sort(O.topk_indices(scores[row, : pos + 1].cpu().numpy(), k_idx))
+        assert np.array_equal(idx[row, :n].cpu().numpy(), ref), row
+
+
+def test_full_row_boundary_selects_the_exact_topk():
+    # rows of up to 32,768 visible tokens send every key to the final pass (full rows); a row
+    # of 32,769 goes through the first-pass groups: both give the exact top-k of the scores,
+    # with and without stored scores
+    say("full-row boundary")
+    wl = synth.custom([32768, 32769, 16385], [2, 2, 1], topk=2048, seed=66, name="full-row-edge")
+    batch = synth.make_batch(wl, DEV)
+    s1, i1, t1 = _stage_by_stage(batch, 2048)
+    s2, i2, t2 = _fused(batch, 2048)
+    assert torch.equal(i1, i2) and torch.equal(t1, t2)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref = np.sort(O.topk_indices(s2[row, : pos + 1].cpu().numpy(), 2048))
+        assert np.array_equal(i2[row].cpu().numpy(), ref), row
+    _check_no_scores_matches(batch, 2048, expect_rescored=None)
+
+
 @pytest.mark.parametrize("wl", [
     SMALL[0], SMALL[3], FUSED[4], FUSED[5],
     synth.custom([5000, 4097], [4, 5], topk=2048, seed=87, name="mx-prep", key_format="mxfp4"),
