@@ -217,17 +217,19 @@ def _probe_lib():
                                         ctypes.c_int, ctypes.c_void_p]
     L.dsa_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.dsa_probe_page_read_mx.argtypes = L.dsa_probe_page_read.argtypes
     return L
 
 
 def page_read_ceiling(torch, batch):
     """Rate at which this GPU reads the workload's own index-key pages through its block
     table with the indexer's load pattern and no arithmetic (our probe kernel): the ceiling
-    of the indexer's key stream.  E4M3 pages only (None for MXFP4 keys)."""
+    of the indexer's key stream, for E4M3 (8,448-byte) or MXFP4 (4,352-byte) pages."""
     wl = batch.wl
-    if wl.key_format != "e4m3":
-        return None
     L = _probe_lib()
+    mx = wl.key_format == "mxfp4"
+    read = L.dsa_probe_page_read_mx if mx else L.dsa_probe_page_read
+    page_bytes = PAGE * (MX_IDX_BYTES_PER_TOKEN if mx else IDX_BYTES_PER_TOKEN)
     pages = torch.cat([batch.block_table[b, : (wl.seq_lens[b] + PAGE - 1) // PAGE]
                        for b in range(wl.num_seqs)]).contiguous()
     n = pages.numel()
@@ -236,21 +238,19 @@ def page_read_ceiling(torch, batch):
     stride = batch.key_pool.stride(0)
     flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     for _ in range(2):
-        L.dsa_probe_page_read(batch.key_pool.data_ptr(), stride, pages.data_ptr(), n,
-                              sink.data_ptr(), st)
+        read(batch.key_pool.data_ptr(), stride, pages.data_ptr(), n, sink.data_ptr(), st)
     ts = []
     for _ in range(5):
         L.dsa_probe_stream_read(flush.data_ptr(), flush.numel(), sink.data_ptr(), 8192, st)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        L.dsa_probe_page_read(batch.key_pool.data_ptr(), stride, pages.data_ptr(), n,
-                              sink.data_ptr(), st)
+        read(batch.key_pool.data_ptr(), stride, pages.data_ptr(), n, sink.data_ptr(), st)
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e-3)
     del flush
     ts.sort()
-    return n * (PAGE * IDX_BYTES_PER_TOKEN) / ts[len(ts) // 2] / 1e9
+    return n * page_bytes / ts[len(ts) // 2] / 1e9
 
 
 def cpu_model():
