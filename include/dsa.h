@@ -111,8 +111,11 @@ typedef enum {
  *            same q_bf16 / head_w / key cache (pass them there).
  *   cand_k, cand_workspace, cand_workspace_bytes: if cand_workspace is not NULL the
  *            scoring waves also write, for a top-k of cand_k (1..4096), every 256-token
- *            group's best candidates (4x the winners a full group holds on average, in
- *            token order) and the group's boundary element into it; it must hold
+ *            group's best candidates (4x the winners a full group holds on average, at
+ *            least 8 below 4 winners, in token order) and the group's boundary element
+ *            into it, and the workspace's layout record (see dsa_topk_workspace_status);
+ *            rows of at most 32,768 visible tokens send every key instead (the final pass
+ *            then selects from the whole row).  It must hold
  *            dsa_topk_workspace_size(n_q, max_seq_len, cand_k) bytes, 256-byte aligned.
  *            Pass it to dsa_topk with from_candidates = 1.  NULL: scores only.
  */
