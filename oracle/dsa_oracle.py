@@ -20,6 +20,9 @@ Readings of points the pages leave open (each is listed in the design notes):
   * A query row at absolute position pos sees tokens 0..pos inclusive.
   * Top-k ties are broken by the lower token index; -0.0 equals +0.0.
   * The LSE is the natural log-sum-exp of the scaled logits.
+  * MXFP4 index keys follow the OCP microscaling recipe (mxfp4_encode): block scale
+    2^(floor(log2 absmax) - 2), elements rounded to nearest even on the E2M1 grid and
+    saturated at 6.
   * Softmax probabilities are not quantised here: this is the exact softmax.  The
     kernel's two-term FP8 probabilities in the value contraction deviate from it by a
     stated bound per probability, and the attention outputs are compared with this
@@ -113,6 +116,48 @@ def e8m0_value(b) -> np.ndarray:
     b = np.asarray(b, dtype=np.int64)
     with np.errstate(over="ignore"):
         return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def floor_log2(a: float) -> int:
+    """The integer f with 2^f <= a < 2^(f+1), for a finite a > 0 (exact, by comparison)."""
+    f = int(math.floor(math.log2(a)))
+    while 2.0 ** f > a:
+        f -= 1
+    while 2.0 ** (f + 1) <= a:
+        f += 1
+    return f
+
+
+def mxfp4_encode(x) -> Tuple[np.ndarray, np.ndarray]:
+    """OCP MX quantisation of key values [n, 128] (finite) to E2M1 nibbles [n, 128] and
+    E8M0 scale bytes [n, 4]: the 68-byte MXFP4 index key of the "Native MXFP4 indexer"
+    section (ネイティブMXFP4インデクサー), blocks of 32 dimensions sharing one scale.
+
+    Reading (the OCP microscaling recipe; the page names the format, not the rounding):
+    block scale X = 2^(floor(log2 absmax) - 2), 2 being E2M1's largest exponent, kept in
+    E8M0's range (exponent at least -127); an all-zero block takes X = 1.  Each element is
+    the E2M1 value nearest |x| / X, a tie going to the value with an even code (mantissa bit
+    0), capped at 6, the largest E2M1 value: round-to-nearest-even with saturation.  The
+    sign bit is x's own, so a negative value that rounds to zero is -0 (nibble 8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[0]
+    nib = np.zeros((n, IDX_DIM), dtype=np.int64)
+    sbytes = np.zeros((n, IDX_DIM // 32), dtype=np.uint8)
+    for t in range(n):
+        for b in range(IDX_DIM // 32):
+            blk = x[t, 32 * b:32 * b + 32]
+            amax = float(np.max(np.abs(blk)))
+            e = max(floor_log2(amax) - 2, -127) if amax > 0 else 0
+            sbytes[t, b] = e + 127
+            for j, v in enumerate(blk):
+                a = abs(v) / 2.0 ** e
+                dist = np.abs(E2M1_MAG - a)
+                near = np.flatnonzero(dist == dist.min())
+                even = [c for c in near if c % 2 == 0]
+                code = int(even[0] if even else near[0])
+                nib[t, 32 * b + j] = code | (8 if np.signbit(v) else 0)
+    return nib, sbytes
 
 
 def bf16_value(bits: np.ndarray) -> np.ndarray:
@@ -218,7 +263,7 @@ def read_latents(latent_pool: np.ndarray, slots: np.ndarray) -> np.ndarray:
 # Cache append: the new tokens' index keys and latents into the paged caches
 # --------------------------------------------------------------------------------------
 def cache_append(key_pool: np.ndarray, latent_pool: np.ndarray, slots, key_bf16, latent_bf16,
-                 latent_scale: float) -> None:
+                 latent_scale: float, key_format: str = "e4m3") -> None:
     """Quantises and writes tokens into the paged caches by physical slot (in place).
 
     The K3.1 page stores one FP8 index key per token, 132 bytes with its scale ("What
@@ -230,14 +275,23 @@ def cache_append(key_pool: np.ndarray, latent_pool: np.ndarray, slots, key_bf16,
     round-to-nearest-even (saturating) of k / s evaluated in fp32; the latent's codes are
     the E4M3 of x / latent_scale in fp32 with the cache's per-tensor scale.  Slot -1 is
     skipped.  key_bf16 [n, 128] / latent_bf16 [n, 576] are bf16 bit patterns (uint16);
-    either may be None (that cache is left alone).
+    either may be None (that cache is left alone).  key_format "mxfp4": the index-key pool
+    holds the page's opt-in 68-byte MXFP4 keys ("Native MXFP4 indexer"), and the key is
+    mxfp4_encode of its bf16 values, written in the page layout of read_index_keys_mxfp4.
     """
     slots = np.asarray(slots, dtype=np.int64)
     for i, slot in enumerate(slots):
         if slot < 0:
             continue
         page, o = int(slot // PAGE), int(slot % PAGE)
-        if key_bf16 is not None:
+        if key_bf16 is not None and key_format == "mxfp4":
+            nib, sb = mxfp4_encode(bf16_value(np.asarray(key_bf16)[i])[None, :])
+            for d in range(0, IDX_DIM, 2):
+                byte = int(nib[0, d]) | (int(nib[0, d + 1]) << 4)
+                key_pool[page, (d // 32) * 1024 + o * 16 + (d % 32) // 2] = byte
+            key_pool[page, MX_PAGE_KEY_BYTES + 4 * o:MX_PAGE_KEY_BYTES + 4 * o + 4] = sb[0]
+        elif key_bf16 is not None:
+            assert key_format == "e4m3", key_format
             k = bf16_value(np.asarray(key_bf16)[i]).astype(np.float32)
             a = np.float32(np.max(np.abs(k)))
             sc = np.float32(a / np.float32(E4M3_MAX)) if a > 0 else np.float32(1.0)

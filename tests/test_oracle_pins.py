@@ -509,6 +509,91 @@ def test_mxfp4_cache_reader_matches_reference_quantisation():
         assert np.isfinite(got).all()
 
 
+def test_mxfp4_encode_ties_saturation_and_scales():
+    # one block per row of this table: (values, expected magnitudes after decoding)
+    x = np.zeros((1, 128))
+    # block 0: absmax 5 -> floor(log2 5) = 2 -> scale 2^0; the E2M1 grid's tie points go to
+    # the even code: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    x[0, :11] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0, -0.75, -0.1, 0.2]
+    # block 1: absmax 7.5 -> scale 2^0 and saturation at 6; 5.5 is nearest 6
+    x[0, 32:35] = [7.5, -5.5, 0.5]
+    # block 2: absmax 0.3 -> floor(log2 0.3) = -2 -> scale 2^-4 (0.3 / 2^-4 = 4.8 -> 4)
+    x[0, 64:66] = [0.3, -0.03125]
+    # block 3: all zero except a -0.0: scale 2^0, codes 0 and -0
+    x[0, 96] = -0.0
+    nib, sb = O.mxfp4_encode(x)
+    assert sb.tolist() == [[127, 127, 123, 127]]
+    dec = O.e2m1_decode(nib[0]) * O.e8m0_value(np.repeat(sb[0], 32))
+    assert dec[:11].tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 4.0, -1.0, -0.0, 0.0]
+    assert nib[0, 9] == 8 and nib[0, 10] == 0          # -0.1 rounds to -0, 0.2 to +0
+    assert dec[32:35].tolist() == [6.0, -6.0, 0.5]
+    assert dec[64:66].tolist() == [0.25, -0.03125]
+    assert nib[0, 96] == 8 and (nib[0, 97:] == 0).all()
+    # the E8M0 floor: a block of fp32 subnormals keeps the scale 2^-127
+    tiny = np.zeros((1, 128))
+    tiny[0, 0] = 2.0 ** -140
+    nib, sb = O.mxfp4_encode(tiny)
+    assert sb[0, 0] == 0 and nib[0, 0] == 0            # 2^-140 / 2^-127 = 2^-13 -> 0
+
+
+def test_mxfp4_encode_reproduces_grid_values():
+    # values on a block's own E2M1 grid (one element of magnitude 4 or 6 fixing the scale)
+    # come back bit for bit
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 16, size=(20, 128))
+    codes[:, ::32] = rng.choice([6, 7, 14, 15], size=(20, 4))
+    e = rng.integers(-30, 30, size=(20, 4))
+    x = O.e2m1_decode(codes) * np.repeat(2.0 ** e, 32, axis=1)
+    nib, sb = O.mxfp4_encode(x)
+    assert np.array_equal(sb, (e + 127).astype(np.uint8))
+    assert np.array_equal(nib, codes)
+
+
+def test_mxfp4_encode_matches_brute_force_and_the_input_generator():
+    rng = np.random.default_rng(12)
+    raw = (rng.normal(size=(6, 128)) * 2.0 ** rng.integers(-8, 8, size=(6, 1))).astype(np.float32)
+    nib, sb = O.mxfp4_encode(raw)
+    got = O.e2m1_decode(nib) * np.repeat(O.e8m0_value(sb), 32, axis=1)
+    assert np.array_equal(got, _mx_reference(raw))
+    # the synthetic MXFP4 pool is written by an independent quantiser: same bytes
+    wl = synth.custom([100], [1], topk=16, seed=19, key_format="mxfp4")
+    b = synth.make_batch(wl, "cpu", keep_logical=True)
+    pool, bt = b.key_pool.numpy(), b.block_table.numpy()
+    nib, sb = O.mxfp4_encode(b.keys_logical[0].numpy())
+    for t in range(100):
+        page, o = bt[0, t // 64], t % 64
+        for d in range(0, 128, 2):
+            assert pool[page, (d // 32) * 1024 + o * 16 + (d % 32) // 2] == nib[t, d] | (nib[t, d + 1] << 4)
+        assert np.array_equal(pool[page, 4096 + 4 * o:4100 + 4 * o], sb[t])
+
+
+def test_cache_append_mxfp4_keys_and_layout():
+    pages, n = 5, 30
+    key_pool = np.full((pages, O.MX_PAGE_BYTES), 0x77, dtype=np.uint8)
+    key_pool[:, O.MX_PAGE_KEY_BYTES:] = 0xFF
+    rng = np.random.default_rng(13)
+    slots = rng.choice(pages * 64, size=n, replace=False).astype(np.int64)
+    slots[4] = -1                                      # skipped
+    kb, _ = _append_inputs(14, n)
+    kb[6] = 0                                          # all-zero key: scale 2^0, codes 0
+    before = key_pool.copy()
+    O.cache_append(key_pool, None, slots, kb, None, 1.0, key_format="mxfp4")
+    kf = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    touched = np.zeros_like(key_pool, dtype=bool)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        page, o = int(slot // 64), int(slot % 64)
+        vals = O.read_index_keys_mxfp4(key_pool, np.array([page]), 64)[o]
+        assert np.array_equal(vals, _mx_reference(kf[i:i + 1])[0]), i
+        for blk in range(4):
+            touched[page, blk * 1024 + o * 16:blk * 1024 + o * 16 + 16] = True
+        touched[page, 4096 + 4 * o:4100 + 4 * o] = True
+    assert np.array_equal(key_pool[~touched], before[~touched])
+    p6, o6 = int(slots[6] // 64), int(slots[6] % 64)
+    assert (key_pool[p6, 4096 + 4 * o6:4100 + 4 * o6] == 127).all()
+
+
 def test_index_scores_values_brute_force():
     rng = np.random.default_rng(5)
     q = torch.from_numpy(rng.normal(size=(32, 128)).astype(np.float32)).to(torch.bfloat16).double().numpy()
