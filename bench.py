@@ -107,8 +107,9 @@ def _traffic_from_profile():
 
 
 def cache_append_timing(torch, dsa, batch, wl, steps):
-    """dsa_cache_append of one new token per query row (its own position), timed with events
-    over `steps` calls; run after everything else (it rewrites those tokens)."""
+    """dsa_cache_append (dsa_cache_append_mxfp4 for MXFP4 keys) of one new token per query
+    row (its own position), timed with events over `steps` calls; run after everything else
+    (it rewrites those tokens)."""
     import numpy as np
     bt = batch.block_table.cpu().numpy()
     slots = []
@@ -119,22 +120,22 @@ def cache_append_timing(torch, dsa, batch, wl, steps):
     g = torch.Generator(device="cuda").manual_seed(99)
     key = torch.randn((n, 128), generator=g, device="cuda").to(torch.bfloat16)
     lat = torch.randn((n, 576), generator=g, device="cuda").to(torch.bfloat16)
-    mx = wl.key_format == "mxfp4"   # the append writes E4M3 index keys: latents only here
-    kk, kp = (None, None) if mx else (key, batch.key_pool)
+    mx = wl.key_format == "mxfp4"
+    append = dsa.dsa_cache_append_mxfp4 if mx else dsa.dsa_cache_append
     for _ in range(3):
-        dsa.dsa_cache_append(slots_d, kk, lat, batch.latent_scale, kp, batch.latent_pool)
+        append(slots_d, key, lat, batch.latent_scale, batch.key_pool, batch.latent_pool)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        dsa.dsa_cache_append(slots_d, kk, lat, batch.latent_scale, kp, batch.latent_pool)
+        append(slots_d, key, lat, batch.latent_scale, batch.key_pool, batch.latent_pool)
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     return {"tokens": n, "us_per_call": round(us, 2),
             "note": ("one new token per query row: " +
-                     ("its latent (576 B; MXFP4 keys are not appended by this library)" if mx
-                      else "its index key (132 B) and latent (576 B)") +
+                     ("its MXFP4 index key (68 B)" if mx else "its index key (132 B)") +
+                     " and latent (576 B)" +
                      " quantised into the paged caches; calls back to back from Python, caches "
                      "warm")}
 

@@ -20,6 +20,7 @@
  *   dsa_lse_combine       stage 4  LSE merge of splits      ("Decode context parallelism with the
  *                                                             sparse indexer")
  *   dsa_cache_append      quantises the step's new tokens into the two paged caches
+ *   dsa_cache_append_mxfp4  the same for MXFP4 index keys  ("Native MXFP4 indexer")
  *   dsa_quantize_q        the query quantisation the stages 1 and 3 apply internally
  *                         (fused indexer front of "Fused low-latency decode for DSA layers"),
  *                         exposed so callers and tests can see the exact FP8 codes.
@@ -340,6 +341,20 @@ dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key
                             const void* latent_bf16, float latent_scale, void* key_pages,
                             int64_t key_page_stride, void* latent_pages,
                             int64_t latent_page_stride, void* stream);
+
+/*
+ * dsa_cache_append for a cache whose index keys are the page's opt-in 68-byte MXFP4 keys
+ * ("Native MXFP4 indexer"; the page layout of dsa_index_score_mxfp4).  Per block of 32
+ * dims (OCP microscaling): the E8M0 scale 2^e, e = floor(log2 absmax) - 2 (2 = E2M1's
+ * largest exponent), e >= -127, and e = 0 for an all-zero block; each element the E2M1 value
+ * nearest |x| / 2^e, ties to the even code, saturating at 6, with x's sign bit (a negative
+ * value that rounds to zero is -0).  Keys must be finite.  key_page_stride >= 4352; the
+ * latent and every other argument as for dsa_cache_append.
+ */
+dsa_status dsa_cache_append_mxfp4(int32_t n_tok, const int32_t* slots, const void* key_bf16,
+                                  const void* latent_bf16, float latent_scale, void* key_pages,
+                                  int64_t key_page_stride, void* latent_pages,
+                                  int64_t latent_page_stride, void* stream);
 
 /*
  * Per-(row, head) E4M3 query quantisation used inside stages 1 and 3.

@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
                                           _F32, _F32, _I32, _P, _P, _P, _SZ, _P]
         L.dsa_lse_combine.argtypes = [_I32, _I32, _P, _P, _P, _P, _P]
         L.dsa_cache_append.argtypes = [_I32, _P, _P, _P, _F32, _P, _I64, _P, _I64, _P]
+        L.dsa_cache_append_mxfp4.argtypes = [_I32, _P, _P, _P, _F32, _P, _I64, _P, _I64, _P]
         L.dsa_quantize_q.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         L.dsa_sparse_mla_decode_noalloc.argtypes = [_I32, _P, _P, _P, _P, _I64, _F32, _P, _I32,
                                                     _F32, _I32, _P, _P, _P, _P, _P]
@@ -74,7 +75,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.restype = ctypes.c_char_p
         for f in ("dsa_index_score", "dsa_index_score_mxfp4", "dsa_index_score_quantize_q", "dsa_topk", "dsa_sparse_mla_decode", "dsa_topk_sparse_mla",
-                  "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append", "dsa_validate_batch",
+                  "dsa_lse_combine", "dsa_quantize_q", "dsa_cache_append", "dsa_cache_append_mxfp4",
+                  "dsa_validate_batch",
                   "dsa_validate_slots", "dsa_sparse_mla_decode_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -409,13 +411,8 @@ def dsa_lse_combine(o_part: torch.Tensor, lse_part: torch.Tensor, out: torch.Ten
                                  _stream(stream)))
 
 
-def dsa_cache_append(slots: torch.Tensor, key: Optional[torch.Tensor],
-                     latent: Optional[torch.Tensor], latent_scale: float,
-                     key_pages: Optional[torch.Tensor], latent_pages: Optional[torch.Tensor], *,
-                     key_page_stride: Optional[int] = None,
-                     latent_page_stride: Optional[int] = None, stream=None) -> None:
-    """Quantises new tokens (index keys bf16 [n, 128], latents bf16 [n, 576]) into the paged
-    caches at their physical slots (int32 [n], -1 = skip)."""
+def _cache_append(fn, slots, key, latent, latent_scale, key_pages, latent_pages,
+                  key_page_stride, latent_page_stride, stream):
     n = slots.shape[0]
     _expect(slots, "slots", torch.int32, (n,))
     if key is not None:
@@ -426,9 +423,30 @@ def dsa_cache_append(slots: torch.Tensor, key: Optional[torch.Tensor],
           else (key_pages.stride(0) * key_pages.element_size() if key_pages is not None else 0))
     ls = (latent_page_stride if latent_page_stride is not None
           else (latent_pages.stride(0) * latent_pages.element_size() if latent_pages is not None else 0))
-    _check(lib().dsa_cache_append(int(n), _ptr(slots), _ptr(key), _ptr(latent),
-                                  float(latent_scale), _ptr(key_pages), int(ks),
-                                  _ptr(latent_pages), int(ls), _stream(stream)))
+    _check(fn(int(n), _ptr(slots), _ptr(key), _ptr(latent), float(latent_scale),
+              _ptr(key_pages), int(ks), _ptr(latent_pages), int(ls), _stream(stream)))
+
+
+def dsa_cache_append(slots: torch.Tensor, key: Optional[torch.Tensor],
+                     latent: Optional[torch.Tensor], latent_scale: float,
+                     key_pages: Optional[torch.Tensor], latent_pages: Optional[torch.Tensor], *,
+                     key_page_stride: Optional[int] = None,
+                     latent_page_stride: Optional[int] = None, stream=None) -> None:
+    """Quantises new tokens (index keys bf16 [n, 128], latents bf16 [n, 576]) into the paged
+    caches at their physical slots (int32 [n], -1 = skip); E4M3 index-key pages."""
+    _cache_append(lib().dsa_cache_append, slots, key, latent, latent_scale, key_pages,
+                  latent_pages, key_page_stride, latent_page_stride, stream)
+
+
+def dsa_cache_append_mxfp4(slots: torch.Tensor, key: Optional[torch.Tensor],
+                           latent: Optional[torch.Tensor], latent_scale: float,
+                           key_pages: Optional[torch.Tensor],
+                           latent_pages: Optional[torch.Tensor], *,
+                           key_page_stride: Optional[int] = None,
+                           latent_page_stride: Optional[int] = None, stream=None) -> None:
+    """dsa_cache_append for MXFP4 index-key pages (68 bytes per token)."""
+    _cache_append(lib().dsa_cache_append_mxfp4, slots, key, latent, latent_scale, key_pages,
+                  latent_pages, key_page_stride, latent_page_stride, stream)
 
 
 class DecodeStep:

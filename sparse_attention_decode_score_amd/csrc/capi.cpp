@@ -424,20 +424,22 @@ dsa_status dsa_topk_sparse_mla(int32_t num_seqs, int32_t n_q, int32_t max_seq_le
                   "dsa_topk_sparse_mla");
 }
 
-dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key_bf16,
-                            const void* latent_bf16, float latent_scale, void* key_pages,
-                            int64_t key_page_stride, void* latent_pages,
-                            int64_t latent_page_stride, void* stream) {
+namespace {
+dsa_status cache_append(int32_t n_tok, const int32_t* slots, const void* key_bf16,
+                        const void* latent_bf16, float latent_scale, void* key_pages,
+                        int64_t key_page_stride, void* latent_pages, int64_t latent_page_stride,
+                        void* stream, bool mx_keys, const char* name) {
   DSA_REQUIRE(n_tok >= 0, "n_tok must be >= 0 (got %d)", n_tok);
   DSA_REQUIRE(slots, "slots must be non-null");
   DSA_REQUIRE(key_bf16 || latent_bf16, "give key_bf16, latent_bf16 or both");
   if (key_bf16) {
+    const int64_t min_stride = mx_keys ? DSA_IDX_MXFP4_PAGE_BYTES : DSA_IDX_PAGE_BYTES;
     DSA_REQUIRE(key_pages, "key_pages must be non-null when key_bf16 is given");
     DSA_REQUIRE(aligned(key_bf16, 16) && aligned(key_pages, 16),
                 "key_bf16 and key_pages must be 16-byte aligned");
-    DSA_REQUIRE(key_page_stride >= DSA_IDX_PAGE_BYTES && key_page_stride % 16 == 0,
-                "key_page_stride must be >= 8448 and a multiple of 16 (got %lld)",
-                (long long)key_page_stride);
+    DSA_REQUIRE(key_page_stride >= min_stride && key_page_stride % 16 == 0,
+                "key_page_stride must be >= %lld and a multiple of 16 (got %lld)",
+                (long long)min_stride, (long long)key_page_stride);
   }
   if (latent_bf16) {
     DSA_REQUIRE(latent_pages, "latent_pages must be non-null when latent_bf16 is given");
@@ -452,8 +454,28 @@ dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key
                                            static_cast<const uint16_t*>(latent_bf16),
                                            latent_scale, static_cast<uint8_t*>(key_pages),
                                            key_page_stride, static_cast<uint8_t*>(latent_pages),
-                                           latent_page_stride, static_cast<hipStream_t>(stream)),
-                  "dsa_cache_append");
+                                           latent_page_stride, mx_keys,
+                                           static_cast<hipStream_t>(stream)),
+                  name);
+}
+}  // namespace
+
+dsa_status dsa_cache_append(int32_t n_tok, const int32_t* slots, const void* key_bf16,
+                            const void* latent_bf16, float latent_scale, void* key_pages,
+                            int64_t key_page_stride, void* latent_pages,
+                            int64_t latent_page_stride, void* stream) {
+  return cache_append(n_tok, slots, key_bf16, latent_bf16, latent_scale, key_pages,
+                      key_page_stride, latent_pages, latent_page_stride, stream, false,
+                      "dsa_cache_append");
+}
+
+dsa_status dsa_cache_append_mxfp4(int32_t n_tok, const int32_t* slots, const void* key_bf16,
+                                  const void* latent_bf16, float latent_scale, void* key_pages,
+                                  int64_t key_page_stride, void* latent_pages,
+                                  int64_t latent_page_stride, void* stream) {
+  return cache_append(n_tok, slots, key_bf16, latent_bf16, latent_scale, key_pages,
+                      key_page_stride, latent_pages, latent_page_stride, stream, true,
+                      "dsa_cache_append_mxfp4");
 }
 
 dsa_status dsa_validate_batch(int32_t num_seqs, int32_t n_q, int32_t max_seq_len,

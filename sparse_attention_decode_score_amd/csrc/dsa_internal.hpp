@@ -116,11 +116,12 @@ hipError_t launch_topk_sparse_mla(int num_seqs, int n_q, const int32_t* cu_q,
                                   float* lse, void* workspace, hipStream_t st);
 
 // New tokens' index keys (bf16 [n][128]) and latents (bf16 [n][576]) quantised into the
-// paged caches at their physical slots (-1: skipped); key or lat may be null.
+// paged caches at their physical slots (-1: skipped); key or lat may be null.  mx_keys: the
+// index-key cache holds MXFP4 pages (else E4M3 pages).
 hipError_t launch_cache_append(int n_tok, const int32_t* slots, const uint16_t* key,
                                const uint16_t* lat, float lat_scale, uint8_t* key_pages,
                                int64_t key_page_stride, uint8_t* lat_pages,
-                               int64_t lat_page_stride, hipStream_t st);
+                               int64_t lat_page_stride, bool mx_keys, hipStream_t st);
 
 hipError_t launch_lse_combine(int num_splits, int n_q, const float* o_part, const float* lse_part,
                               uint16_t* out_bf16, float* lse, hipStream_t st);

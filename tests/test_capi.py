@@ -29,7 +29,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"dsa_index_score", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla_decode",
-            "dsa_sparse_mla_workspace_size", "dsa_topk_sparse_mla", "dsa_lse_combine", "dsa_cache_append", "dsa_quantize_q", "dsa_last_error",
+            "dsa_sparse_mla_workspace_size", "dsa_topk_sparse_mla", "dsa_lse_combine", "dsa_cache_append", "dsa_cache_append_mxfp4", "dsa_quantize_q", "dsa_last_error",
             "dsa_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -203,6 +203,24 @@ def test_cache_append_rejects_bad_host_args(L):
     args[3], args[7], args[8] = None, None, 0
     args[0] = -1
     assert f(*args) == 1 and "n_tok" in _err()
+
+
+def test_cache_append_mxfp4_rejects_bad_host_args(L):
+    f = L.dsa_cache_append_mxfp4
+    base = [4, FAKE, FAKE, FAKE, ctypes.c_float(0.01), FAKE, 4352, FAKE, 36864, None]
+    for patch, word in [({0: -1}, "n_tok"), ({1: None}, "slots"), ({2: None, 3: None}, "give"),
+                        ({5: None}, "key_pages"), ({6: 4351}, "key_page_stride"),
+                        ({6: 4360}, "key_page_stride"), ({2: FAKE_ODD}, "aligned"),
+                        ({4: ctypes.c_float(0.0)}, "latent_scale")]:
+        args = list(base)
+        for i, v in patch.items():
+            args[i] = v
+        assert f(*args) == 1, (patch, _err())
+        assert word in _err(), (patch, _err())
+    # any stride of at least 4352 (a multiple of 16) is accepted; no tokens launch nothing
+    args = list(base)
+    args[0], args[6] = 0, 8448
+    assert f(*args) == 0, _err()
 
 
 def test_index_score_mxfp4_rejects_bad_host_args(L):

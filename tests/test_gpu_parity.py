@@ -1034,6 +1034,72 @@ def test_cache_append_keys_only_leaves_latents_and_feeds_the_indexer():
         check_scores(scores[row, : pos + 1].cpu().numpy(), ref, mag, f"append row {row}")
 
 
+def _mx_edge_keys(n, g):
+    """bf16 keys [n, 128] with the MXFP4 append's edge cases: E2M1 tie points and saturation
+    on a block's own grid, all-zero and -0 blocks, fp32-subnormal (bf16) blocks that reach the
+    E8M0 floor, huge magnitudes, and negative values that round to -0."""
+    k = torch.randn((n, 128), generator=g) * torch.logspace(-4, 4, n).view(n, 1)
+    ties = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.5, 5.5, -0.75, -0.1, 4.0])
+    for i in range(0, n, 7):
+        blk = i % 4
+        e = float(2.0 ** ((i % 21) - 10))
+        k[i, 32 * blk:32 * blk + 32] = 0.0
+        k[i, 32 * blk:32 * blk + len(ties)] = ties * e
+    if n > 3:
+        k[1] = 0.0
+        k[2, :32] = -0.0
+        k[3, 32:64] = torch.linspace(-1, 1, 32) * 1e-39   # bf16 subnormals
+        k[3, 64:96] = torch.linspace(-1, 1, 32) * 3e38
+    return k.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n,pad", [(1, 0), (40, 0), (300, 48)])
+def test_cache_append_mxfp4_bit_exact(n, pad):
+    say("append mxfp4", n, pad)
+    pages = 20
+    g = torch.Generator().manual_seed(100 + n)
+    key_pool = torch.full((pages, 4352 + pad), 0x77, dtype=torch.uint8)
+    key_pool[:, 4096:4352] = 0xFF
+    lat_pool = torch.full((pages, 64 * 576), 0x7F, dtype=torch.uint8)
+    slots = torch.randperm(pages * 64, generator=g)[:n].to(torch.int32)
+    if n > 4:
+        slots[4] = -1
+    key = _mx_edge_keys(n, g)
+    lat = torch.randn((n, 576), generator=g).to(torch.bfloat16)
+    lat_scale = float(np.float32(lat.float().abs().max() / 448.0))
+    kp_ref, lp_ref = key_pool.numpy().copy(), lat_pool.numpy().copy()
+    O.cache_append(kp_ref, lp_ref, slots.numpy(), _bf16_bits(key), _bf16_bits(lat), lat_scale,
+                   key_format="mxfp4")
+    kp, lp = key_pool.to(DEV), lat_pool.to(DEV)
+    dsa.dsa_cache_append_mxfp4(slots.to(DEV), key.to(DEV), lat.to(DEV), lat_scale, kp, lp)
+    torch.cuda.synchronize()
+    got = kp.cpu().numpy()
+    bad = np.argwhere(got != kp_ref)
+    assert bad.size == 0, (bad[:5].tolist(), got[tuple(bad[0])], kp_ref[tuple(bad[0])])
+    assert np.array_equal(lp.cpu().numpy(), lp_ref)
+
+
+def test_cache_append_mxfp4_keys_feed_the_mxfp4_indexer():
+    wl = synth.custom([1000, 70], [1, 1], topk=64, seed=72, key_format="mxfp4")
+    batch = synth.make_batch(wl, DEV)
+    bt = batch.block_table.cpu().numpy()
+    g = torch.Generator().manual_seed(72)
+    key = torch.randn((2, 128), generator=g).to(torch.bfloat16)
+    slots = torch.tensor([O.physical_slot(bt[b], np.array([L - 1]))[0]
+                          for b, L in enumerate(wl.seq_lens)], dtype=torch.int32)
+    lat_before = batch.latent_pool.clone()
+    kp_ref = batch.key_pool.cpu().numpy().copy()
+    O.cache_append(kp_ref, None, slots.numpy(), _bf16_bits(key), None, 1.0, key_format="mxfp4")
+    dsa.dsa_cache_append_mxfp4(slots.to(DEV), key.to(DEV), None, 1.0, batch.key_pool, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(batch.key_pool.cpu().numpy(), kp_ref)
+    assert torch.equal(batch.latent_pool, lat_before)
+    scores = run_scores(batch)
+    for row, (b, pos) in enumerate(wl.row_positions()):
+        ref, mag = oracle_scores(batch, row, keys=request_keys(batch, b, kp_ref, bt))
+        check_scores(scores[row, : pos + 1].cpu().numpy(), ref, mag, f"mx append row {row}")
+
+
 # ------------------------------------------------------------------------ MXFP4 index keys
 MX_SMALL = [
     synth.custom([300, 64, 129, 1000], [1, 2, 3, 8], topk=128, seed=81, name="mx-ragged",
