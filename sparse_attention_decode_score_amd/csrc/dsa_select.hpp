@@ -78,7 +78,7 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // selection that would keep a large share of each group anyway (m >= 64 below 32,768 tokens).
 constexpr int kFullRowMax = DSA_FULL_ROW_MAX;
 static_assert(kFullRowMax <= kFinalThreads * kFinalRegPerThread, "full rows fit the registers");
-__host__ __device__ __forceinline__ int group_cand_count(int n_vis, int k) {
+__host__ __device__ __forceinline__ constexpr int group_cand_count(int n_vis, int k) {
   if (n_vis <= kFullRowMax) return kGroupTok;
   const int64_t num = 4 * (int64_t)k * kGroupTok;  // 4 lambda n_vis
   int64_t m = (num + n_vis - 1) / n_vis;           // ceil(4 lambda)
@@ -90,6 +90,12 @@ __host__ __device__ __forceinline__ int group_cand_count(int n_vis, int k) {
   if (m > kGroupTok) m = kGroupTok;
   return (int)m;
 }
+
+constexpr int kMaxTopk = 4096;  // the largest k the library accepts
+// The most candidates a group of a row that is not full keeps (k = 4096 just past 32,768
+// tokens): what a buffer of candidate token indices must hold per group.
+constexpr int kMaxPartialCand = group_cand_count(kFullRowMax + 1, kMaxTopk);
+static_assert(kMaxPartialCand == 128, "partial-row candidate bound");
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -12,7 +12,6 @@
 
 namespace dsa {
 
-constexpr int kMaxTopk = 4096;
 
 // Request and absolute position of query row `row`: one wave-wide ballot over cu_q per 64
 // requests (rows are grouped by request and are its last tokens).

@@ -47,6 +47,7 @@ struct IdxCfg {
   static constexpr int kMaxGroups = (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1);
   static constexpr int kSegTok = kWaves * kGroupTok * kMaxGroups;  // tokens per workgroup
   static constexpr int kCandSlots = kWaves * kMaxGroups * kGroupTok;  // worst case (m = 256)
+  static constexpr int kIdxSlots = kWaves * kMaxGroups * kMaxPartialCand;  // rows not full
 };
 
 // Candidate output of the fused first top-k pass.
@@ -127,9 +128,12 @@ __device__ __forceinline__ void quantize_mla_rows(const MlaQueryPrep& pp, int r0
 // Eight-row groups are held to three workgroups per CU (168 VGPRs, three waves per SIMD: the
 // LDS of three fits): their rows' products and selections are latency-bound, and the third
 // wave hides more of it than the registers it costs (a few spills; speculative decode
-// indexer 44 -> 35 us).
+// indexer 44 -> 35 us).  So are one-row groups on MXFP4 keys (half-size pages, the same
+// arithmetic per page): three waves at 168 VGPRs without spills, 50 KB of LDS each (MXFP4
+// indexer at 128K x 32: 58.1 -> 55.3 us).  One-row groups on E4M3 keys need 228 VGPRs and
+// keep two.
 template <int R, bool CAND, bool MX>
-__global__ __launch_bounds__(256, (R == 8 ? 3 : 1)) void index_score_kernel(
+__global__ __launch_bounds__(256, (R == 8 || (R == 1 && MX) ? 3 : 1)) void index_score_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ head_w,
     const uint8_t* __restrict__ key_pages, int64_t page_stride,
@@ -143,7 +147,8 @@ __global__ __launch_bounds__(256, (R == 8 ? 3 : 1)) void index_score_kernel(
   __shared__ __attribute__((aligned(16))) float wps[R][kIdxHeads];
   __shared__ __attribute__((aligned(16))) float sbuf[STAGE ? R : 1][STAGE ? Cfg::kSegTok : 1];
   __shared__ __attribute__((aligned(16))) uint32_t cbuf_key[CSTAGE ? R : 1][CSTAGE ? Cfg::kCandSlots : 1];
-  __shared__ __attribute__((aligned(16))) int32_t cbuf_idx[CSTAGE ? R : 1][CSTAGE ? Cfg::kCandSlots : 1];
+  // token indices only for rows that are not full (at most kMaxPartialCand per group)
+  __shared__ __attribute__((aligned(16))) int32_t cbuf_idx[CSTAGE ? R : 1][CSTAGE ? Cfg::kIdxSlots : 1];
   __shared__ __attribute__((aligned(16))) ChunkInfo cbuf_info[CSTAGE ? R : 1][CSTAGE ? kWaves * Cfg::kMaxGroups : 1];
   __shared__ __attribute__((aligned(16))) uint32_t ghist[CAND ? kWaves : 1][256];  // per wave
 
@@ -250,7 +255,8 @@ __global__ __launch_bounds__(256, (R == 8 ? 3 : 1)) void index_score_kernel(
           const int gl = kWaves * gi + wave;  // group index in the workgroup
           if constexpr (CSTAGE) {
             group_select(keys[r], min(kGroupTok, n_vis - t0), m, t0, &cbuf_key[r][gl * m],
-                         &cbuf_idx[r][gl * m], &cbuf_info[r][gl], &ghist[wave][0]);
+                         &cbuf_idx[r][m == kGroupTok ? 0 : gl * m],  // (full: unused)
+                         &cbuf_info[r][gl], &ghist[wave][0]);
           } else {
             const int64_t base = (int64_t)row * cand.row_cap + (int64_t)grp * m;
             group_select(keys[r], min(kGroupTok, n_vis - t0), m, t0, cand.key + base,
