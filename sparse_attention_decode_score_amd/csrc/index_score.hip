@@ -35,14 +35,17 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kGroupPages = kGroupTok / kPage;  // 4
 
-// Pages each wave keeps in flight: four for one or two rows, two for larger row groups
-// (register budget).  Groups per wave at most: the staged scores of a workgroup are
+// Pages each wave keeps in flight: four for two rows, two for larger row groups (register
+// budget); one row runs three waves per SIMD (see the kernel) with two E4M3 pages or four
+// (half-size) MXFP4 pages in flight per wave.  A group's four pages cycle through the ring
+// in order, so the ring size divides four.  Groups per wave at most: the staged scores of a workgroup are
 // 16 KB of LDS for up to four rows; eight rows store directly and take up to four groups,
 // which the grid rule below gives them only when there are many row groups (a prefill),
 // where long segments amortise the eight rows' query set-up.
 template <int R>
 struct IdxCfg {
-  static constexpr int kInFlight = R <= 2 ? 4 : 2;
+  template <bool MX>
+  static constexpr int kInFlight = R == 1 ? (MX ? 4 : 2) : R == 2 ? 4 : 2;
   static constexpr bool kStage = R <= 4;
   static constexpr int kMaxGroups = (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1);
   static constexpr int kSegTok = kWaves * kGroupTok * kMaxGroups;  // tokens per workgroup
@@ -128,19 +131,19 @@ __device__ __forceinline__ void quantize_mla_rows(const MlaQueryPrep& pp, int r0
 // Eight-row groups are held to three workgroups per CU (168 VGPRs, three waves per SIMD: the
 // LDS of three fits): their rows' products and selections are latency-bound, and the third
 // wave hides more of it than the registers it costs (a few spills; speculative decode
-// indexer 44 -> 35 us).  So are one-row groups on MXFP4 keys (half-size pages, the same
-// arithmetic per page): three waves at 168 VGPRs without spills, 50 KB of LDS each (MXFP4
-// indexer at 128K x 32: 58.1 -> 55.3 us).  One-row groups on E4M3 keys need 228 VGPRs and
-// keep two.
+// indexer 44 -> 35 us).  So are one-row groups: three waves at <= 168 VGPRs without spills
+// (two E4M3 pages in flight per wave instead of four; MXFP4 pages are half the size) and
+// 50 KB of LDS each (at 128K x 32: E4M3 indexer ~94 -> ~92 us, MXFP4 58.1 -> 55.3 us).
 template <int R, bool CAND, bool MX>
-__global__ __launch_bounds__(256, (R == 8 || (R == 1 && MX) ? 3 : 1)) void index_score_kernel(
+__global__ __launch_bounds__(256, (R == 8 || R == 1 ? 3 : 1)) void index_score_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ q, const float* __restrict__ head_w,
     const uint8_t* __restrict__ key_pages, int64_t page_stride,
     const int32_t* __restrict__ block_table, int bt_stride, float* __restrict__ scores,
     int64_t score_stride, int groups_per_wave, CandOut cand, MlaQueryPrep prep) {
   using Cfg = IdxCfg<R>;
-  constexpr int NF = Cfg::kInFlight;
+  constexpr int NF = Cfg::template kInFlight<MX>;
+  static_assert(kGroupPages % NF == 0, "ring slot of page s is s % NF = jj % NF");
   constexpr bool STAGE = Cfg::kStage;
   constexpr bool CSTAGE = CAND && STAGE;
   __shared__ __attribute__((aligned(16))) uint8_t q8s[R][kIdxHeads][kQRowStride];
