@@ -36,7 +36,11 @@ __global__ __launch_bounds__(128) void lse_combine_kernel(Part o_part, const flo
                                                           int num_splits, int64_t rows_heads,
                                                           float scale, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse_out) {
-  const int64_t rh = blockIdx.x;  // row * 96 + head
+  // (row, head) = row * 96 + head.  Workgroups are dealt to the 8 XCDs round-robin by
+  // linear id; when the grid divides evenly, XCD x takes the contiguous eighth x of the rows,
+  // as the attention kernel's split partials of those rows were written from that XCD.
+  int64_t rh = blockIdx.x;
+  if ((gridDim.x & 7) == 0) rh = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int t = threadIdx.x;
   float m = -INFINITY;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
