@@ -382,8 +382,10 @@ hipError_t launch_index_score(int num_seqs, int n_q, int max_seq_len, int max_q_
 #endif
   const unsigned gz = (unsigned)((max_q_per_seq + R - 1) / R);
   // groups per wave: the longest segments (up to the staging limit of R) that still give
-  // >= 1,024 workgroups (4 per CU)
-  int G = (R == 1 || R == 8) ? 4 : (R == 2 ? 2 : 1);
+  // >= 1,024 workgroups (4 per CU); one-row MXFP4 groups at most two (measured: at 128K x 32
+  // the MXFP4 indexer takes 54.1 us with two groups per wave, 55.8 us with four; E4M3 keys
+  // are indifferent)
+  int G = (R == 1 || R == 8) ? (R == 1 && mxfp4 ? 2 : 4) : (R == 2 ? 2 : 1);
   while (G > 1 && (int64_t)num_seqs * gz *
                           ((max_pages + kWaves * kGroupPages * G - 1) / (kWaves * kGroupPages * G)) <
                       1024)
