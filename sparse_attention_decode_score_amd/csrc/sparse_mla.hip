@@ -76,7 +76,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // The memory clobber keeps every LDS access on its side.
 template <int pending>
 __device__ __forceinline__ void ring_barrier() {
-  static_assert(pending >= 0 && pending < 16, "vmcnt field");
+  static_assert(pending >= 0 && pending < 64, "vmcnt field");
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(pending) : "memory");
 }
 
@@ -312,7 +312,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 
   // ---- gathers: wave w moves columns w, w+8, .. (< 36) of every row of a tile; lane l
   // moves token l.  Tiles past the split gather zero rows into a buffer nobody reads, so
-  // every wave issues the same number of loads per tile and its wait counts are fixed.
+  // every wave issues a fixed number of loads per tile (tiles 0 and 1: the value waves
+  // only, see issue_value_half) and its wait counts are fixed.
   // Steps jj0 .. jj1-1 (of 5) of tile t's gathers; a wave may issue them in pieces.
   auto issue = [&](int t, int jj0, int jj1) {
     const int j = t * kTile + lane;
@@ -327,6 +328,21 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       if (jj >= jj0 && jj < jj1 && (jj < 4 || c < kCols))  // wave-uniform
         __builtin_amdgcn_global_load_lds(src + 16 * c, dst + 1024 * c, 16, 0, 0);
     }
+  };
+  // All of tile t's gathers from the two value waves: wave 6 the even columns, wave 7 the
+  // odd ones (18 each).  Tiles 0 and 1 go out this way, so that the duty waves prepare the
+  // query meanwhile instead of queueing behind 80 gathers.
+  auto issue_value_half = [&](int t) {
+    const int j = t * kTile + lane;
+    const int slot = j < n_tok ? slot_l[j] : -1;
+    const uint8_t* src = slot >= 0 ? lat_pages + (int64_t)(slot >> 6) * page_stride +
+                                         (int64_t)(slot & (kPage - 1)) * kLatDim
+                                   : g_zero_row;
+    DSA_LDS uint8_t* dst = (DSA_LDS uint8_t*)(&sm.lat[t % kRing][0]);
+    const int c0 = wave - kDutyWaves;  // 0 or 1
+#pragma unroll
+    for (int i = 0; i < kCols / 2; ++i)
+      __builtin_amdgcn_global_load_lds(src + 16 * (c0 + 2 * i), dst + 1024 * (c0 + 2 * i), 16, 0, 0);
   };
 
   // Two roles, so that no wave needs more than 256 registers and every SIMD (waves w and
@@ -373,8 +389,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       }
     }
     lds_barrier();
-    issue(0, 0, 5);
-    issue(1, 0, 5);
+    if constexpr (!DUTY) {
+      issue_value_half(0);
+      issue_value_half(1);
+    }
     if (q8_in && qthread) {
       uint8_t* dst = qstage + qh * kQStride + qpart * 144;
 #pragma unroll
@@ -498,7 +516,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       // tile t is in LDS once every wave's own gathers of it are done (tile t+1 may still
       // be in flight); the barrier also publishes tile t-1's probabilities and frees the
       // buffer tile t-1 used
-      if (wave < kCols - 4 * kWaves) ring_barrier<5>();
+      // (tiles 0 and 1: 18 gathers each from every value wave and none from the duty waves)
+      if (!DUTY && t == 0) ring_barrier<kCols / 2>();
+      else if (wave < kCols - 4 * kWaves) ring_barrier<5>();
       else ring_barrier<4>();
       // the lane index as an opaque value of this step: the LDS addresses derived from it are
       // recomputed here (a few ALU ops) instead of being hoisted out of the loop and spilled
