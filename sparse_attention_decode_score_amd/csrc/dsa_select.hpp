@@ -332,9 +332,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* red, int&
 }
 
 // Exact top-k (1 <= k <= number of real keys) of up to kFinalThreads * E keys held in
-// registers: thread t holds elements t*E .. t*E+E-1 (keys kv, values vv; elements past the
-// end hold the sentinel key).  Writes the values of the chosen elements, in element order,
-// to out[0..k) (LDS) and returns the k-th element's key and value.
+// registers: thread t holds elements t*E .. t*E+E-1 (keys kv; elements past the end hold the
+// sentinel key).  Writes the values of the chosen elements, in element order, to out[0..k)
+// (LDS) and returns the k-th element's key and value.  elem(j) names this thread's element j:
+// its value itself when elem_is_value (a value held in registers, no further reads), else
+// its element index, which val() turns into the value after the selection.
 //
 // K, the k-th largest key, is found digit by digit (a radix select).  All real keys share
 // the bits of their maximum and minimum above the highest bit where those differ; below it,
@@ -354,9 +356,9 @@ struct KthKey {
   int idx;
 };
 
-template <int E, class Val>
-__device__ KthKey block_topk_regs(const uint32_t (&kv)[E], Val val, int k, int* out, int* red,
-                                  int* note, uint32_t* hist) {
+template <int E, class Val, class Elem>
+__device__ KthKey block_topk_regs(const uint32_t (&kv)[E], Val val, Elem elem, bool elem_is_value,
+                                  int k, int* out, int* red, int* note, uint32_t* hist) {
   const int tid = threadIdx.x, lane = tid & 63;
   int parity = 0;
   for (int i = tid; i < 2 * kHistSet; i += kFinalThreads) hist[i] = 0u;
@@ -443,19 +445,20 @@ __device__ KthKey block_topk_regs(const uint32_t (&kv)[E], Val val, int k, int* 
   const int eq_before = before >> 16;
   int pos = (before & 0xFFFF) + min(eq_before, r);
   int e_rank = eq_before;
-  // element indices first (no loads in this loop), then every thread turns k / 512 of them
-  // into values with independent loads
+  // values, or element indices (no loads in this loop) that every thread then turns, k / 512
+  // of them, into values with independent loads
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     bool take = kv[j] > K;
     if (kv[j] == K) {
       take = e_rank < r;
-      if (e_rank == r - 1) *note = tid * E + j;
+      if (e_rank == r - 1) *note = elem(j);
       ++e_rank;
     }
-    if (take) out[pos++] = tid * E + j;
+    if (take) out[pos++] = elem(j);
   }
   __syncthreads();
+  if (elem_is_value) return KthKey{K, *note};
   const int I = val(*note);
 #pragma unroll 4
   for (int i = tid; i < k; i += kFinalThreads) out[i] = val(out[i]);
@@ -481,7 +484,8 @@ __device__ KthKey block_topk_e(Get get, Val val, int n, int k, int* out, int* re
     const int e = tid * E + j;
     kv[j] = e < n ? get(e) : kSentinel;
   }
-  return block_topk_regs<E>(kv, val, k, out, red, note, hist);
+  return block_topk_regs<E>(kv, val, [tid](int j) { return tid * E + j; }, false, k, out, red,
+                            note, hist);
 }
 
 // (get / val are taken by value: they hold a pointer or two, and the slow path is a call.)

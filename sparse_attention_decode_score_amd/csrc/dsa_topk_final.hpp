@@ -448,13 +448,24 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
       auto run = [&](auto e_tag) {
         constexpr int E = decltype(e_tag)::value;
         uint32_t kv[E];
-        // the keys only: a chosen element's token index is read when it is written out
-        // (a quad past the end reads element 0 and is masked below)
-        v4i a[E / 4];
+        // the keys, then (up to 32 per thread) the token indices: the search waits for the
+        // keys only, and the chosen elements' tokens are in registers when they are written
+        // out.  A full row's token is its position.  With 64 per thread the index of a chosen
+        // element is read when it is written out.  (A quad past the end reads element 0 and
+        // is masked below.)
+        constexpr bool kIdxRegs = E <= 32;
+        v4i a[E / 4], c[kIdxRegs ? E / 4 : 1];
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
           const int e = tid * E + 4 * q;
           a[q] = *reinterpret_cast<const v4i*>(ck + (e < n_cand ? e : 0));
+        }
+        if constexpr (kIdxRegs) {
+#pragma unroll
+          for (int q = 0; q < E / 4; ++q) {
+            const int e = tid * E + 4 * q;
+            c[q] = full ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(ci + (e < n_cand ? e : 0));
+          }
         }
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
@@ -462,8 +473,15 @@ __device__ inline int final_select_row(int row, int n_vis, float* scores, int64_
 #pragma unroll
           for (int j = 0; j < 4; ++j) kv[4 * q + j] = in ? (uint32_t)a[q][j] : kSentinel;
         }
-        kth = block_topk_regs<E>(kv, [ci, full](int e) { return full ? e : ci[e]; }, k, out,
-                                 red, note_p, hist);
+        const auto val = [ci, full](int e) { return full ? e : ci[e]; };
+        if constexpr (kIdxRegs) {
+          kth = block_topk_regs<E>(
+              kv, val, [&](int j) { return full ? tid * E + j : (int)c[j / 4][j % 4]; }, true, k,
+              out, red, note_p, hist);
+        } else {
+          kth = block_topk_regs<E>(kv, val, [tid](int j) { return tid * E + j; }, full, k, out,
+                                   red, note_p, hist);
+        }
       };
       switch (final_per_thread(n_cand)) {
         case 8: run(std::integral_constant<int, 8>()); break;
