@@ -94,8 +94,8 @@ __host__ __device__ __forceinline__ constexpr int group_cand_count(int n_vis, in
 constexpr int kMaxTopk = 4096;  // the largest k the library accepts
 // The most candidates a group of a row that is not full keeps (k = 4096 just past 32,768
 // tokens): what a buffer of candidate token indices must hold per group.
-constexpr int kMaxPartialCand = group_cand_count(kFullRowMax + 1, kMaxTopk);
-static_assert(kMaxPartialCand == 128, "partial-row candidate bound");
+constexpr int kMaxPartialCand = group_cand_count(kFullRowMax + 1, kMaxTopk);  // 128
+static_assert(kMaxPartialCand % 4 == 0 && kMaxPartialCand <= kGroupTok, "partial-row bound");
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
