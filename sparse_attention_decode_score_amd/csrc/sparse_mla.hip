@@ -10,8 +10,9 @@
 //
 // Workgroup = 8 waves, one per CU (two per SIMD).  The split's slots sit in LDS; 64-token
 // latent tiles are gathered straight into a 3-tile LDS ring with 16-byte global-to-LDS loads
-// (every wave moves 4 or 5 of a tile's 36 16-byte columns; lane l moves token l), so tile
-// t+2 is in flight while tile t is used and no register holds gathered bytes.  A tile is
+// (every wave moves 4 or 5 of a tile's 36 16-byte columns; lane l moves token l; the first
+// two tiles come from the two value waves alone while the others prepare the query), so
+// tile t+2 is in flight while tile t is used and no register holds gathered bytes.  A tile is
 // stored column-blocked, [36 columns][64 tokens][16 B], which serves both products without
 // bank conflicts:
 //   logits  S[token][head] = L8[32 tokens x 576] * Q8^T   (9 x v_mfma 32x32x64 per 32 tokens)
