@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (CPU, oracle and the seeded input generator; nothing of the HIP
 library).  The K3.1 page's fused indexer front quantises the indexer query to FP8 before
 scoring ("Fused low-latency decode for DSA layers" / DSA層のための融合低レイテンシデコード)
-and is silent on the MLA query; this build quantises both (one power-of-two scale per
+and is silent on the MLA query; the kernels quantise both (one power-of-two scale per
 (row, head)).  This script measures, on seeded inputs drawn like the decode workloads
 (bf16 N(0,1) queries, N(0, 1/32) head weights, E4M3 keys and latents from N(0,1)), the
 deviation of every stage from the same stage evaluated on the unquantised bf16 query:
